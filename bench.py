@@ -1,0 +1,225 @@
+"""Benchmark: bf16 -> MXFP8 quantize throughput on one MI355X.
+
+A step is one pass of the quantize path over one batch: the rowwise and
+columnwise planes of the bf16 weight [4096, 4096] (N(0, 0.02) with 0.1%
+outliers x1000, 1% zero and 1% subnormal 32x32 tiles) from a single read.
+Inputs are resident in HBM before timing starts.  The step rotates over
+enough copies of input and outputs that the working set exceeds the 256 MB
+Infinity Cache, so every step streams from HBM.
+
+Printed: one JSON line with GB/s of algorithmic bytes (input read once plus
+every output written once), its fraction of the 8 TB/s HBM peak, the other
+entry points measured the same way on their workloads, and the CPU oracle
+timed on a bounded sample on this host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "mxfp8_block_scaled_02_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter runs, if they were taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(workload)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timed:
+    """Times `steps` calls of fn(i) on the current stream with HIP events."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            fn(i)
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(stop) / steps, wall
+
+
+def rotation(per_set_bytes: int) -> int:
+    return max(2, -(-3 * MALL_BYTES // max(per_set_bytes, 1)))
+
+
+def bench_rowcol(torch, mx, synth, steps, warmup):
+    dev = torch.device("cuda:0")
+    x = synth.workload("rowcol_4096x4096", device=dev)["x"]
+    rows, cols = x.shape
+    alg = rows * cols * 2 + 2 * rows * cols + rows * cols // 32 + (rows // 32) * cols
+    sets = rotation(alg)
+    xs = [x.clone() for _ in range(sets)]
+    outs = [mx.quantize(xi, True, True) for xi in xs]
+    fn = lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets])
+    ms, wall = Timed(torch).run(fn, steps, warmup)
+    return {"ms": ms, "bytes": alg, "elems": rows * cols, "sets": sets, "wall_s": wall}
+
+
+def bench_other_rows(torch, mx, synth, steps):
+    """Each remaining entry point on its own workload (fewer steps)."""
+    dev = torch.device("cuda:0")
+    res = {}
+    T = Timed(torch)
+
+    x = synth.workload("rowwise_256x1024", device=dev)["x"]
+    r, c = x.shape
+    alg = r * c * 3 + r * c // 32
+    sets = rotation(alg) if alg * rotation(alg) < (1 << 31) else 1
+    xs = [x.clone() for _ in range(min(sets, 512))]
+    outs = [mx.quantize(xi, True, False) for xi in xs]
+    n = len(xs)
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % n], True, False, out=outs[i % n]), steps, 10)
+    res["rowwise_256x1024"] = (ms, alg, r * c)
+
+    w = synth.workload("rmsnorm_8192x8192", device=dev)
+    r, c = w["x"].shape
+    alg = r * c * 2 + r * c * 2 + r * c + r * c // 32 + c * 2
+    o = mx.rmsnorm_quantize(w["x"], w["gamma"], w["weight_offset"], w["eps"])
+    ms, _ = T.run(lambda i: mx.rmsnorm_quantize(w["x"], w["gamma"], w["weight_offset"], w["eps"], out=o),
+                  max(steps // 4, 5), 3)
+    res["rmsnorm_8192x8192"] = (ms, alg, r * c)
+    del w, o
+
+    xs = synth.workload("grouped_64x2048x7168", device=dev)["xs"]
+    r, c = xs[0].shape
+    alg = len(xs) * (r * c * 2 + 2 * r * c + r * c // 32 + (r // 32) * c)
+    outs = mx.quantize_grouped(xs, True, True)
+    ms, _ = T.run(lambda i: mx.quantize_grouped(xs, True, True, outs=outs), max(steps // 10, 5), 2)
+    res["grouped_64x2048x7168"] = (ms, alg, len(xs) * r * c)
+    del xs, outs
+
+    for name in ("rmsnorm_decode_16x7168", "rmsnorm_prefill_65536x7168"):
+        w = synth.workload(name, device=dev)
+        r, c = w["x"].shape
+        alg = r * c * 2 + r * c * 2 + r * c + r * c // 32 + c * 2
+        o = mx.rmsnorm_quantize(w["x"], w["gamma"], w["weight_offset"], w["eps"])
+        k = steps if r < 1024 else max(steps // 10, 5)
+        ms, _ = T.run(lambda i: mx.rmsnorm_quantize(w["x"], w["gamma"], w["weight_offset"], w["eps"],
+                                                    out=o), k, 3)
+        res[name] = (ms, alg, r * c)
+        del w, o
+
+    x = synth.workload("rowcol_4096x4096", device=dev)["x"]
+    p = mx.quantize(x, True, True)
+    r, c = x.shape
+    for axis, q, s in ((0, p.rowwise_data, p.rowwise_scale), (1, p.columnwise_data, p.columnwise_scale)):
+        alg = r * c + s.numel() + r * c * 4
+        out = mx.dequantize(q, s, axis)
+        ms, _ = T.run(lambda i: mx.dequantize(q, s, axis, out=out), steps, 5)
+        res["dequantize_f32_%s_4096x4096" % ("row" if axis == 0 else "col")] = (ms, alg, r * c)
+    return {k: {"ms_per_launch": round(ms, 5), "GB_s": round(b / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "Gelem_s": round(e / (ms * 1e-3) / 1e9, 2), "alg_bytes": b}
+            for k, (ms, b, e) in res.items()}
+
+
+def cpu_baseline(synth, target_s=10.0):
+    import oracle
+    x = synth.workload("rowcol_4096x4096")["x"]
+    bits = synth.bf16_bits(x)
+    rows, cols = bits.shape
+    alg = rows * cols * 2 + 2 * rows * cols + rows * cols // 32 + (rows // 32) * cols
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.quantize_rowwise(bits)
+        oracle.quantize_colwise(bits)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 50:
+            break
+    return {"value": round(alg * reps / el / 1e9, 3), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d passes of the full 4096x4096 weight, rowwise + columnwise planes, %.1f s"
+                      % (reps, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-rows", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path shards rows with no "
+              "communication, so it runs and is reported per GPU (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp8_block_scaled_02_amd as mx
+    from mxfp8_block_scaled_02_amd import synth
+    mx.lib()
+
+    main_run = bench_rowcol(torch, mx, synth, args.steps, args.warmup)
+    ms = main_run["ms"]
+    gbs = main_run["bytes"] / (ms * 1e-3) / 1e9
+    traffic = measured_traffic("rowcol_4096x4096")
+    line = {
+        "metric": "bf16->MXFP8 quantize GB/s (frac of MI355X HBM peak) + Gelem/s, 1 GPU",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->e4m3fn/e8m0",
+        "data": "synthetic",
+        "config": {"workload": "rowcol_4096x4096", "shape": [4096, 4096],
+                   "planes": ["rowwise", "columnwise"], "alg_bytes_per_step": main_run["bytes"],
+                   "rotating_sets": main_run["sets"]},
+        "Gelem_s": round(main_run["elems"] / (ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if not args.no_other_rows:
+        line["other_entry_points"] = bench_other_rows(torch, mx, synth, max(args.steps // 2, 20))
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

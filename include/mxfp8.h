@@ -1,0 +1,191 @@
+/*
+ * mxfp8.h - C ABI of libmxfp8, an MXFP8 block-quantization library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the library computes.  A bf16 tensor is cut into blocks of 32 elements
+ * (Megatron-Core quantized_dbuffer page, "Data", _MXFP8_BLOCK_SIZE).  Each
+ * block gets one float8_e8m0fnu scale byte S and each element one
+ * float8_e4m3fn byte (Mojo DistributedAllGatherRMSNormQuantMXFP8 page,
+ * "Parameters", quant_dtype and scales_dtype).  The pages leave the scale
+ * rule and the rounding open; the library follows OCP MX v1.0:
+ *
+ *     S = clamp(floor(log2(amax)) - 8 + 127, 0, 254)   (amax: block max |x|)
+ *     S = 0x00 for an all-zero block, 0xFF for a block holding a NaN or an
+ *         infinity (then every element byte is sign | 0x7F)
+ *     q = e4m3fn(x * 2^(127 - S)), round to nearest even, saturate at +-448,
+ *         sign of zero kept.
+ *
+ * Two planes can be produced from one read of the input:
+ *   rowwise:    blocks x[r, 32j .. 32j+31]; scales [rows, cols/32]
+ *               (Mojo page, "Args", outputs_scale);
+ *   columnwise: blocks x[32i .. 32i+31, c]; scales [rows/32, cols] (one
+ *               columnwise scale row covers a 32-row block: quantized_dbuffer
+ *               page, API, _block_atomic_to_flat).
+ * Both data planes are [rows, cols] row-major, the input's own layout, not
+ * transposed (quantized_dbuffer page, Functions: _rowwise_scale_layout and
+ * _columnwise_scale_layout derive both scale layouts from one data layout).
+ * Every plane is compact and unswizzled, with no padding (quantized_dbuffer
+ * page, API: QuantizedDBuffer and get_tensor_view).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are 2D, row-major and contiguous.  rows and cols count
+ *     elements.  Element types: bf16 for x / gamma / normed, uint8 for e4m3
+ *     and e8m0 bytes, float32 or bf16 for dequantized output.
+ *   - Every pointer is a device pointer (hipMalloc or equivalent) and must be
+ *     16-byte aligned.  The caller owns all memory.  The library never
+ *     allocates, frees or synchronizes; outputs are written in place into the
+ *     caller's persistent buffers, so captured HIP graphs keep valid
+ *     pointers (Megatron-Core quantization.utils page, quantize_params_to_mxfp8:
+ *     results are copied into persistent buffers for graph captures).
+ *     Inputs are read only.
+ *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *     it and the call returns at once; results are ready when the stream is.
+ *   - Every argument is checked before anything is launched, so a call that
+ *     returns an error has written nothing.  rows == 0 or cols == 0 is a
+ *     no-op that returns MXFP8_OK.  Device faults surface at the caller's
+ *     next synchronization, as with any HIP work.
+ *   - The library keeps no state: calls may come from any thread.
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXFP8_ABI_VERSION 1
+#define MXFP8_BLOCK 32
+/* Descriptors handled by one kernel launch in the grouped calls; longer
+ * lists are processed in consecutive launches of at most this many. */
+#define MXFP8_GROUP_PER_LAUNCH 64
+
+typedef enum {
+    MXFP8_OK = 0,
+    MXFP8_ERR_NULL = 1,      /* a required pointer is NULL, or a plane's data /
+                                scale pointers are not both set or both NULL */
+    MXFP8_ERR_SHAPE = 2,     /* negative size, partial block, or size limit */
+    MXFP8_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+    MXFP8_ERR_NO_OUTPUT = 4, /* neither plane requested */
+    MXFP8_ERR_ARG = 5,       /* bad enum value, n < 0, or a non-finite eps */
+    MXFP8_ERR_HIP = 6        /* the HIP runtime refused the launch */
+} mxfp8_status;
+
+typedef enum { MXFP8_ROWWISE = 0, MXFP8_COLUMNWISE = 1 } mxfp8_axis;
+typedef enum { MXFP8_OUT_F32 = 0, MXFP8_OUT_BF16 = 1 } mxfp8_out_dtype;
+
+/* MXFP8_ABI_VERSION of the built library. */
+int mxfp8_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *mxfp8_status_string(mxfp8_status status);
+
+/*
+ * mxfp8_quantize - one read of x, one or both planes written.
+ *
+ * Quantizes a local weight or activation shard into its planes
+ * (quantized_dbuffer page, API, QuantizedDBuffer.quantize_; quantization.utils
+ * page, mm_mxfp8 quantizes the bf16 activation on the fly).  The pair
+ * (q_row, s_row) selects the rowwise plane and (q_col, s_col) the columnwise
+ * plane, like the rowwise / columnwise usages of the quantizer
+ * (quantized_dbuffer page, _get_quantizer and planes_for).
+ *
+ *   x      bf16 [rows, cols]
+ *   q_row  uint8 e4m3 [rows, cols]     s_row  uint8 e8m0 [rows, cols/32]
+ *   q_col  uint8 e4m3 [rows, cols]     s_col  uint8 e8m0 [rows/32, cols]
+ *
+ * A plane whose two pointers are NULL is not requested; one NULL and one set
+ * is MXFP8_ERR_NULL; both planes NULL is MXFP8_ERR_NO_OUTPUT.  A rowwise
+ * request needs cols % 32 == 0, a columnwise request rows % 32 == 0 and
+ * cols % 8 == 0 (MXFP8_ERR_SHAPE otherwise).
+ */
+mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols,
+                            void *q_row, void *s_row, void *q_col, void *s_col,
+                            void *stream);
+
+/*
+ * mxfp8_rmsnorm_quantize - RMSNorm, then the rowwise plane of its bf16 output.
+ *
+ * The fused norm-and-quantize of the Mojo DistributedAllGatherRMSNormQuantMXFP8
+ * page (execute; "Args": outputs_normed, outputs_quant, outputs_scale, gammas,
+ * epsilons, weight_offsets) on one GPU's rows, without the all-gather:
+ *
+ *   normed[r, c] = bf16( x[r, c] / sqrt(mean_c(x[r, :]^2) + eps)
+ *                        * (gamma[c] + weight_offset) )
+ *
+ * accumulated in float32 and rounded once to bf16; (q_row, s_row) is then
+ * exactly mxfp8_quantize's rowwise plane of those normed bf16 values (the
+ * page's execute: the quantize reads the same bf16 that lands in
+ * outputs_normed, so it is byte-identical to a standalone quantize).
+ *
+ *   x, normed  bf16 [rows, cols]     gamma  bf16 [cols]
+ *   q_row      uint8 [rows, cols]    s_row  uint8 [rows, cols/32]
+ *
+ * All pointers are required; cols % 32 == 0; eps must be finite and >= 0.
+ */
+mxfp8_status mxfp8_rmsnorm_quantize(const void *x, const void *gamma,
+                                    float weight_offset, float eps,
+                                    int64_t rows, int64_t cols, void *normed,
+                                    void *q_row, void *s_row, void *stream);
+
+/*
+ * mxfp8_dequantize - values of one plane: out = e4m3(q) * 2^(S - 127).
+ *
+ * The check that compares a dequantized tensor with a fresh quantize
+ * (quantization.utils page, _verify_te_to_mcore_mxfp8_conversion) needs it.
+ * axis picks the scale layout: MXFP8_ROWWISE s [rows, cols/32] (cols % 32 ==
+ * 0), MXFP8_COLUMNWISE s [rows/32, cols] (rows % 32 == 0, cols % 8 == 0).
+ * out is float32 or bf16 [rows, cols]: the exact value rounded to nearest
+ * even.  Float32 results are exact (values from 2^-136 up), except that
+ * scale bytes above 246, which no quantize of bf16 input produces, can push a
+ * value past float32's range, giving +-inf; bf16 results are exact except
+ * below 2^-133.  Scale 0xFF or element 0x7F / 0xFF gives NaN.
+ */
+mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
+                              int64_t cols, mxfp8_axis axis, void *out,
+                              mxfp8_out_dtype out_dtype, void *stream);
+
+/*
+ * Grouped calls: one launch over a list of independent 2D tensors of any
+ * shapes, such as the experts of an MoE layer (quantized_dbuffer page,
+ * QuantizedDBuffer.empty takes a list of logical 2D shapes; quantization.utils
+ * page, resolve_mxfp8_backend serves grouped-MoE GEMMs).  Each descriptor
+ * follows the rules of the matching single call and the results equal n
+ * single calls.  descs is a host array of n entries, read before the call
+ * returns.  n == 0 is a no-op; n < 0 is MXFP8_ERR_ARG.  Each launch takes at
+ * most MXFP8_GROUP_PER_LAUNCH descriptors.
+ */
+typedef struct {
+    const void *x;
+    int64_t rows, cols;
+    void *q_row, *s_row; /* both NULL: rowwise plane not requested */
+    void *q_col, *s_col; /* both NULL: columnwise plane not requested */
+} mxfp8_quant_desc;
+
+typedef struct {
+    const void *x, *gamma;
+    float weight_offset, eps;
+    int64_t rows, cols;
+    void *normed, *q_row, *s_row;
+} mxfp8_norm_desc;
+
+typedef struct {
+    const void *q, *s;
+    int64_t rows, cols;
+    mxfp8_axis axis;
+    void *out;
+} mxfp8_deq_desc;
+
+mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc *descs, int32_t n,
+                                    void *stream);
+mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc *descs,
+                                            int32_t n, void *stream);
+mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc *descs, int32_t n,
+                                      mxfp8_out_dtype out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H */

@@ -1,0 +1,283 @@
+"""MXFP8 block quantization on AMD MI355X (gfx950): Python binding.
+
+This module only marshals arguments to ``libmxfp8.so`` (C ABI in
+``include/mxfp8.h``); every step of the computation runs in its HIP kernels.
+torch provides device memory and the current stream.  If the library has not
+been built the first call raises ``RuntimeError``; there is no fallback.
+
+Format: blocks of 32 bf16 values share one float8_e8m0fnu scale byte and each
+value becomes one float8_e4m3fn byte (Megatron-Core quantized_dbuffer page,
+"Data"; Mojo DistributedAllGatherRMSNormQuantMXFP8 page, "Parameters").
+Planes are returned in rowwise-data-first order (quantized_dbuffer page,
+QuantizedDBuffer.planes): rowwise data, columnwise data, rowwise scale,
+columnwise scale, all as ``torch.uint8`` tensors; ``as_fp8`` views them with
+the float8 dtypes.  Tensors with more than two dims are flattened into rows
+(Mojo page, "Parameters", rank).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional, Sequence
+
+import torch
+
+__all__ = [
+    "MXFP8Planes", "quantize", "rmsnorm_quantize", "dequantize", "quantize_grouped",
+    "rmsnorm_quantize_grouped", "dequantize_grouped", "as_fp8", "library_path", "lib",
+    "BLOCK", "ROWWISE", "COLUMNWISE",
+]
+
+BLOCK = 32
+ROWWISE, COLUMNWISE = 0, 1
+_OUT_F32, _OUT_BF16 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
+_lib = None
+
+_STATUS = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_ERR_ALIGN",
+           4: "MXFP8_ERR_NO_OUTPUT", 5: "MXFP8_ERR_ARG", 6: "MXFP8_ERR_HIP"}
+
+
+class _QuantDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("q_row", ctypes.c_void_p), ("s_row", ctypes.c_void_p),
+                ("q_col", ctypes.c_void_p), ("s_col", ctypes.c_void_p)]
+
+
+class _NormDesc(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("weight_offset", ctypes.c_float), ("eps", ctypes.c_float),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("normed", ctypes.c_void_p), ("q_row", ctypes.c_void_p),
+                ("s_row", ctypes.c_void_p)]
+
+
+class _DeqDesc(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("axis", ctypes.c_int), ("out", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises RuntimeError if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libmxfp8.so is not built; run `python -m "
+                           "mxfp8_block_scaled_02_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(_LIB_PATH)
+    p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    L.mxfp8_abi_version.argtypes, L.mxfp8_abi_version.restype = [], ctypes.c_int
+    L.mxfp8_status_string.argtypes, L.mxfp8_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    L.mxfp8_quantize.argtypes = [p, i64, i64, p, p, p, p, p]
+    L.mxfp8_rmsnorm_quantize.argtypes = [p, p, f32, f32, i64, i64, p, p, p, p]
+    L.mxfp8_dequantize.argtypes = [p, p, i64, i64, ctypes.c_int, p, ctypes.c_int, p]
+    L.mxfp8_quantize_grouped.argtypes = [ctypes.POINTER(_QuantDesc), i32, p]
+    L.mxfp8_rmsnorm_quantize_grouped.argtypes = [ctypes.POINTER(_NormDesc), i32, p]
+    L.mxfp8_dequantize_grouped.argtypes = [ctypes.POINTER(_DeqDesc), i32, ctypes.c_int, p]
+    for name in ("mxfp8_quantize", "mxfp8_rmsnorm_quantize", "mxfp8_dequantize",
+                 "mxfp8_quantize_grouped", "mxfp8_rmsnorm_quantize_grouped",
+                 "mxfp8_dequantize_grouped"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status == 0:
+        return
+    msg = "%s: %s" % (_STATUS.get(status, status), lib().mxfp8_status_string(status).decode())
+    if status == 6:
+        raise RuntimeError(msg)
+    raise ValueError(msg)
+
+
+class MXFP8Planes(NamedTuple):
+    """Physical planes of one MXFP8 tensor in rowwise-data-first order; a plane
+    that was not requested is None."""
+    rowwise_data: Optional[torch.Tensor]
+    columnwise_data: Optional[torch.Tensor]
+    rowwise_scale: Optional[torch.Tensor]
+    columnwise_scale: Optional[torch.Tensor]
+
+
+def as_fp8(planes: MXFP8Planes) -> MXFP8Planes:
+    """The same storage viewed as float8_e4m3fn data and float8_e8m0fnu scales."""
+    def v(t, dt):
+        return None if t is None else t.view(dt)
+    return MXFP8Planes(v(planes.rowwise_data, torch.float8_e4m3fn),
+                       v(planes.columnwise_data, torch.float8_e4m3fn),
+                       v(planes.rowwise_scale, torch.float8_e8m0fnu),
+                       v(planes.columnwise_scale, torch.float8_e8m0fnu))
+
+
+def _as2d(x: torch.Tensor, name: str, dtype=torch.bfloat16) -> torch.Tensor:
+    if x.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, x.dtype))
+    if not x.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if x.dim() == 1:
+        return x.view(1, -1)
+    return x.reshape(-1, x.shape[-1]) if x.dim() > 2 else x
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dtype, tuple(shape), device))
+    return t
+
+
+def _quant_desc(x, rowwise, columnwise, out):
+    x2 = _as2d(x, "x")
+    rows, cols = x2.shape
+    o = out or MXFP8Planes(None, None, None, None)
+    dev = x.device
+    qr = _out(o.rowwise_data, (rows, cols), torch.uint8, dev, "rowwise_data") if rowwise else None
+    sr = _out(o.rowwise_scale, (rows, cols // BLOCK), torch.uint8, dev, "rowwise_scale") if rowwise else None
+    qc = _out(o.columnwise_data, (rows, cols), torch.uint8, dev, "columnwise_data") if columnwise else None
+    sc = _out(o.columnwise_scale, (rows // BLOCK, cols), torch.uint8, dev, "columnwise_scale") if columnwise else None
+    d = _QuantDesc(_ptr(x2), rows, cols, _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc))
+    return d, MXFP8Planes(qr, qc, sr, sc)
+
+
+def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
+             out: Optional[MXFP8Planes] = None) -> MXFP8Planes:
+    """Quantize bf16 x [rows, cols] into the requested planes in one launch.
+
+    ``out`` supplies persistent plane buffers that are overwritten in place
+    (Megatron-Core quantization.utils page, quantize_params_to_mxfp8)."""
+    d, planes = _quant_desc(x, rowwise, columnwise, out)
+    with torch.cuda.device(x.device):
+        _check(lib().mxfp8_quantize(d.x, d.rows, d.cols, d.q_row, d.s_row, d.q_col,
+                                    d.s_col, _stream(x.device)))
+    return planes
+
+
+def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwise: bool = False,
+                     outs: Optional[Sequence[MXFP8Planes]] = None) -> list:
+    """Quantize a list of bf16 tensors of any shapes in one launch."""
+    if not xs:
+        return []
+    dev = xs[0].device
+    descs, planes = [], []
+    for i, x in enumerate(xs):
+        if x.device != dev:
+            raise ValueError("all tensors must be on one device")
+        d, p = _quant_desc(x, rowwise, columnwise, outs[i] if outs else None)
+        descs.append(d)
+        planes.append(p)
+    arr = (_QuantDesc * len(descs))(*descs)
+    with torch.cuda.device(dev):
+        _check(lib().mxfp8_quantize_grouped(arr, len(descs), _stream(dev)))
+    return planes
+
+
+def _norm_desc(x, gamma, weight_offset, eps, out):
+    x2 = _as2d(x, "x")
+    rows, cols = x2.shape
+    g = _as2d(gamma, "gamma")
+    if g.numel() != cols:
+        raise ValueError("gamma must have %d elements" % cols)
+    dev = x.device
+    o = out or (None, None, None)
+    normed = _out(o[0], (rows, cols), torch.bfloat16, dev, "normed")
+    q = _out(o[1], (rows, cols), torch.uint8, dev, "q")
+    s = _out(o[2], (rows, cols // BLOCK), torch.uint8, dev, "s")
+    d = _NormDesc(_ptr(x2), _ptr(g), float(weight_offset), float(eps), rows, cols,
+                  _ptr(normed), _ptr(q), _ptr(s))
+    return d, (normed, q, s)
+
+
+def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, weight_offset: float = 0.0,
+                     eps: float = 1e-6, out=None):
+    """RMSNorm in float32 rounded once to bf16, then its rowwise MXFP8 plane.
+
+    Returns (normed bf16 [rows, cols], data uint8 [rows, cols], scales uint8
+    [rows, cols/32]); the bytes equal ``quantize(normed)``."""
+    d, res = _norm_desc(x, gamma, weight_offset, eps, out)
+    with torch.cuda.device(x.device):
+        _check(lib().mxfp8_rmsnorm_quantize(d.x, d.gamma, d.weight_offset, d.eps, d.rows,
+                                            d.cols, d.normed, d.q_row, d.s_row,
+                                            _stream(x.device)))
+    return res
+
+
+def rmsnorm_quantize_grouped(xs, gammas, weight_offsets, epss, outs=None) -> list:
+    """Fused RMSNorm + rowwise quantize over a list of tensors in one launch."""
+    if not xs:
+        return []
+    dev = xs[0].device
+    descs, res = [], []
+    for i, x in enumerate(xs):
+        if x.device != dev:
+            raise ValueError("all tensors must be on one device")
+        d, r = _norm_desc(x, gammas[i], weight_offsets[i], epss[i], outs[i] if outs else None)
+        descs.append(d)
+        res.append(r)
+    arr = (_NormDesc * len(descs))(*descs)
+    with torch.cuda.device(dev):
+        _check(lib().mxfp8_rmsnorm_quantize_grouped(arr, len(descs), _stream(dev)))
+    return res
+
+
+def _deq_desc(q, s, axis, dtype, out):
+    q2 = _as2d(q, "q", torch.uint8)
+    s2 = _as2d(s, "s", torch.uint8)
+    rows, cols = q2.shape
+    want = (rows, cols // BLOCK) if axis == ROWWISE else (rows // BLOCK, cols)
+    if tuple(s2.shape) != want:
+        raise ValueError("scale shape %s, expected %s" % (tuple(s2.shape), want))
+    o = _out(out, (rows, cols), dtype, q.device, "out")
+    return _DeqDesc(_ptr(q2), _ptr(s2), rows, cols, int(axis), _ptr(o)), o
+
+
+def _out_code(dtype):
+    if dtype == torch.float32:
+        return _OUT_F32
+    if dtype == torch.bfloat16:
+        return _OUT_BF16
+    raise ValueError("dequantize output must be float32 or bfloat16")
+
+
+def dequantize(q: torch.Tensor, s: torch.Tensor, axis: int = ROWWISE,
+               dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None):
+    """Values of one plane, e4m3(q) * 2^(s - 127), as float32 or bf16."""
+    code = _out_code(dtype)
+    d, o = _deq_desc(q, s, axis, dtype, out)
+    with torch.cuda.device(q.device):
+        _check(lib().mxfp8_dequantize(d.q, d.s, d.rows, d.cols, d.axis, d.out, code,
+                                      _stream(q.device)))
+    return o
+
+
+def dequantize_grouped(qs, ss, axes, dtype=torch.float32, outs=None) -> list:
+    if not qs:
+        return []
+    code = _out_code(dtype)
+    dev = qs[0].device
+    descs, res = [], []
+    for i, q in enumerate(qs):
+        d, o = _deq_desc(q, ss[i], axes[i], dtype, outs[i] if outs else None)
+        descs.append(d)
+        res.append(o)
+    arr = (_DeqDesc * len(descs))(*descs)
+    with torch.cuda.device(dev):
+        _check(lib().mxfp8_dequantize_grouped(arr, len(descs), code, _stream(dev)))
+    return res

@@ -1,0 +1,233 @@
+// C ABI of libmxfp8 (declared in include/mxfp8.h): argument checks, tensor
+// tables and launches.  Every check runs before the first launch, so a call
+// that fails has enqueued nothing.  The library holds no state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "mx_kernels.h"
+#include "mxfp8.h"
+
+namespace {
+
+using mx::kGroupMax;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Largest element count and task count one launch may carry.
+constexpr int64_t kMaxTasksPerLaunch = (int64_t)1 << 30;
+
+bool fits(int64_t rows, int64_t cols) {
+  return rows >= 0 && cols >= 0 && (cols == 0 || rows <= INT64_MAX / 4 / cols);
+}
+
+mxfp8_status check_quant(const mxfp8_quant_desc& d) {
+  if (d.rows < 0 || d.cols < 0 || !fits(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
+  if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
+  const bool row = d.q_row || d.s_row, col = d.q_col || d.s_col;
+  if ((d.q_row == nullptr) != (d.s_row == nullptr)) return MXFP8_ERR_NULL;
+  if ((d.q_col == nullptr) != (d.s_col == nullptr)) return MXFP8_ERR_NULL;
+  if (!row && !col) return MXFP8_ERR_NO_OUTPUT;
+  if (d.x == nullptr) return MXFP8_ERR_NULL;
+  if (row && d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
+  if (col && (d.rows % MXFP8_BLOCK || d.cols % 8)) return MXFP8_ERR_SHAPE;
+  if (misaligned(d.x) || misaligned(d.q_row) || misaligned(d.s_row) ||
+      misaligned(d.q_col) || misaligned(d.s_col))
+    return MXFP8_ERR_ALIGN;
+  return MXFP8_OK;
+}
+
+mxfp8_status check_norm(const mxfp8_norm_desc& d) {
+  if (d.rows < 0 || d.cols < 0 || d.rows > INT32_MAX || d.cols > INT32_MAX)
+    return MXFP8_ERR_SHAPE;
+  if (!isfinite(d.eps) || d.eps < 0.0f) return MXFP8_ERR_ARG;
+  if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
+  if (!d.x || !d.gamma || !d.normed || !d.q_row || !d.s_row) return MXFP8_ERR_NULL;
+  if (d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
+  if (misaligned(d.x) || misaligned(d.gamma) || misaligned(d.normed) ||
+      misaligned(d.q_row) || misaligned(d.s_row))
+    return MXFP8_ERR_ALIGN;
+  return MXFP8_OK;
+}
+
+mxfp8_status check_deq(const mxfp8_deq_desc& d) {
+  if (d.axis != MXFP8_ROWWISE && d.axis != MXFP8_COLUMNWISE) return MXFP8_ERR_ARG;
+  if (d.rows < 0 || d.cols < 0 || !fits(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
+  if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
+  if (!d.q || !d.s || !d.out) return MXFP8_ERR_NULL;
+  if (d.axis == MXFP8_ROWWISE && d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
+  if (d.axis == MXFP8_COLUMNWISE && (d.rows % MXFP8_BLOCK || d.cols % 8))
+    return MXFP8_ERR_SHAPE;
+  if (misaligned(d.q) || misaligned(d.s) || misaligned(d.out)) return MXFP8_ERR_ALIGN;
+  return MXFP8_OK;
+}
+
+mxfp8_status hip_status(hipError_t e) { return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_HIP; }
+
+// Packs non-empty tensors into argument blocks of at most kGroupMax entries
+// and kMaxTasksPerLaunch tasks, launching each block as it fills.
+template <class Args, class Desc, class TaskFn, class LaunchFn>
+mxfp8_status run_groups(const std::vector<Desc>& descs, TaskFn tasks, LaunchFn launch,
+                        Args& a) {
+  a.n = 0;
+  a.task_start[0] = 0;
+  int64_t total = 0;
+  bool cleared = false;
+  for (const Desc& d : descs) {
+    const int64_t t = tasks(d);
+    if (t == 0) continue;
+    if (!cleared) {
+      (void)hipGetLastError();  // report only errors raised by this call's launches
+      cleared = true;
+    }
+    if (a.n == kGroupMax || total + t > kMaxTasksPerLaunch) {
+      if (mxfp8_status st = hip_status(launch(a, total))) return st;
+      a.n = 0;
+      total = 0;
+    }
+    a.d[a.n] = d;
+    total += t;
+    a.task_start[++a.n] = (int32_t)total;
+  }
+  if (a.n) return hip_status(launch(a, total));
+  return MXFP8_OK;
+}
+
+mx::QuantDesc to_internal(const mxfp8_quant_desc& d) {
+  mx::QuantDesc q;
+  q.x = static_cast<const uint16_t*>(d.x);
+  q.q_row = static_cast<uint8_t*>(d.q_row);
+  q.s_row = static_cast<uint8_t*>(d.s_row);
+  q.q_col = static_cast<uint8_t*>(d.q_col);
+  q.s_col = static_cast<uint8_t*>(d.s_col);
+  q.rows = d.rows;
+  q.cols = d.cols;
+  return q;
+}
+
+mx::NormDesc to_internal(const mxfp8_norm_desc& d) {
+  mx::NormDesc n;
+  n.x = static_cast<const uint16_t*>(d.x);
+  n.gamma = static_cast<const uint16_t*>(d.gamma);
+  n.normed = static_cast<uint16_t*>(d.normed);
+  n.q = static_cast<uint8_t*>(d.q_row);
+  n.s = static_cast<uint8_t*>(d.s_row);
+  n.rows = (int32_t)d.rows;
+  n.cols = (int32_t)d.cols;
+  n.weight_offset = d.weight_offset;
+  n.eps = d.eps;
+  return n;
+}
+
+mx::DeqDesc to_internal(const mxfp8_deq_desc& d) {
+  mx::DeqDesc q;
+  q.q = static_cast<const uint8_t*>(d.q);
+  q.s = static_cast<const uint8_t*>(d.s);
+  q.out = d.out;
+  q.rows = d.rows;
+  q.cols = d.cols;
+  q.axis = d.axis == MXFP8_COLUMNWISE ? 1 : 0;
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp8_abi_version(void) { return MXFP8_ABI_VERSION; }
+
+const char* mxfp8_status_string(mxfp8_status status) {
+  switch (status) {
+    case MXFP8_OK: return "ok";
+    case MXFP8_ERR_NULL: return "a required pointer is NULL or a plane is half specified";
+    case MXFP8_ERR_SHAPE: return "bad shape: negative size, partial 32-element block or size limit";
+    case MXFP8_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MXFP8_ERR_NO_OUTPUT: return "neither the rowwise nor the columnwise plane was requested";
+    case MXFP8_ERR_ARG: return "bad argument: enum value, group count or eps";
+    case MXFP8_ERR_HIP: return "the HIP runtime refused the launch";
+  }
+  return "unknown status";
+}
+
+mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc* descs, int32_t n, void* stream) {
+  if (n < 0) return MXFP8_ERR_ARG;
+  if (n == 0) return MXFP8_OK;
+  if (!descs) return MXFP8_ERR_NULL;
+  std::vector<mx::QuantDesc> v;
+  v.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (mxfp8_status st = check_quant(descs[i])) return st;
+    v.push_back(to_internal(descs[i]));
+  }
+  mx::QuantArgs a;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run_groups(v, mx::quant_tasks,
+                    [&](const mx::QuantArgs& args, int64_t t) { return mx::launch_quantize(args, t, s); },
+                    a);
+}
+
+mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, void* q_row,
+                            void* s_row, void* q_col, void* s_col, void* stream) {
+  mxfp8_quant_desc d = {x, rows, cols, q_row, s_row, q_col, s_col};
+  return mxfp8_quantize_grouped(&d, 1, stream);
+}
+
+mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc* descs, int32_t n,
+                                            void* stream) {
+  if (n < 0) return MXFP8_ERR_ARG;
+  if (n == 0) return MXFP8_OK;
+  if (!descs) return MXFP8_ERR_NULL;
+  std::vector<mx::NormDesc> v;
+  v.reserve(n);
+  int64_t max_cols = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (mxfp8_status st = check_norm(descs[i])) return st;
+    v.push_back(to_internal(descs[i]));
+    if (descs[i].rows > 0 && descs[i].cols > max_cols) max_cols = descs[i].cols;
+  }
+  const int variant = mx::norm_variant(max_cols);
+  mx::NormArgs a;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run_groups(
+      v, [](const mx::NormDesc& d) -> int64_t { return d.cols ? d.rows : 0; },
+      [&](const mx::NormArgs& args, int64_t t) { return mx::launch_rmsnorm_quantize(args, t, variant, s); },
+      a);
+}
+
+mxfp8_status mxfp8_rmsnorm_quantize(const void* x, const void* gamma, float weight_offset,
+                                    float eps, int64_t rows, int64_t cols, void* normed,
+                                    void* q_row, void* s_row, void* stream) {
+  mxfp8_norm_desc d = {x, gamma, weight_offset, eps, rows, cols, normed, q_row, s_row};
+  return mxfp8_rmsnorm_quantize_grouped(&d, 1, stream);
+}
+
+mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc* descs, int32_t n,
+                                      mxfp8_out_dtype out_dtype, void* stream) {
+  if (n < 0) return MXFP8_ERR_ARG;
+  if (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16) return MXFP8_ERR_ARG;
+  if (n == 0) return MXFP8_OK;
+  if (!descs) return MXFP8_ERR_NULL;
+  std::vector<mx::DeqDesc> v;
+  v.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (mxfp8_status st = check_deq(descs[i])) return st;
+    v.push_back(to_internal(descs[i]));
+  }
+  mx::DeqArgs a;
+  a.out_bf16 = out_dtype == MXFP8_OUT_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run_groups(v, mx::deq_tasks,
+                    [&](const mx::DeqArgs& args, int64_t t) { return mx::launch_dequantize(args, t, s); },
+                    a);
+}
+
+mxfp8_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t cols,
+                              mxfp8_axis axis, void* out, mxfp8_out_dtype out_dtype,
+                              void* stream) {
+  mxfp8_deq_desc d = {q, s, rows, cols, axis, out};
+  return mxfp8_dequantize_grouped(&d, 1, out_dtype, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Kernel argument blocks and launchers shared by the C ABI and the kernels.
+//
+// Every launch takes a small table of tensors (one entry for the single-
+// tensor calls, up to kGroupMax for the grouped calls) passed by value in the
+// kernel argument segment, plus a prefix sum of per-tensor wave tasks.  A
+// wave finds its tensor by binary search over that prefix sum, so tensors of
+// any mix of shapes share one launch (Megatron-Core quantized_dbuffer page:
+// QuantizedDBuffer.empty builds one layout from a list of logical 2D shapes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+constexpr int kGroupMax = 64;        // tensors per launch (argument block < 4 KiB)
+constexpr int kWavesPerGroup = 4;    // waves per workgroup
+constexpr int kThreads = 64 * kWavesPerGroup;
+constexpr int kFlatUnroll = 4;       // 16-byte chunks per lane per flat task
+constexpr int kTileRows = 32;        // rows of a row+column tile (one MX block)
+constexpr int kRowsPerWave = kTileRows / kWavesPerGroup;
+constexpr int kTileCols = 512;       // columns of a tile: 64 lanes x 8
+constexpr int kDeqRows = 4;          // rows per columnwise dequantize task
+
+// ---- quantize ------------------------------------------------------------
+struct QuantDesc {
+  const uint16_t* x;
+  uint8_t* q_row;
+  uint8_t* s_row;  // NULL: rowwise plane not requested
+  uint8_t* q_col;
+  uint8_t* s_col;  // NULL: columnwise plane not requested
+  int64_t rows, cols;
+};
+struct QuantArgs {
+  int32_t n;
+  int32_t task_start[kGroupMax + 1];
+  QuantDesc d[kGroupMax];
+};
+// Workgroup tasks a tensor needs: 32 x 512 tiles when a columnwise plane is
+// requested, otherwise 256 x kFlatUnroll chunks of the flattened tensor.
+int64_t quant_tasks(const QuantDesc& d);
+hipError_t launch_quantize(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
+
+// ---- RMSNorm + rowwise quantize ------------------------------------------
+struct NormDesc {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  uint16_t* normed;
+  uint8_t* q;
+  uint8_t* s;
+  int32_t rows, cols;
+  float weight_offset, eps;
+};
+struct NormArgs {
+  int32_t n;
+  int32_t task_start[kGroupMax + 1];
+  NormDesc d[kGroupMax];
+};
+// Kernel shape for the longest row of a launch: waves per row and chunks
+// per lane (see rmsnorm_quantize.hip).  One task per row.
+int norm_variant(int64_t cols);
+hipError_t launch_rmsnorm_quantize(const NormArgs& a, int64_t total_tasks, int variant,
+                                   hipStream_t s);
+
+// ---- dequantize ----------------------------------------------------------
+struct DeqDesc {
+  const uint8_t* q;
+  const uint8_t* s;
+  void* out;
+  int64_t rows, cols;
+  int32_t axis;  // 0 rowwise scales, 1 columnwise scales
+};
+struct DeqArgs {
+  int32_t n;
+  int32_t out_bf16;
+  int32_t task_start[kGroupMax + 1];
+  DeqDesc d[kGroupMax];
+};
+int64_t deq_tasks(const DeqDesc& d);
+hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s);
+
+}  // namespace mx

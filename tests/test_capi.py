@@ -1,0 +1,117 @@
+"""The C ABI library without a GPU: it loads, exports every function that
+include/mxfp8.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_02_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_NO_OUTPUT, ERR_ARG, ERR_HIP = range(7)
+A = 0x10000   # aligned fake device addresses: never dereferenced, every call fails checks
+B = 0x20000
+C = 0x30000
+D = 0x40000
+MIS = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp8_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mx.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return mx.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), "missing export " + n
+
+
+def test_version_and_status_strings(L):
+    assert L.mxfp8_abi_version() == 1
+    for code in range(7):
+        assert L.mxfp8_status_string(code)
+    assert b"unknown" in L.mxfp8_status_string(99)
+
+
+def test_quantize_argument_checks(L):
+    q = L.mxfp8_quantize
+    assert q(A, -1, 32, B, C, None, None, None) == ERR_SHAPE
+    assert q(A, 4, 48, B, C, None, None, None) == ERR_SHAPE          # partial row block
+    assert q(A, 48, 32, None, None, B, C, None) == ERR_SHAPE         # partial column block
+    assert q(A, 32, 36, None, None, B, C, None) == ERR_SHAPE         # cols % 8
+    assert q(A, 4, 32, B, None, None, None, None) == ERR_NULL        # half a plane
+    assert q(A, 32, 32, None, None, None, C, None) == ERR_NULL
+    assert q(None, 4, 32, B, C, None, None, None) == ERR_NULL
+    assert q(A, 4, 32, None, None, None, None, None) == ERR_NO_OUTPUT
+    assert q(MIS, 4, 32, B, C, None, None, None) == ERR_ALIGN
+    assert q(A, 4, 32, B, C + 1, None, None, None) == ERR_ALIGN
+    assert q(A, 1 << 40, 1 << 40, B, C, None, None, None) == ERR_SHAPE   # overflow
+    # empty tensors are a no-op, whatever the pointers
+    assert q(None, 0, 32, None, None, None, None, None) == OK
+    assert q(None, 5, 0, None, None, None, None, None) == OK
+
+
+def test_rmsnorm_argument_checks(L):
+    r = L.mxfp8_rmsnorm_quantize
+    assert r(A, B, 0.0, 1e-6, 4, 48, C, D, A, None) == ERR_SHAPE
+    assert r(A, None, 0.0, 1e-6, 4, 32, C, D, A, None) == ERR_NULL
+    assert r(A, B, 0.0, float("nan"), 4, 32, C, D, A, None) == ERR_ARG
+    assert r(A, B, 0.0, -1.0, 4, 32, C, D, A, None) == ERR_ARG
+    assert r(A, B, 0.0, 1e-6, 4, 32, C, D, MIS, None) == ERR_ALIGN
+    assert r(A, B, 0.0, 1e-6, 1 << 31, 32, C, D, A, None) == ERR_SHAPE
+    assert r(None, None, 0.0, 1e-6, 0, 32, None, None, None, None) == OK
+
+
+def test_dequantize_argument_checks(L):
+    d = L.mxfp8_dequantize
+    assert d(A, B, 4, 32, 2, C, 0, None) == ERR_ARG           # axis
+    assert d(A, B, 4, 32, 0, C, 7, None) == ERR_ARG           # out dtype
+    assert d(A, B, 4, 48, 0, C, 0, None) == ERR_SHAPE
+    assert d(A, B, 40, 32, 1, C, 0, None) == ERR_SHAPE
+    assert d(A, None, 4, 32, 0, C, 0, None) == ERR_NULL
+    assert d(A, B, 4, 32, 0, MIS, 1, None) == ERR_ALIGN
+    assert d(None, None, 0, 0, 1, None, 1, None) == OK
+
+
+def test_grouped_checks_every_descriptor_first(L):
+    good = mx._QuantDesc(A, 4, 32, B, C, None, None)
+    bad = mx._QuantDesc(A, 4, 48, B, C, None, None)
+    arr = (mx._QuantDesc * 3)(good, good, bad)
+    # the bad third entry fails the call before the good ones are launched
+    assert L.mxfp8_quantize_grouped(arr, 3, None) == ERR_SHAPE
+    assert L.mxfp8_quantize_grouped(arr, -1, None) == ERR_ARG
+    assert L.mxfp8_quantize_grouped(None, 2, None) == ERR_NULL
+    assert L.mxfp8_quantize_grouped(None, 0, None) == OK
+    n = (mx._NormDesc * 1)(mx._NormDesc(A, B, 0.0, float("inf"), 4, 32, C, D, A))
+    assert L.mxfp8_rmsnorm_quantize_grouped(n, 1, None) == ERR_ARG
+    dq = (mx._DeqDesc * 1)(mx._DeqDesc(A, B, 32, 40, 1, MIS))
+    assert L.mxfp8_dequantize_grouped(dq, 1, 0, None) == ERR_ALIGN
+    dq = (mx._DeqDesc * 1)(mx._DeqDesc(A, B, 32, 36, 1, C))
+    assert L.mxfp8_dequantize_grouped(dq, 1, 0, None) == ERR_SHAPE
+
+
+def test_descriptor_layout_matches_header():
+    # the ctypes mirrors must have the C structs' sizes (x86-64 ABI)
+    assert ctypes.sizeof(mx._QuantDesc) == 56
+    assert ctypes.sizeof(mx._NormDesc) == 64
+    assert ctypes.sizeof(mx._DeqDesc) == 48
+
+
+def test_python_layer_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        mx.quantize(torch.zeros(4, 32, dtype=torch.bfloat16))
