@@ -7,10 +7,14 @@ Inputs are resident in HBM before timing starts.  The step rotates over
 enough copies of input and outputs that the working set exceeds the 256 MB
 Infinity Cache, so every step streams from HBM.
 
+The timed steps are captured into one HIP graph and replayed once between
+HIP events, so the figure is GPU time, not Python's per-call overhead.
+
 Printed: one JSON line with GB/s of algorithmic bytes (input read once plus
 every output written once), its fraction of the 8 TB/s HBM peak, the other
-entry points measured the same way on their workloads, and the CPU oracle
-timed on a bounded sample on this host.
+entry points measured the same way on their workloads, a plain device copy
+of the same byte count for context, and the CPU oracle timed on a bounded
+sample on this host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -55,7 +59,12 @@ def measured_traffic(workload: str):
 
 
 class Timed:
-    """Times `steps` calls of fn(i) on the current stream with HIP events."""
+    """Times exactly `steps` calls of fn(i).
+
+    The calls are captured once into a HIP graph (after `warmup` eager calls)
+    and the graph is replayed once inside the timed region, so the time is
+    the GPU's and not Python's per-call overhead.  HIP events on the replay
+    stream bracket the replay; the host synchronizes on both sides."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -65,16 +74,23 @@ class Timed:
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        start.record()
-        for i in range(steps):
-            fn(i)
-        stop.record()
+        start.record(stream)
+        g.replay()
+        stop.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return start.elapsed_time(stop) / steps, wall
+        ms = start.elapsed_time(stop) / steps
+        del g
+        return ms, wall
 
 
 def rotation(per_set_bytes: int) -> int:
@@ -138,6 +154,14 @@ def bench_other_rows(torch, mx, synth, steps):
         res[name] = (ms, alg, r * c)
         del w, o
 
+    # context: a plain device copy moving the row+column step's input volume
+    sets = rotation(2 * (32 << 20))
+    srcs = [torch.empty(32 << 20, dtype=torch.uint8, device=dev).fill_(1) for _ in range(sets)]
+    dsts = [torch.empty_like(t) for t in srcs]
+    ms, _ = T.run(lambda i: dsts[i % sets].copy_(srcs[i % sets]), steps, 5)
+    res["context_device_copy_32MiB"] = (ms, 2 * (32 << 20), 0)
+    del srcs, dsts
+
     x = synth.workload("rowcol_4096x4096", device=dev)["x"]
     p = mx.quantize(x, True, True)
     r, c = x.shape
@@ -172,13 +196,83 @@ def cpu_baseline(synth, target_s=10.0):
                       % (reps, el)}
 
 
+def short_kernel_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def trace_summary(trace_csv: str) -> str:
+    """Per-kernel launch durations from a rocprofv3 --kernel-trace CSV (text)."""
+    import csv
+    import collections
+    agg = collections.defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "mx::" not in name and "copy" not in name.lower():
+                continue
+            key = (short_kernel_name(name), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+            agg[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["%-60s %10s %6s %12s %12s %12s" % ("kernel", "workgroups", "calls", "mean_us",
+                                                "median_us", "min_us")]
+    for (name, wgs), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        lines.append("%-60s %10d %6d %12.3f %12.3f %12.3f" % (
+            name[-60:], wgs, len(v), sum(v) / len(v) / 1e3, v[len(v) // 2] / 1e3, v[0] / 1e3))
+    return "\n".join(lines)
+
+
+def counter_bytes(counter_csv: str, counter: str):
+    """{(kernel, workgroups): [KiB per dispatch]} for one counter."""
+    import csv
+    import collections
+    out = collections.defaultdict(list)
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (short_kernel_name(r["Kernel_Name"]),
+                   int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+            out[key].append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int = 256 << 20):
+    """HBM bytes per launch of the quantize kernel, each counter scaled by what
+    it reads for a plain device copy of copy_bytes (the largest copy kernel
+    dispatch in the same run)."""
+    fetch = counter_bytes(fetch_csv, "FETCH_SIZE")
+    write = counter_bytes(write_csv, "WRITE_SIZE")
+    copy_f = max(max(v) for k, v in fetch.items() if "copy" in k[0].lower())
+    copy_w = max(max(v) for k, v in write.items() if "copy" in k[0].lower())
+    f_scale = copy_bytes / (copy_f * 1024.0)
+    w_scale = copy_bytes / (copy_w * 1024.0)
+    res = {}
+    for key, v in fetch.items():
+        if "mx::" not in key[0] or key not in write:
+            continue
+        fb = sum(v) / len(v) * 1024.0 * f_scale
+        wb = sum(write[key]) / len(write[key]) * 1024.0 * w_scale
+        res["%s/%d" % key] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    return {"fetch_scale": f_scale, "write_scale": w_scale, "kernels": res}
+
+
 def main():
+    if len(sys.argv) > 2 and sys.argv[1] == "--trace-summary":
+        print(trace_summary(sys.argv[2]))
+        return
+    if len(sys.argv) > 3 and sys.argv[1] == "--traffic-summary":
+        print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3]), indent=1))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-rows", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy, the reference that "
+                         "scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path shards rows with no "
@@ -189,6 +283,14 @@ def main():
     import mxfp8_block_scaled_02_amd as mx
     from mxfp8_block_scaled_02_amd import synth
     mx.lib()
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     main_run = bench_rowcol(torch, mx, synth, args.steps, args.warmup)
     ms = main_run["ms"]

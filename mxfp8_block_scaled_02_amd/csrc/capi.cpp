@@ -181,18 +181,24 @@ mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc* descs, int32_
   if (!descs) return MXFP8_ERR_NULL;
   std::vector<mx::NormDesc> v;
   v.reserve(n);
-  int64_t max_cols = 0;
+  int64_t max_cols = 0, total_rows = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (mxfp8_status st = check_norm(descs[i])) return st;
     v.push_back(to_internal(descs[i]));
-    if (descs[i].rows > 0 && descs[i].cols > max_cols) max_cols = descs[i].cols;
+    if (descs[i].rows > 0 && descs[i].cols > 0) {
+      if (descs[i].cols > max_cols) max_cols = descs[i].cols;
+      total_rows += descs[i].rows;
+    }
   }
   const int variant = mx::norm_variant(max_cols);
+  const int rpt = mx::norm_rows_per_task(total_rows, variant);
   mx::NormArgs a;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return run_groups(
-      v, [](const mx::NormDesc& d) -> int64_t { return d.cols ? d.rows : 0; },
-      [&](const mx::NormArgs& args, int64_t t) { return mx::launch_rmsnorm_quantize(args, t, variant, s); },
+      v, [rpt](const mx::NormDesc& d) -> int64_t { return d.cols ? (d.rows + rpt - 1) / rpt : 0; },
+      [&](const mx::NormArgs& args, int64_t t) {
+        return mx::launch_rmsnorm_quantize(args, t, variant, rpt, s);
+      },
       a);
 }
 

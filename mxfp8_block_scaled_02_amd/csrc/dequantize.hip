@@ -6,9 +6,11 @@
 // [rows/32, cols]); every float32 result is exact, bf16 results round to
 // nearest even only below 2^-133.
 //
-// Wave tasks: rowwise planes are walked flat (64 x kFlatUnroll chunks of 8
-// bytes, scale byte = chunk / 4); columnwise planes by kDeqRows rows x 512
-// columns, each lane reading its 8 columns' scale bytes once.
+// Wave tasks, 4 elements per lane per step so that every load and store
+// instruction covers contiguous memory: rowwise planes are walked flat
+// (64 x kDeqUnroll units, scale byte = unit / 8); columnwise planes by
+// kDeqRows rows x 256 columns, each lane reading its 4 columns' scale bytes
+// once.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -25,76 +27,68 @@ __device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t ta
   return lo;
 }
 
-// Decode 8 bytes with per-element scales sc[0..7] and store them at element e.
-__device__ __forceinline__ void put8(void* out, bool bf16, int64_t e, u32x2 q,
+// Decode the 4 bytes of q with per-element scales sc[0..3] and store them at
+// element e (16 bytes of float32 or 8 bytes of bf16 per lane, so each store
+// instruction writes one contiguous span across the wave).
+__device__ __forceinline__ void put4(void* out, bool bf16, int64_t e, uint32_t q,
                                      const float* sc) {
-  float f[8];
+  float f[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    f[k] = decode_e4m3((q.x >> (8 * k)) & 0xFFu, sc[k]);
-    f[k + 4] = decode_e4m3((q.y >> (8 * k)) & 0xFFu, sc[k + 4]);
-  }
+  for (int k = 0; k < 4; ++k) f[k] = decode_e4m3((q >> (8 * k)) & 0xFFu, sc[k]);
   if (bf16) {
-    u32x4 w;
-    w.x = f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16);
-    w.y = f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16);
-    w.z = f32_to_bf16(f[4]) | (f32_to_bf16(f[5]) << 16);
-    w.w = f32_to_bf16(f[6]) | (f32_to_bf16(f[7]) << 16);
-    store16(reinterpret_cast<uint16_t*>(out) + e, w);
+    const u32x2 w = {f32_to_bf16(f[0]) | (f32_to_bf16(f[1]) << 16),
+                     f32_to_bf16(f[2]) | (f32_to_bf16(f[3]) << 16)};
+    store8(reinterpret_cast<uint16_t*>(out) + e, w);
   } else {
-    u32x4 a, b;
-    a.x = __builtin_bit_cast(uint32_t, f[0]); a.y = __builtin_bit_cast(uint32_t, f[1]);
-    a.z = __builtin_bit_cast(uint32_t, f[2]); a.w = __builtin_bit_cast(uint32_t, f[3]);
-    b.x = __builtin_bit_cast(uint32_t, f[4]); b.y = __builtin_bit_cast(uint32_t, f[5]);
-    b.z = __builtin_bit_cast(uint32_t, f[6]); b.w = __builtin_bit_cast(uint32_t, f[7]);
-    float* o = reinterpret_cast<float*>(out) + e;
-    store16(o, a);
-    store16(o + 4, b);
+    const u32x4 w = {__builtin_bit_cast(uint32_t, f[0]), __builtin_bit_cast(uint32_t, f[1]),
+                     __builtin_bit_cast(uint32_t, f[2]), __builtin_bit_cast(uint32_t, f[3])};
+    store16(reinterpret_cast<float*>(out) + e, w);
   }
 }
 
+// Rowwise planes, walked flat in 4-element units: unit u of a wave task is
+// lane + 64 u, so every load and store instruction covers contiguous memory.
 __device__ void deq_flat_task(const DeqDesc& d, bool bf16, int64_t task, int lane) {
-  const int64_t nchunks = d.rows * d.cols / kChunk;
-  const int64_t base = task * (int64_t)(kWave * kFlatUnroll) + lane;
-  u32x2 q[kFlatUnroll];
-  uint32_t s[kFlatUnroll];
+  const int64_t nunits = d.rows * d.cols / 4;
+  const int64_t base = task * (int64_t)(kWave * kDeqUnroll) + lane;
+  uint32_t q[kDeqUnroll], s[kDeqUnroll];
 #pragma unroll
-  for (int u = 0; u < kFlatUnroll; ++u) {
-    int64_t c = base + u * kWave;
-    bool ok = c < nchunks;
-    q[u] = ok ? load8(d.q + c * kChunk) : u32x2{0, 0};
-    s[u] = ok ? d.s[c >> 2] : 0u;
+  for (int u = 0; u < kDeqUnroll; ++u) {
+    const int64_t p = base + u * kWave;
+    const bool ok = p < nunits;
+    q[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(d.q) + p) : 0u;
+    s[u] = ok ? d.s[p >> 3] : 0u;                    // 8 units per 32-element block
   }
 #pragma unroll
-  for (int u = 0; u < kFlatUnroll; ++u) {
-    int64_t c = base + u * kWave;
-    if (c < nchunks) {
-      float sv = e8m0_value(s[u]);
-      const float sc[8] = {sv, sv, sv, sv, sv, sv, sv, sv};
-      put8(d.out, bf16, c * kChunk, q[u], sc);
+  for (int u = 0; u < kDeqUnroll; ++u) {
+    const int64_t p = base + u * kWave;
+    if (p < nunits) {
+      const float sv = e8m0_value(s[u]);
+      const float sc[4] = {sv, sv, sv, sv};
+      put4(d.out, bf16, p * 4, q[u], sc);
     }
   }
 }
 
+// Columnwise planes: kDeqRows rows x 256 columns per wave task; lane l owns
+// columns 4l .. 4l+3 and reads their scale bytes once.
 __device__ void deq_col_task(const DeqDesc& d, bool bf16, int64_t task, int lane) {
   const int64_t cols = d.cols;
-  const int64_t col_tiles = (cols + kTileCols - 1) / kTileCols;
+  const int64_t col_tiles = (cols + kDeqTileCols - 1) / kDeqTileCols;
   const int64_t r0 = (task / col_tiles) * kDeqRows;
-  const int64_t c = (task % col_tiles) * kTileCols + (int64_t)lane * kChunk;
-  if (c >= cols) return;
+  const int64_t c = (task % col_tiles) * kDeqTileCols + (int64_t)lane * 4;
+  if (c >= cols) return;                              // cols % 8 == 0: whole units only
   // rows r0 .. r0 + kDeqRows - 1 lie in one 32-row block (kDeqRows divides 32)
-  u32x2 sb = load8(d.s + (r0 / kBlock) * cols + c);
-  float sc[8];
+  const uint32_t sb = *reinterpret_cast<const uint32_t*>(d.s + (r0 / kBlock) * cols + c);
+  float sc[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    sc[k] = e8m0_value((sb.x >> (8 * k)) & 0xFFu);
-    sc[k + 4] = e8m0_value((sb.y >> (8 * k)) & 0xFFu);
-  }
+  for (int k = 0; k < 4; ++k) sc[k] = e8m0_value((sb >> (8 * k)) & 0xFFu);
+  uint32_t q[kDeqRows];
 #pragma unroll
-  for (int r = 0; r < kDeqRows; ++r) {
-    const int64_t e = (r0 + r) * cols + c;
-    put8(d.out, bf16, e, load8(d.q + e), sc);
-  }
+  for (int r = 0; r < kDeqRows; ++r)
+    q[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(d.q + (r0 + r) * cols + c));
+#pragma unroll
+  for (int r = 0; r < kDeqRows; ++r) put4(d.out, bf16, (r0 + r) * cols + c, q[r], sc);
 }
 
 __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const DeqArgs a) {
@@ -116,11 +110,11 @@ __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const DeqArg
 int64_t deq_tasks(const DeqDesc& d) {
   if (d.rows == 0 || d.cols == 0) return 0;
   if (d.axis == 0) {
-    const int64_t chunks = d.rows * d.cols / kChunk;
-    const int64_t per = (int64_t)kWave * kFlatUnroll;
-    return (chunks + per - 1) / per;
+    const int64_t units = d.rows * d.cols / 4;
+    const int64_t per = (int64_t)kWave * kDeqUnroll;
+    return (units + per - 1) / per;
   }
-  return (d.rows / kDeqRows) * ((d.cols + kTileCols - 1) / kTileCols);
+  return (d.rows / kDeqRows) * ((d.cols + kDeqTileCols - 1) / kDeqTileCols);
 }
 
 hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s) {

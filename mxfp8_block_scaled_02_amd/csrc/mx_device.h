@@ -47,6 +47,26 @@ __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
       __builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b)));
 }
 
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_min_i16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(
+      __builtin_bit_cast(v2s16, a), __builtin_bit_cast(v2s16, b)));
+}
+
+// Both bf16 halves of w with their magnitude clamped to the halves of lim
+// (each <= 0x7FFF), signs kept; NaN and Inf clamp like large numbers.  As
+// unsigned 16-bit values negatives lie above 0x8000, so min_u16 against
+// 0x8000 | lim clamps the negatives and passes the positives; as signed
+// values the positives are the larger ones, so min_i16 against lim then
+// clamps the positives and passes the (clamped) negatives.
+__device__ __forceinline__ uint32_t clamp_mag(uint32_t w, uint32_t lim) {
+  return pk_min_i16(pk_min_u16(w, lim | 0x80008000u), lim);
+}
+
+// float32 values of the low and high bf16 halves of a dword.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
 // Magnitude bits of both halves of a bf16 pair.
 __device__ __forceinline__ uint32_t mag2(uint32_t w) { return w & 0x7FFF7FFFu; }
 
@@ -65,50 +85,53 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t k) {
   return k;
 }
 
-// E8M0 scale byte from a block's magnitude key.  For a finite key the bf16
-// exponent field key >> 7 is floor(log2 amax) + 127 (bf16 subnormals and
-// zero have field 0 and land on the clamp), so S = field - 8, clamped at 0.
-__device__ __forceinline__ uint32_t scale_byte(uint32_t key) {
-  int s = (int)(key >> 7) - 8;
-  s = s < 0 ? 0 : s;
-  return key >= 0x7F80u ? 0xFFu : (uint32_t)s;
-}
-
 // ---- rowwise encode: one scale for the whole chunk ------------------------
 
 struct RowScale {
-  float div;      // 2^(S - 127) as float32 (S == 0: the subnormal 2^-127)
+  float div;      // 2^(S - 127) as float32 bits S << 23 (S == 0 gives +0.0, which the
+                  // conversion reads, like every scale operand, by its exponent field)
   uint32_t lim2;  // bf16 magnitude of 448 * 2^(S - 127), in both halves
   uint32_t nan4;  // 0x7F7F7F7F for a NaN/Inf block, else 0
+  uint32_t sbyte; // the stored scale byte (0xFF for a NaN/Inf block)
 };
 
-__device__ __forceinline__ RowScale row_scale(uint32_t s) {
-  // A NaN/Inf block is converted with the finite stand-in scale 2^0: the
-  // clamp below maps NaN/Inf magnitudes to 448 with their own sign, and nan4
-  // then turns every byte into sign | 0x7F.
-  const uint32_t se = s == 0xFFu ? 127u : s;
+// Scale parameters of a block from its magnitude key.  A NaN/Inf block is
+// converted with the finite stand-in key 0x7F7F: the clamp then maps its
+// NaN/Inf magnitudes to 448 with their own sign, and nan4 turns every byte
+// into sign | 0x7F.
+__device__ __forceinline__ RowScale row_scale_key(uint32_t key) {
+  const uint32_t e = min(key, 0x7F7Fu) >> 7;     // bf16 exponent field
+  const uint32_t s = e > 8u ? e - 8u : 0u;
+  const bool nan = key >= 0x7F80u;
   RowScale r;
-  r.div = __builtin_bit_cast(float, se ? (se << 23) : 0x00400000u);
-  uint32_t lim = ((se + 8u) << 7) | 0x60u;  // 1.75 * 2^(S + 8 - 127) as bf16
+  r.div = __builtin_bit_cast(float, s << 23);
+  const uint32_t lim = (max(e, 8u) << 7) | 0x60u;  // 1.75 * 2^(S + 8 - 127) as bf16
   r.lim2 = lim | (lim << 16);
-  r.nan4 = s == 0xFFu ? 0x7F7F7F7Fu : 0u;
+  r.nan4 = nan ? 0x7F7F7F7Fu : 0u;
+  r.sbyte = nan ? 0xFFu : s;
   return r;
 }
 
 // Two e4m3 bytes of a bf16 pair (low byte = low half) in the low 16 bits.
 template <bool HI>
 __device__ __forceinline__ v2i16 cvt_pair(uint32_t w, const RowScale& rs, v2i16 old) {
-  uint32_t clamped = (w & 0x80008000u) | pk_min_u16(mag2(w), rs.lim2);
   return __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
-      old, __builtin_bit_cast(v2bf16, clamped), rs.div, HI);
+      old, __builtin_bit_cast(v2bf16, clamp_mag(w, rs.lim2)), rs.div, HI);
+}
+
+// Same, for the low half of a fresh dword: the input's own register serves
+// as the (fully overwritten) old value, so no zero has to be materialized.
+__device__ __forceinline__ v2i16 cvt_pair_first(uint32_t w, const RowScale& rs) {
+  const uint32_t c = clamp_mag(w, rs.lim2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      __builtin_bit_cast(v2i16, c), __builtin_bit_cast(v2bf16, c), rs.div, false);
 }
 
 // 8 e4m3 bytes of a chunk, in element order.
 __device__ __forceinline__ u32x2 encode_chunk_row(const u32x4& v, const RowScale& rs) {
-  v2i16 z = {0, 0};
-  v2i16 a = cvt_pair<false>(v.x, rs, z);
+  v2i16 a = cvt_pair_first(v.x, rs);
   a = cvt_pair<true>(v.y, rs, a);
-  v2i16 b = cvt_pair<false>(v.z, rs, z);
+  v2i16 b = cvt_pair_first(v.z, rs);
   b = cvt_pair<true>(v.w, rs, b);
   u32x2 r;
   r.x = __builtin_bit_cast(uint32_t, a) | rs.nan4;
@@ -116,42 +139,95 @@ __device__ __forceinline__ u32x2 encode_chunk_row(const u32x4& v, const RowScale
   return r;
 }
 
-// ---- columnwise encode: one scale per element column ----------------------
-
-// 2^(127 - S) as float32 (S <= 246 for any finite bf16 block); a NaN/Inf
-// column (S = 0xFF) gets 1.0, its elements having been reduced to signed
-// zeros by the caller before conversion.
-__device__ __forceinline__ float col_mul(uint32_t s) {
-  return s == 0xFFu ? 1.0f : __builtin_bit_cast(float, (uint32_t)(254 - (int)s) << 23);
+// Largest magnitude key among 16 bf16 values (two chunks).
+__device__ __forceinline__ uint32_t chunk16_key(const u32x4& a, const u32x4& b) {
+  uint32_t m = pk_max_u16(pk_max_u16(pk_max_u16(mag2(a.x), mag2(a.y)),
+                                     pk_max_u16(mag2(a.z), mag2(a.w))),
+                          pk_max_u16(pk_max_u16(mag2(b.x), mag2(b.y)),
+                                     pk_max_u16(mag2(b.z), mag2(b.w))));
+  return max(m & 0xFFFFu, m >> 16);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
-__device__ __forceinline__ float clamp448(float v) {
-  return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+// Max over each aligned lane pair (a 32-element block when each lane holds
+// 16 consecutive elements), one DPP quad permute.
+__device__ __forceinline__ uint32_t pair_max(uint32_t k) {
+  return max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
 }
 
-// Two e4m3 bytes of a bf16 pair whose halves have their own multipliers.
-template <bool HI>
-__device__ __forceinline__ int cvt_pair_cols(uint32_t w, float m_lo, float m_hi, int old) {
-  return __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(bf16_lo(w) * m_lo),
-                                         clamp448(bf16_hi(w) * m_hi), old, HI);
+// 16 e4m3 bytes of two chunks sharing one block scale.
+__device__ __forceinline__ u32x4 encode_chunk16_row(const u32x4& a, const u32x4& b,
+                                                    const RowScale& rs) {
+  const u32x2 lo = encode_chunk_row(a, rs);
+  const u32x2 hi = encode_chunk_row(b, rs);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
-// 8 e4m3 bytes of a chunk whose 8 columns have multipliers m[0..7];
-// nan8 holds 0x7F in the byte of every NaN/Inf column, whose input halves
-// must already be reduced to their sign bit.
-__device__ __forceinline__ u32x2 encode_chunk_cols(const u32x4& v, const float* m,
-                                                   u32x2 nan8) {
-  int a = cvt_pair_cols<false>(v.x, m[0], m[1], 0);
-  a = cvt_pair_cols<true>(v.y, m[2], m[3], a);
-  int b = cvt_pair_cols<false>(v.z, m[4], m[5], 0);
-  b = cvt_pair_cols<true>(v.w, m[6], m[7], b);
-  u32x2 r;
-  r.x = (uint32_t)a | nan8.x;
-  r.y = (uint32_t)b | nan8.y;
-  return r;
+// ---- columnwise encode on row pairs ----------------------------------------
+//
+// A lane holds rows r, r+1 of columns 2j, 2j+1 as two bf16-pair dwords.  The
+// two rows of one column are gathered into one dword (v_perm_b32), converted
+// with that column's scale by v_cvt_scalef32_pk_fp8_bf16, and the resulting
+// bytes are permuted back into row order.
+
+// Packed per-column parameters for the two columns of pair-dword j.
+struct ColPair {
+  uint32_t lim;     // bf16 clamp magnitudes (low half: column 2j, high: 2j+1)
+  float div_lo;     // scale operands 2^(S - 127) of the two columns
+  float div_hi;
+  uint32_t nanff;   // 0x00FF in each half whose column holds a NaN/Inf
+  uint32_t sbytes;  // stored scale bytes in each half (0xFF for NaN/Inf)
+};
+
+__device__ __forceinline__ uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(
+      __builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b)));
+}
+__device__ __forceinline__ uint32_t pk_shr_u16(uint32_t a, int n) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, a) >> (unsigned short)n);
+}
+__device__ __forceinline__ uint32_t pk_shl_u16(uint32_t a, int n) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2u16, a) << (unsigned short)n);
+}
+
+// Column parameters from the packed magnitude keys of two columns; the same
+// rule as row_scale_key, two columns per operation.
+__device__ __forceinline__ ColPair col_pair(uint32_t keys) {
+  const uint32_t e = pk_shr_u16(pk_min_u16(keys, 0x7F7F7F7Fu), 7);
+  const uint32_t s = pk_sub_sat_u16(e, 0x00080008u);
+  ColPair c;
+  c.lim = pk_shl_u16(pk_max_u16(e, 0x00080008u), 7) | 0x00600060u;
+  c.div_lo = __builtin_bit_cast(float, s << 23);
+  c.div_hi = __builtin_bit_cast(float, (s >> 16) << 23);
+  // a half is NaN/Inf iff its key exceeds 0x7F7F; such a column is clamped
+  // to magnitude 0, leaving each element's sign for the final sign | 0x7F
+  c.nanff = pk_min_u16(pk_shl_u16(pk_sub_sat_u16(keys, 0x7F7F7F7Fu), 8), 0x00FF00FFu);
+  c.lim &= ~(c.nanff | (c.nanff << 8));
+  c.sbytes = pk_max_u16(s, c.nanff);
+  return c;
+}
+
+
+// e4m3 bytes of rows r (wr) and r+1 (wr1) for the four columns of pair-dwords
+// j and j+1: returns {row r dword, row r+1 dword}.
+__device__ __forceinline__ u32x2 encode_col_quad(uint32_t wr_a, uint32_t wr1_a,
+                                                 uint32_t wr_b, uint32_t wr1_b,
+                                                 const ColPair& pa, const ColPair& pb) {
+  const uint32_t ca = clamp_mag(wr_a, pa.lim), ca1 = clamp_mag(wr1_a, pa.lim);
+  const uint32_t cb = clamp_mag(wr_b, pb.lim), cb1 = clamp_mag(wr1_b, pb.lim);
+  // column 2j: rows r, r+1 (low halves); column 2j+1: high halves
+  const uint32_t pa0 = __builtin_amdgcn_perm(ca1, ca, 0x05040100u);
+  const uint32_t pb0 = __builtin_amdgcn_perm(cb1, cb, 0x05040100u);
+  v2i16 da = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      __builtin_bit_cast(v2i16, pa0), __builtin_bit_cast(v2bf16, pa0), pa.div_lo, false);
+  da = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      da, __builtin_bit_cast(v2bf16, __builtin_amdgcn_perm(ca1, ca, 0x07060302u)), pa.div_hi, true);
+  v2i16 db = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      __builtin_bit_cast(v2i16, pb0), __builtin_bit_cast(v2bf16, pb0), pb.div_lo, false);
+  db = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      db, __builtin_bit_cast(v2bf16, __builtin_amdgcn_perm(cb1, cb, 0x07060302u)), pb.div_hi, true);
+  // da bytes: (r,c0) (r+1,c0) (r,c1) (r+1,c1); db likewise for c2, c3
+  const uint32_t ua = __builtin_bit_cast(uint32_t, da), ub = __builtin_bit_cast(uint32_t, db);
+  return u32x2{__builtin_amdgcn_perm(ub, ua, 0x06040200u), __builtin_amdgcn_perm(ub, ua, 0x07050301u)};
 }
 
 // ---- decode ----------------------------------------------------------------
@@ -192,18 +268,26 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 }
 
 // ---- memory ----------------------------------------------------------------
+//
+// Every tensor the kernels stream is touched once, so loads and stores carry
+// the nontemporal hint (global_load/store ... nt): the lines are not kept in
+// the caches for reuse that never comes.  Data that is reused (gamma) goes
+// through load16_cached.
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ u32x2 load8(const void* p) {
-  return *reinterpret_cast<const u32x2*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ u32x4 load16_cached(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void store8(void* p, u32x2 v) {
-  *reinterpret_cast<u32x2*>(p) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
 }
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
-  *reinterpret_cast<u32x4*>(p) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -16,11 +16,14 @@ namespace mx {
 constexpr int kGroupMax = 64;        // tensors per launch (argument block < 4 KiB)
 constexpr int kWavesPerGroup = 4;    // waves per workgroup
 constexpr int kThreads = 64 * kWavesPerGroup;
-constexpr int kFlatUnroll = 4;       // 16-byte chunks per lane per flat task
+constexpr int kLaneCols = 8;         // consecutive row elements a lane holds (8 or 16)
+constexpr int kFlatUnroll = 4;       // kLaneCols-element pieces per lane per flat task
 constexpr int kTileRows = 32;        // rows of a row+column tile (one MX block)
 constexpr int kRowsPerWave = kTileRows / kWavesPerGroup;
-constexpr int kTileCols = 512;       // columns of a tile: 64 lanes x 8
+constexpr int kTileCols = 64 * kLaneCols;  // columns of a tile
+constexpr int kDeqUnroll = 8;        // 4-element units per lane per flat dequantize task
 constexpr int kDeqRows = 4;          // rows per columnwise dequantize task
+constexpr int kDeqTileCols = 256;    // columns per columnwise dequantize task: 64 lanes x 4
 
 // ---- quantize ------------------------------------------------------------
 struct QuantDesc {
@@ -36,8 +39,9 @@ struct QuantArgs {
   int32_t task_start[kGroupMax + 1];
   QuantDesc d[kGroupMax];
 };
-// Workgroup tasks a tensor needs: 32 x 512 tiles when a columnwise plane is
-// requested, otherwise 256 x kFlatUnroll chunks of the flattened tensor.
+// Workgroup tasks a tensor needs: 32 x 1024 tiles when a columnwise plane is
+// requested, otherwise 256 x kFlatUnroll 16-element pieces of the flattened
+// tensor.
 int64_t quant_tasks(const QuantDesc& d);
 hipError_t launch_quantize(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
 
@@ -57,10 +61,12 @@ struct NormArgs {
   NormDesc d[kGroupMax];
 };
 // Kernel shape for the longest row of a launch: waves per row and chunks
-// per lane (see rmsnorm_quantize.hip).  One task per row.
+// per lane (see rmsnorm_quantize.hip).  A task is rows_per_task consecutive
+// rows of one tensor, chosen from the launch's total row count.
 int norm_variant(int64_t cols);
+int norm_rows_per_task(int64_t total_rows, int variant);
 hipError_t launch_rmsnorm_quantize(const NormArgs& a, int64_t total_tasks, int variant,
-                                   hipStream_t s);
+                                   int rows_per_task, hipStream_t s);
 
 // ---- dequantize ----------------------------------------------------------
 struct DeqDesc {

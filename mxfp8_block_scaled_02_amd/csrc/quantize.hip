@@ -8,18 +8,18 @@
 //              _block_atomic_to_flat); q_col keeps x's layout, so the
 //              "columnwise" direction is only the direction of the reduction.
 //
-// Two workgroup-task shapes (4 waves, 256 lanes), both HBM-streaming with
-// 16-byte loads per lane:
+// Two workgroup-task shapes (4 waves, 256 lanes).  A lane holds kLaneCols = 8
+// consecutive elements of a row (one 16-byte load, so every load instruction
+// reads 1 KiB of contiguous memory), and a rowwise block is a lane quad whose
+// amax takes two DPP steps.
 //   flat  (rowwise only): the tensor is a flat array whose 32-element blocks
-//         are contiguous and whose scale array is in block order, so a
-//         workgroup walks 256 x kFlatUnroll consecutive 16-byte chunks; a lane
-//         quad holds one block and reduces its amax with two DPP steps.
+//         are contiguous and whose scale array is in block order; a workgroup
+//         walks 256 x kFlatUnroll consecutive 8-element pieces.
 //   tile  (any columnwise request): a workgroup owns a 32 x 512 tile, each
-//         wave 8 of its rows, each lane 8 rows x 8 columns in registers.
-//         Rowwise blocks are lane quads of one row.  A columnwise block is one
-//         lane column across the 4 waves: each wave reduces its 8 rows in
-//         registers and the 4 partial maxima meet in 4 KiB of LDS.  The tile
-//         is read from HBM once for both planes.
+//         wave 8 of its rows, each lane 8 rows x 8 columns in registers.  A
+//         columnwise block is one lane column across the 4 waves: each wave
+//         reduces its 8 rows in registers and the partial maxima meet in
+//         4 KiB of LDS.  The tile is read from HBM once for both planes.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -36,23 +36,39 @@ __device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t ta
   return lo;
 }
 
+constexpr u32x4 kZero4 = {0, 0, 0, 0};
+constexpr int kCh = kLaneCols / kChunk;     // 16-byte chunks per lane per row (1 or 2)
+
+// Rowwise scale parameters of the block that holds this lane's kLaneCols
+// elements (a lane quad for 8 columns per lane, a lane pair for 16).
+__device__ __forceinline__ RowScale lane_row_scale(const u32x4* v) {
+  if constexpr (kCh == 1)
+    return row_scale_key(quad_max(chunk_key(v[0])));
+  else
+    return row_scale_key(pair_max(chunk16_key(v[0], v[1])));
+}
+
 __device__ void quant_flat_task(const QuantDesc& d, int64_t task, int tid) {
-  const int64_t nchunks = d.rows * d.cols / kChunk;
+  const int64_t npieces = d.rows * d.cols / kLaneCols;   // whole blocks: cols % 32 == 0
   const int64_t base = task * (int64_t)(kThreads * kFlatUnroll) + tid;
-  u32x4 v[kFlatUnroll];
+  u32x4 v[kFlatUnroll][kCh];
 #pragma unroll
   for (int u = 0; u < kFlatUnroll; ++u) {
-    int64_t c = base + u * kThreads;
-    v[u] = c < nchunks ? load16(d.x + c * kChunk) : u32x4{0, 0, 0, 0};
+    const int64_t p = base + u * kThreads;
+#pragma unroll
+    for (int h = 0; h < kCh; ++h)
+      v[u][h] = p < npieces ? load16(d.x + p * kLaneCols + h * kChunk) : kZero4;
   }
 #pragma unroll
   for (int u = 0; u < kFlatUnroll; ++u) {
-    int64_t c = base + u * kThreads;
-    uint32_t s = scale_byte(quad_max(chunk_key(v[u])));
-    u32x2 q = encode_chunk_row(v[u], row_scale(s));
-    if (c < nchunks) {
-      store8(d.q_row + c * kChunk, q);
-      if ((tid & 3) == 0) d.s_row[c >> 2] = (uint8_t)s;
+    const int64_t p = base + u * kThreads;
+    const RowScale rs = lane_row_scale(v[u]);
+    if (p < npieces) {
+#pragma unroll
+      for (int h = 0; h < kCh; ++h)
+        store8(d.q_row + p * kLaneCols + h * kChunk, encode_chunk_row(v[u][h], rs));
+      if ((tid & (kBlock / kLaneCols - 1)) == 0)
+        d.s_row[p * kLaneCols / kBlock] = (uint8_t)rs.sbyte;
     }
   }
 }
@@ -63,91 +79,102 @@ __device__ void quant_tile_task(const QuantDesc& d, int64_t task, int wave, int 
   const int64_t col_tiles = (cols + kTileCols - 1) / kTileCols;
   const int64_t rb = task / col_tiles;                       // 32-row block index
   const int64_t r0 = rb * kTileRows + wave * kRowsPerWave;    // this wave's first row
-  const int64_t c = (task % col_tiles) * kTileCols + (int64_t)lane * kChunk;
-  const bool active = c < cols;
+  const int64_t c = (task % col_tiles) * kTileCols + (int64_t)lane * kLaneCols;
+  bool ok[kCh];                                              // chunk h: columns c + 8h ..
+#pragma unroll
+  for (int h = 0; h < kCh; ++h) ok[h] = c + h * kChunk < cols;
   const uint16_t* xp = d.x + r0 * cols + c;
 
-  u32x4 v[kRowsPerWave];
+  u32x4 v[kRowsPerWave][kCh];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r)
-    v[r] = active ? load16(xp + r * cols) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < kCh; ++h)
+      v[r][h] = ok[h] ? load16(xp + r * cols + h * kChunk) : kZero4;
 
   if (d.q_row) {
+    // cols % 32 == 0 here, so a block's lanes are either all present or absent
     const int64_t sb_per_row = cols / kBlock;
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
-      uint32_t s = scale_byte(quad_max(chunk_key(v[r])));
-      u32x2 q = encode_chunk_row(v[r], row_scale(s));
-      if (active) {
-        store8(d.q_row + (r0 + r) * cols + c, q);
-        if ((lane & 3) == 0) d.s_row[(r0 + r) * sb_per_row + (c >> 5)] = (uint8_t)s;
+      const RowScale rs = lane_row_scale(v[r]);
+      if (ok[0]) {
+#pragma unroll
+        for (int h = 0; h < kCh; ++h)
+          store8(d.q_row + (r0 + r) * cols + c + h * kChunk, encode_chunk_row(v[r][h], rs));
+        if ((lane & (kBlock / kLaneCols - 1)) == 0)
+          d.s_row[(r0 + r) * sb_per_row + (c >> 5)] = (uint8_t)rs.sbyte;
       }
     }
   }
 
   if (d.q_col) {
-    // packed column maxima: word k holds columns 2k (low half) and 2k+1 (high half)
-    u32x4 m = {0, 0, 0, 0};
+    // packed column maxima: word j of chunk h holds columns c + 8h + 2j, + 1
+    u32x4 m[kCh];
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      m.x = pk_max_u16(m.x, mag2(v[r].x));
-      m.y = pk_max_u16(m.y, mag2(v[r].y));
-      m.z = pk_max_u16(m.z, mag2(v[r].z));
-      m.w = pk_max_u16(m.w, mag2(v[r].w));
+    for (int h = 0; h < kCh; ++h) {
+      m[h] = kZero4;
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[h][j] = pk_max_u16(m[h][j], mag2(v[r][h][j]));
+      colmax[(wave * kWave + lane) * kCh + h] = m[h];
     }
-    colmax[wave * kWave + lane] = m;
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWavesPerGroup; ++w) {
       if (w == wave) continue;
-      const u32x4 o = colmax[w * kWave + lane];
-      m.x = pk_max_u16(m.x, o.x);
-      m.y = pk_max_u16(m.y, o.y);
-      m.z = pk_max_u16(m.z, o.z);
-      m.w = pk_max_u16(m.w, o.w);
-    }
-    const uint32_t keys[8] = {m.x & 0xFFFFu, m.x >> 16, m.y & 0xFFFFu, m.y >> 16,
-                              m.z & 0xFFFFu, m.z >> 16, m.w & 0xFFFFu, m.w >> 16};
-    uint32_t sb[8];
-    float mul[8];
-    bool any_nan = false;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sb[k] = scale_byte(keys[k]);
-      mul[k] = col_mul(sb[k]);
-      any_nan |= sb[k] == 0xFFu;
-    }
-    u32x2 nan8;
-    nan8.x = (sb[0] == 0xFFu ? 0x7Fu : 0u) | (sb[1] == 0xFFu ? 0x7F00u : 0u) |
-             (sb[2] == 0xFFu ? 0x7F0000u : 0u) | (sb[3] == 0xFFu ? 0x7F000000u : 0u);
-    nan8.y = (sb[4] == 0xFFu ? 0x7Fu : 0u) | (sb[5] == 0xFFu ? 0x7F00u : 0u) |
-             (sb[6] == 0xFFu ? 0x7F0000u : 0u) | (sb[7] == 0xFFu ? 0x7F000000u : 0u);
-    if (active && wave == 0) {
-      u32x2 packed;
-      packed.x = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
-      packed.y = sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24);
-      store8(d.s_col + rb * cols + c, packed);
-    }
-    if (any_nan) {
-      // a NaN/Inf column keeps only each element's sign bit
-      u32x4 keep;
-      keep.x = (sb[0] == 0xFFu ? 0x8000u : 0xFFFFu) | (sb[1] == 0xFFu ? 0x80000000u : 0xFFFF0000u);
-      keep.y = (sb[2] == 0xFFu ? 0x8000u : 0xFFFFu) | (sb[3] == 0xFFu ? 0x80000000u : 0xFFFF0000u);
-      keep.z = (sb[4] == 0xFFu ? 0x8000u : 0xFFFFu) | (sb[5] == 0xFFu ? 0x80000000u : 0xFFFF0000u);
-      keep.w = (sb[6] == 0xFFu ? 0x8000u : 0xFFFFu) | (sb[7] == 0xFFu ? 0x80000000u : 0xFFFF0000u);
+      for (int h = 0; h < kCh; ++h) {
+        const u32x4 o = colmax[(w * kWave + lane) * kCh + h];
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) v[r] &= keep;
+        for (int j = 0; j < 4; ++j) m[h][j] = pk_max_u16(m[h][j], o[j]);
+      }
+    }
+    ColPair cp[kCh][4];
+    u32x2 sb[kCh], nanq[kCh];
+#pragma unroll
+    for (int h = 0; h < kCh; ++h) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cp[h][j] = col_pair(m[h][j]);
+      // scale bytes and NaN bytes of the chunk's 8 columns, in column order
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        sb[h][k] = __builtin_amdgcn_perm(cp[h][2 * k + 1].sbytes, cp[h][2 * k].sbytes, 0x06040200u);
+        nanq[h][k] = __builtin_amdgcn_perm(cp[h][2 * k + 1].nanff, cp[h][2 * k].nanff,
+                                           0x06040200u) & 0x7F7F7F7Fu;
+      }
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int h = 0; h < kCh; ++h)
+        if (ok[h]) store8(d.s_col + rb * cols + c + h * kChunk, sb[h]);
     }
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      u32x2 q = encode_chunk_cols(v[r], mul, nan8);
-      if (active) store8(d.q_col + (r0 + r) * cols + c, q);
+    for (int r = 0; r < kRowsPerWave; r += 2) {
+      uint8_t* qp = d.q_col + (r0 + r) * cols + c;
+#pragma unroll
+      for (int h = 0; h < kCh; ++h) {
+        u32x2 q0, q1;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const u32x2 o = encode_col_quad(v[r][h][2 * k], v[r + 1][h][2 * k],
+                                          v[r][h][2 * k + 1], v[r + 1][h][2 * k + 1],
+                                          cp[h][2 * k], cp[h][2 * k + 1]);
+          q0[k] = o.x | nanq[h][k];
+          q1[k] = o.y | nanq[h][k];
+        }
+        if (ok[h]) {
+          store8(qp + h * kChunk, q0);
+          store8(qp + cols + h * kChunk, q1);
+        }
+      }
     }
   }
 }
 
 __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const QuantArgs a) {
-  __shared__ u32x4 colmax[kThreads];
+  __shared__ u32x4 colmax[kThreads * kCh];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -167,9 +194,9 @@ int64_t quant_tasks(const QuantDesc& d) {
   if (d.rows == 0 || d.cols == 0) return 0;
   if (d.q_col)
     return (d.rows / kTileRows) * ((d.cols + kTileCols - 1) / kTileCols);
-  const int64_t chunks = d.rows * d.cols / kChunk;
+  const int64_t pieces = d.rows * d.cols / kLaneCols;
   const int64_t per = (int64_t)kThreads * kFlatUnroll;
-  return (chunks + per - 1) / per;
+  return (pieces + per - 1) / per;
 }
 
 hipError_t launch_quantize(const QuantArgs& a, int64_t total_tasks, hipStream_t s) {

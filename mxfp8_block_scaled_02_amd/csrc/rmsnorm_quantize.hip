@@ -58,98 +58,135 @@ __device__ __forceinline__ uint32_t norm_pair(uint32_t xw, uint32_t gw, float rs
   return pack_bf16x2(lo, hi);
 }
 
-// Normalize one chunk, store normed, quantize the stored words.
+// Normalize one chunk with its float32 weights w (gamma + offset), store
+// normed, quantize the stored words.
 __device__ __forceinline__ void finish_chunk(const NormDesc& d, int64_t row, int64_t c,
-                                             bool valid, const u32x4& v, float rstd,
-                                             int t) {
-  u32x4 g = valid ? load16(d.gamma + c * kChunk) : u32x4{0, 0, 0, 0};
+                                             bool valid, const u32x4& v, const float* w,
+                                             float rstd, int t) {
   u32x4 y;
-  y.x = norm_pair(v.x, g.x, rstd, d.weight_offset);
-  y.y = norm_pair(v.y, g.y, rstd, d.weight_offset);
-  y.z = norm_pair(v.z, g.z, rstd, d.weight_offset);
-  y.w = norm_pair(v.w, g.w, rstd, d.weight_offset);
-  uint32_t s = scale_byte(quad_max(chunk_key(y)));
-  u32x2 q = encode_chunk_row(y, row_scale(s));
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    y[k] = pack_bf16x2(bf16_lo(v[k]) * rstd * w[2 * k], bf16_hi(v[k]) * rstd * w[2 * k + 1]);
+  const RowScale rs = row_scale_key(quad_max(chunk_key(y)));
+  const u32x2 q = encode_chunk_row(y, rs);
   if (valid) {
     const int64_t e = row * (int64_t)d.cols + c * kChunk;
     store16(d.normed + e, y);
     store8(d.q + e, q);
-    if ((t & 3) == 0) d.s[e >> 5] = (uint8_t)s;
+    if ((t & 3) == 0) d.s[e >> 5] = (uint8_t)rs.sbyte;
+  }
+}
+
+__device__ __forceinline__ void load_weights(const NormDesc& d, int64_t c, bool valid, float* w) {
+  const u32x4 g = valid ? load16_cached(d.gamma + c * kChunk) : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    w[2 * k] = bf16_lo(g[k]) + d.weight_offset;
+    w[2 * k + 1] = bf16_hi(g[k]) + d.weight_offset;
   }
 }
 
 // Sum of a row's partial sums: wave butterfly, then (WPR > 1) the WPR wave
-// totals in wave order through LDS.
+// totals in wave order through LDS.  part holds two slots, alternated by row,
+// so one barrier per row keeps writers of row k+1 off the values of row k.
 template <int WPR>
-__device__ __forceinline__ float row_sum(float acc, int sub, int lane, float* part) {
+__device__ __forceinline__ float row_sum(float acc, int sub, int lane, float* part, int slot) {
   float w = wave_sum(acc);
   if constexpr (WPR == 1) {
     return w;
   } else {
-    if (lane == 0) part[sub] = w;
+    float* p = part + slot * WPR;
+    if (lane == 0) p[sub] = w;
     __syncthreads();
-    float total = part[0];
+    float total = p[0];
 #pragma unroll
-    for (int k = 1; k < WPR; ++k) total += part[k];
+    for (int k = 1; k < WPR; ++k) total += p[k];
     return total;
   }
 }
 
+// Rows first_row, first_row + step, ... (count of them) of one tensor; the
+// row's L = 64 * WPR lanes each hold NCH chunks (chunk j of lane t is chunk
+// t + L j).  The weights gamma + offset stay in registers across the rows.
 template <int WPR, int NCH>
-__device__ void norm_row(const NormDesc& d, int64_t row, int sub, int lane, float* part) {
+__device__ void norm_rows(const NormDesc& d, int64_t first_row, int step, int count,
+                          int sub, int lane, float* part) {
   constexpr int L = kWave * WPR;           // lanes per row
   const int t = sub * kWave + lane;        // this lane's index within the row
   const int64_t nch = d.cols / kChunk;
-  const uint16_t* xr = d.x + row * (int64_t)d.cols;
   const float inv_cols = 1.0f / (float)d.cols;
   if constexpr (NCH > 0) {
-    u32x4 v[NCH];
+    float w[NCH][8];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      int64_t c = t + (int64_t)j * L;
-      v[j] = c < nch ? load16(xr + c * kChunk) : u32x4{0, 0, 0, 0};
+      const int64_t c = t + (int64_t)j * L;
+      load_weights(d, c, c < nch, w[j]);
     }
-    float acc = 0.0f;
+    for (int k = 0; k < count; ++k) {
+      const int64_t row = first_row + (int64_t)k * step;
+      const uint16_t* xr = d.x + row * (int64_t)d.cols;
+      u32x4 v[NCH];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) acc = sumsq_chunk(v[j], acc);
-    const float ss = row_sum<WPR>(acc, sub, lane, part);
-    const float rstd = 1.0f / __builtin_sqrtf(ss * inv_cols + d.eps);
+      for (int j = 0; j < NCH; ++j) {
+        const int64_t c = t + (int64_t)j * L;
+        v[j] = c < nch ? load16(xr + c * kChunk) : u32x4{0, 0, 0, 0};
+      }
+      float acc = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      int64_t c = t + (int64_t)j * L;
-      finish_chunk(d, row, c, c < nch, v[j], rstd, t);
+      for (int j = 0; j < NCH; ++j) acc = sumsq_chunk(v[j], acc);
+      const float ss = row_sum<WPR>(acc, sub, lane, part, k & 1);
+      const float rstd = 1.0f / __builtin_sqrtf(ss * inv_cols + d.eps);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int64_t c = t + (int64_t)j * L;
+        finish_chunk(d, row, c, c < nch, v[j], w[j], rstd, t);
+      }
     }
   } else {
-    float acc = 0.0f;
-    for (int64_t c0 = 0; c0 < nch; c0 += L) {
-      int64_t c = c0 + t;
-      u32x4 v = c < nch ? load16(xr + c * kChunk) : u32x4{0, 0, 0, 0};
-      acc = sumsq_chunk(v, acc);
-    }
-    const float ss = row_sum<WPR>(acc, sub, lane, part);
-    const float rstd = 1.0f / __builtin_sqrtf(ss * inv_cols + d.eps);
-    for (int64_t c0 = 0; c0 < nch; c0 += L) {
-      int64_t c = c0 + t;
-      bool valid = c < nch;
-      u32x4 v = valid ? load16(xr + c * kChunk) : u32x4{0, 0, 0, 0};
-      finish_chunk(d, row, c, valid, v, rstd, t);
+    // rows too long for registers: a cached first pass for the sum, then a
+    // second pass over the (now cache-resident) row
+    for (int k = 0; k < count; ++k) {
+      const int64_t row = first_row + (int64_t)k * step;
+      const uint16_t* xr = d.x + row * (int64_t)d.cols;
+      float acc = 0.0f;
+      for (int64_t c0 = 0; c0 < nch; c0 += L) {
+        const int64_t c = c0 + t;
+        const u32x4 v = c < nch ? load16_cached(xr + c * kChunk) : u32x4{0, 0, 0, 0};
+        acc = sumsq_chunk(v, acc);
+      }
+      const float ss = row_sum<WPR>(acc, sub, lane, part, k & 1);
+      const float rstd = 1.0f / __builtin_sqrtf(ss * inv_cols + d.eps);
+      for (int64_t c0 = 0; c0 < nch; c0 += L) {
+        const int64_t c = c0 + t;
+        const bool valid = c < nch;
+        const u32x4 v = valid ? load16_cached(xr + c * kChunk) : u32x4{0, 0, 0, 0};
+        float w[8];
+        load_weights(d, c, valid, w);
+        finish_chunk(d, row, c, valid, v, w, rstd, t);
+      }
     }
   }
 }
 
-// WPR waves per row (1 or 4), NCH chunks per lane (0: two passes).
+// WPR waves per row (1 or 4), NCH chunks per lane (0: two passes).  A task
+// is rows_per_task consecutive rows of one tensor: with WPR == 4 the whole
+// workgroup walks them in order; with WPR == 1 wave w takes rows w, w + 4, ...
 template <int WPR, int NCH>
-__global__ __launch_bounds__(kThreads) void mxfp8_rmsnorm_quantize_kernel(const NormArgs a) {
-  __shared__ float part[kWavesPerGroup];
-  constexpr int kRowsPerGroup = kWavesPerGroup / WPR;
+__global__ __launch_bounds__(kThreads) void mxfp8_rmsnorm_quantize_kernel(const NormArgs a,
+                                                                         int rows_per_task) {
+  __shared__ float part[2 * kWavesPerGroup];
+  constexpr int kSlots = kWavesPerGroup / WPR;          // row slots per workgroup
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int32_t task = (int32_t)blockIdx.x * kRowsPerGroup + wave / WPR;
-  if (task >= a.task_start[a.n]) return;   // only when WPR == 1: no barrier follows
+  const int32_t task = (int32_t)blockIdx.x;
   const int i = find_desc(a.task_start, a.n, task);
   const NormDesc& d = a.d[i];
-  const int64_t row = task - a.task_start[i];
-  norm_row<WPR, NCH>(d, row, wave % WPR, lane, part);
+  const int64_t row0 = (int64_t)(task - a.task_start[i]) * rows_per_task;
+  const int64_t left = (int64_t)d.rows - row0;
+  const int in_task = (int)(left < rows_per_task ? left : rows_per_task);
+  const int slot = wave / WPR;
+  const int count = (in_task - slot + kSlots - 1) / kSlots;   // rows slot, slot + kSlots, ...
+  norm_rows<WPR, NCH>(d, row0 + slot, kSlots, count, wave % WPR, lane, part);
 }
 
 }  // namespace
@@ -165,20 +202,30 @@ int norm_variant(int64_t cols) {
   return 10;                               // four waves per row, two passes
 }
 
+int norm_rows_per_task(int64_t total_rows, int variant) {
+  // Two rows per row slot once the launch has rows to spare: the weights are
+  // then loaded once per two rows while the grid still covers every CU many
+  // times (measured on the 8192 x 8192 and 65536 x 7168 workloads: 1 and 2
+  // rows per task beat 4 and 8).
+  const int64_t slots = variant < 10 ? kWavesPerGroup : 1;
+  const int64_t g = total_rows >= slots * 8192 ? 2 : 1;
+  return (int)(g * slots);
+}
+
 hipError_t launch_rmsnorm_quantize(const NormArgs& a, int64_t total_tasks, int variant,
-                                   hipStream_t s) {
+                                   int rows_per_task, hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
   const dim3 block(kThreads);
-  const dim3 g1((uint32_t)((total_tasks + kWavesPerGroup - 1) / kWavesPerGroup));
-  const dim3 g4((uint32_t)total_tasks);
+  const dim3 grid((uint32_t)total_tasks);
+  const int r = rows_per_task;
   switch (variant) {
-    case 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<1, 1>), g1, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<1, 2>), g1, block, 0, s, a); break;
-    case 11: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 1>), g4, block, 0, s, a); break;
-    case 12: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 2>), g4, block, 0, s, a); break;
-    case 14: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 4>), g4, block, 0, s, a); break;
-    case 18: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 8>), g4, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 0>), g4, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<1, 1>), grid, block, 0, s, a, r); break;
+    case 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<1, 2>), grid, block, 0, s, a, r); break;
+    case 11: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 1>), grid, block, 0, s, a, r); break;
+    case 12: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 2>), grid, block, 0, s, a, r); break;
+    case 14: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 4>), grid, block, 0, s, a, r); break;
+    case 18: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 8>), grid, block, 0, s, a, r); break;
+    default: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 0>), grid, block, 0, s, a, r); break;
   }
   return hipGetLastError();
 }

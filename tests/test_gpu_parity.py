@@ -256,7 +256,9 @@ def check_fused(orc, x, gamma, off, eps, rows_sel=None, what=""):
 
 
 @pytest.mark.parametrize("shape", [(1, 32), (5, 96), (16, 512), (3, 544), (64, 4096),
-                                   (8, 16384), (4, 16416), (2, 40000)])
+                                   (8, 16384), (4, 16416), (2, 40000),
+                                   # enough rows that a workgroup walks several, last group ragged
+                                   (2051, 96), (4099, 2048), (16411, 4096), (20003, 7168)])
 def test_fused_shapes(orc, shape):
     x, gamma = synth.rmsnorm_inputs(*shape, seed=shape[1], x_std=2.0, row_decades=1.5)
     check_fused(orc, x.to(DEV), gamma.to(DEV), 0.5, 1e-5, what="shape %s" % (shape,))
