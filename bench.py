@@ -52,10 +52,10 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         data = json.load(f)
-    rec = data.get(workload)
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if data.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    rec = data.get("kernels", {}).get(workload)
+    return None if rec is None else round(rec["bytes_per_launch"])
 
 
 class Timed:
@@ -66,14 +66,26 @@ class Timed:
     the GPU's and not Python's per-call overhead.  HIP events on the replay
     stream bracket the replay; the host synchronizes on both sides."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, eager=False):
         self.torch = torch
+        self.eager = eager
 
     def run(self, fn, steps, warmup):
         torch = self.torch
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        if self.eager:
+            # plain launches (for counter collection, one dispatch per call)
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            start.record()
+            for i in range(steps):
+                fn(i)
+            stop.record()
+            torch.cuda.synchronize()
+            return start.elapsed_time(stop) / steps, time.perf_counter() - t0
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
@@ -97,6 +109,9 @@ def rotation(per_set_bytes: int) -> int:
     return max(2, -(-3 * MALL_BYTES // max(per_set_bytes, 1)))
 
 
+EAGER = False
+
+
 def bench_rowcol(torch, mx, synth, steps, warmup):
     dev = torch.device("cuda:0")
     x = synth.workload("rowcol_4096x4096", device=dev)["x"]
@@ -106,7 +121,7 @@ def bench_rowcol(torch, mx, synth, steps, warmup):
     xs = [x.clone() for _ in range(sets)]
     outs = [mx.quantize(xi, True, True) for xi in xs]
     fn = lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets])
-    ms, wall = Timed(torch).run(fn, steps, warmup)
+    ms, wall = Timed(torch, EAGER).run(fn, steps, warmup)
     return {"ms": ms, "bytes": alg, "elems": rows * cols, "sets": sets, "wall_s": wall}
 
 
@@ -114,7 +129,7 @@ def bench_other_rows(torch, mx, synth, steps):
     """Each remaining entry point on its own workload (fewer steps)."""
     dev = torch.device("cuda:0")
     res = {}
-    T = Timed(torch)
+    T = Timed(torch, EAGER)
 
     x = synth.workload("rowwise_256x1024", device=dev)["x"]
     r, c = x.shape
@@ -243,8 +258,10 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int = 256 << 20)
     dispatch in the same run)."""
     fetch = counter_bytes(fetch_csv, "FETCH_SIZE")
     write = counter_bytes(write_csv, "WRITE_SIZE")
-    copy_f = max(max(v) for k, v in fetch.items() if "copy" in k[0].lower())
-    copy_w = max(max(v) for k, v in write.items() if "copy" in k[0].lower())
+    # the runtime's device-to-device copy kernel; its largest dispatch is the
+    # 256 MiB calibration copy
+    copy_f = max(max(v) for k, v in fetch.items() if "copyBuffer" in k[0])
+    copy_w = max(max(v) for k, v in write.items() if "copyBuffer" in k[0])
     f_scale = copy_bytes / (copy_f * 1024.0)
     w_scale = copy_bytes / (copy_w * 1024.0)
     res = {}
@@ -262,7 +279,12 @@ def main():
         print(trace_summary(sys.argv[2]))
         return
     if len(sys.argv) > 3 and sys.argv[1] == "--traffic-summary":
-        print(json.dumps(traffic_summary(sys.argv[2], sys.argv[3]), indent=1))
+        res = traffic_summary(sys.argv[2], sys.argv[3])
+        res["source_hash"] = kernel_source_hash()
+        print(json.dumps(res, indent=1))
+        if "--write" in sys.argv:
+            with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+                json.dump(res, f, indent=1)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +292,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-rows", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="time plain launches instead of one graph replay (counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference that "
                          "scales HBM byte counters")
@@ -279,6 +303,8 @@ def main():
               "communication, so it runs and is reported per GPU (--gpus 1).", file=sys.stderr)
         sys.exit(2)
 
+    global EAGER
+    EAGER = args.eager
     import torch
     import mxfp8_block_scaled_02_amd as mx
     from mxfp8_block_scaled_02_amd import synth
@@ -295,7 +321,8 @@ def main():
     main_run = bench_rowcol(torch, mx, synth, args.steps, args.warmup)
     ms = main_run["ms"]
     gbs = main_run["bytes"] / (ms * 1e-3) / 1e9
-    traffic = measured_traffic("rowcol_4096x4096")
+    # the row+column launch on the 4096 x 4096 weight: (4096/32) x (4096/512) tiles
+    traffic = measured_traffic("mx::mxfp8_quantize_kernel/1024")
     line = {
         "metric": "bf16->MXFP8 quantize GB/s (frac of MI355X HBM peak) + Gelem/s, 1 GPU",
         "value": round(gbs, 1),
