@@ -43,6 +43,17 @@ def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
     return out
 
 
+def _values(x):
+    """bf16 bit patterns (uint16) or float32 values, contiguous; the suffix of
+    the C function that takes them."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x, ""
+    if x.dtype == np.float32:
+        return x, "_f32"
+    raise TypeError("inputs are bf16 bit patterns (uint16) or float32, got %s" % x.dtype)
+
+
 def _bits16(x) -> np.ndarray:
     x = np.ascontiguousarray(x)
     if x.dtype != np.uint16:
@@ -60,6 +71,8 @@ class Oracle:
     _SIGS = {
         "mxfp8_oracle_quantize_rowwise": "p i64 i64 p p",
         "mxfp8_oracle_quantize_colwise": "p i64 i64 p p",
+        "mxfp8_oracle_quantize_rowwise_f32": "p i64 i64 p p",
+        "mxfp8_oracle_quantize_colwise_f32": "p i64 i64 p p",
         "mxfp8_oracle_dequantize": "p p i64 i64 i32 p",
         "mxfp8_oracle_round_bf16": "p i64 p",
         "mxfp8_oracle_rmsnorm_f64": "p p f32 f32 i64 i64 p",
@@ -86,26 +99,28 @@ class Oracle:
     def max_threads(self) -> int:
         return int(self.lib.mxfp8_oracle_max_threads())
 
-    def quantize_rowwise(self, x_bits):
-        """Rowwise plane of bf16 [rows, cols]: (q [rows, cols], s [rows, cols/32])."""
-        x = _bits16(x_bits)
+    def quantize_rowwise(self, x):
+        """Rowwise plane of a [rows, cols] tensor given as bf16 bit patterns
+        (uint16) or float32: (q [rows, cols], s [rows, cols/32])."""
+        x, sfx = _values(x)
         rows, cols = x.shape
         if cols % BLOCK:
             raise ValueError("cols must be a multiple of 32")
         q = np.empty((rows, cols), np.uint8)
         s = np.empty((rows, cols // BLOCK), np.uint8)
-        self.lib.mxfp8_oracle_quantize_rowwise(_ptr(x), rows, cols, _ptr(q), _ptr(s))
+        getattr(self.lib, "mxfp8_oracle_quantize_rowwise" + sfx)(_ptr(x), rows, cols, _ptr(q), _ptr(s))
         return q, s
 
-    def quantize_colwise(self, x_bits):
-        """Columnwise plane of bf16 [rows, cols]: (q [rows, cols], s [rows/32, cols])."""
-        x = _bits16(x_bits)
+    def quantize_colwise(self, x):
+        """Columnwise plane of a [rows, cols] tensor given as bf16 bit patterns
+        (uint16) or float32: (q [rows, cols], s [rows/32, cols])."""
+        x, sfx = _values(x)
         rows, cols = x.shape
         if rows % BLOCK:
             raise ValueError("rows must be a multiple of 32")
         q = np.empty((rows, cols), np.uint8)
         s = np.empty((rows // BLOCK, cols), np.uint8)
-        self.lib.mxfp8_oracle_quantize_colwise(_ptr(x), rows, cols, _ptr(q), _ptr(s))
+        getattr(self.lib, "mxfp8_oracle_quantize_colwise" + sfx)(_ptr(x), rows, cols, _ptr(q), _ptr(s))
         return q, s
 
     def dequantize(self, q, s, axis: int):

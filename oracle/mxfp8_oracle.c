@@ -28,6 +28,8 @@
  *     a scale below 2^-127 is clamped to byte 0x00; a block holding a NaN or
  *     an infinity gets scale byte 0xFF and every element byte sign|0x7F; the
  *     sign of zero is kept.
+ *   - A float32 master weight (quantized_dbuffer page, QuantizedDBuffer.quantize_
+ *     on a local master shard) follows the same rule on its float32 values.
  *   - RMSNorm (Mojo page, "Args": gammas, float32 epsilons, weight_offsets):
  *     y = x / sqrt(mean(x^2) + eps) * (gamma + offset), rounded once to bf16;
  *     the quantized copy is a plain rowwise quantize of that bf16 (Mojo page,
@@ -107,11 +109,10 @@ static uint8_t e4m3_byte(double v) {
     return sign | (uint8_t)(((er + 7) << 3) | mant);
 }
 
-/* Quantize one block of n values (stride apart in x, and in q). */
-static void quantize_block(const uint16_t *x, int64_t stride, int n,
-                           uint8_t *q, uint8_t *s) {
-    double v[MX_BLOCK];
-    for (int i = 0; i < n; ++i) v[i] = bf16_value(x[(int64_t)i * stride]);
+/* Quantize one block of n values v[0..n-1]; element bytes go to q, stride
+ * apart, and the scale byte to *s. */
+static void quantize_values(const double *v, int n, uint8_t *q, int64_t stride,
+                            uint8_t *s) {
     int sb = block_scale_byte(v, n);
     *s = (uint8_t)sb;
     for (int i = 0; i < n; ++i) {
@@ -122,6 +123,22 @@ static void quantize_block(const uint16_t *x, int64_t stride, int n,
             b = e4m3_byte(ldexp(v[i], E8M0_BIAS - sb));
         q[(int64_t)i * stride] = b;
     }
+}
+
+/* One block of bf16 values, stride apart in x (and in q). */
+static void quantize_block(const uint16_t *x, int64_t stride, int n,
+                           uint8_t *q, uint8_t *s) {
+    double v[MX_BLOCK];
+    for (int i = 0; i < n; ++i) v[i] = bf16_value(x[(int64_t)i * stride]);
+    quantize_values(v, n, q, stride, s);
+}
+
+/* One block of float32 values (a float32 master weight), stride apart. */
+static void quantize_block_f32(const float *x, int64_t stride, int n,
+                               uint8_t *q, uint8_t *s) {
+    double v[MX_BLOCK];
+    for (int i = 0; i < n; ++i) v[i] = (double)x[(int64_t)i * stride];
+    quantize_values(v, n, q, stride, s);
 }
 
 /* Rowwise plane: q[r, c] and s[r, c/32] from x[r, 32j .. 32j+31]. */
@@ -145,6 +162,27 @@ void mxfp8_oracle_quantize_colwise(const uint16_t *x, int64_t rows, int64_t cols
         for (int64_t c = 0; c < cols; ++c)
             quantize_block(x + i * MX_BLOCK * cols + c, cols, MX_BLOCK,
                            q + i * MX_BLOCK * cols + c, s + i * cols + c);
+}
+
+/* The same two planes of a float32 tensor. */
+void mxfp8_oracle_quantize_rowwise_f32(const float *x, int64_t rows, int64_t cols,
+                                       uint8_t *q, uint8_t *s) {
+    int64_t nb = cols / MX_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < nb; ++j)
+            quantize_block_f32(x + r * cols + j * MX_BLOCK, 1, MX_BLOCK,
+                               q + r * cols + j * MX_BLOCK, s + r * nb + j);
+}
+
+void mxfp8_oracle_quantize_colwise_f32(const float *x, int64_t rows, int64_t cols,
+                                       uint8_t *q, uint8_t *s) {
+    int64_t nb = rows / MX_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nb; ++i)
+        for (int64_t c = 0; c < cols; ++c)
+            quantize_block_f32(x + i * MX_BLOCK * cols + c, cols, MX_BLOCK,
+                               q + i * MX_BLOCK * cols + c, s + i * cols + c);
 }
 
 /* Value of one float8_e4m3fn byte (NaN for 0x7F / 0xFF). */

@@ -400,6 +400,54 @@ def check_rmsnorm(orc, seed=11):
     assert np.allclose(y[0], want, rtol=1e-14)
 
 
+def f32_blocks(seed=17, nblocks=4096):
+    """float32 blocks: random values over a wide exponent range, plus blocks of
+    exact e4m3 ties and ties +- 1 float32 ulp under an anchor that fixes the
+    scale byte, so the rounding sees every bit of float32 precision."""
+    g = np.random.default_rng(seed)
+    mant = g.uniform(1.0, 2.0, (nblocks, 32))
+    expo = g.integers(-140, 120, (nblocks, 1)) + g.integers(-20, 1, (nblocks, 32))
+    sign = np.where(g.random((nblocks, 32)) < 0.5, -1.0, 1.0)
+    x = (sign * np.ldexp(mant, expo)).astype(np.float32)
+    x[g.random((nblocks, 32)) < 0.02] = 0.0
+    # ties: midpoints of the e4m3 grid at scale 2^0 (anchor 256 -> S = 127)
+    grid = e4m3_decode_table()[:0x7F]
+    mids = (grid[:-1] + grid[1:]) / 2
+    t = []
+    for m in mids:
+        m32 = np.float32(m)
+        t += [m32, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9))]
+    t = np.array(t, np.float32)
+    pad = (-t.size) % 31
+    t = np.concatenate([t, np.zeros(pad, np.float32)]).reshape(-1, 31)
+    anchor = np.full((t.shape[0], 1), 256.0, np.float32)
+    ties = np.concatenate([anchor, t], axis=1)
+    neg = -ties
+    # the same ties at a large and a tiny scale (exact power-of-two shifts)
+    big = np.ldexp(ties.astype(np.float64), 60).astype(np.float32)
+    tiny = np.ldexp(ties.astype(np.float64), -100).astype(np.float32)
+    return np.concatenate([x, ties, neg, big, tiny]).astype(np.float32)
+
+
+def check_f32_input(orc):
+    x = f32_blocks()
+    q, s = orc.quantize_rowwise(x)
+    vals = x.astype(np.float64)
+    check_scale_property(np.abs(vals).max(axis=1), s[:, 0])
+    want = expected_elements(vals, np.repeat(s.astype(np.int64), 32, axis=1))
+    bad = q != want
+    assert not bad.any(), "float32 rowwise: %d mismatches, first x=%r S=%d got %#x want %#x" % (
+        bad.sum(), vals[bad][0], np.repeat(s, 32, 1)[bad][0], q[bad][0], want[bad][0])
+    xt = np.ascontiguousarray(x.T)
+    qc, sc = orc.quantize_colwise(xt)
+    assert (qc == q.T).all() and (sc == s.T).all(), "float32 columnwise != rowwise of transpose"
+    # a bf16-representable float32 tensor quantizes exactly like its bf16 bits
+    b = random_tensors(seed=5, rows=64, cols=64)[2]
+    qb, sb = orc.quantize_rowwise(b)
+    qf, sf = orc.quantize_rowwise(bf16_values(b).astype(np.float32))
+    assert (qb == qf).all() and (sb == sf).all(), "float32 and bf16 paths disagree"
+
+
 QUICK_CHECKS = [
     ("golden", check_golden),
     ("single_value_blocks", lambda o: check_single_value_blocks(o, stride=1)),
@@ -409,4 +457,5 @@ QUICK_CHECKS = [
     ("rmsnorm", check_rmsnorm),
     ("col_is_row_of_transpose", lambda o: check_col_is_row_of_transpose(o, random_tensors(rows=64, cols=64))),
     ("error_bound", lambda o: check_error_bound(o, random_tensors(rows=64, cols=64))),
+    ("f32_input", check_f32_input),
 ]

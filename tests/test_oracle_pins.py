@@ -19,6 +19,10 @@ def test_pair_blocks_every_scale(orc):
     P.check_pair_blocks(orc)
 
 
+def test_float32_input_against_torch_and_ties(orc):
+    P.check_f32_input(orc)
+
+
 def test_dequant_decode_tables(orc):
     P.check_dequant_tables(orc)
 
