@@ -169,6 +169,16 @@ def bench_other_rows(torch, mx, synth, steps):
         res[name] = (ms, alg, r * c)
         del w, o
 
+    x = synth.workload("rowcol_f32_4096x4096", device=dev)["x"]
+    r, c = x.shape
+    alg = r * c * 4 + 2 * r * c + r * c // 32 + (r // 32) * c
+    sets = rotation(alg)
+    xs = [x.clone() for _ in range(sets)]
+    outs = [mx.quantize(xi, True, True) for xi in xs]
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets]), steps, 5)
+    res["rowcol_f32_4096x4096"] = (ms, alg, r * c)
+    del xs, outs
+
     # context: a plain device copy moving the row+column step's input volume
     sets = rotation(2 * (32 << 20))
     srcs = [torch.empty(32 << 20, dtype=torch.uint8, device=dev).fill_(1) for _ in range(sets)]

@@ -105,6 +105,19 @@ mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols,
                             void *stream);
 
 /*
+ * mxfp8_quantize_f32 - mxfp8_quantize for a float32 tensor.
+ *
+ * Quantizes a float32 master weight straight into its planes
+ * (quantized_dbuffer page, QuantizedDBuffer.quantize_ on a local master
+ * shard): the same blocks, scale rule, rounding and plane layouts as
+ * mxfp8_quantize, applied to the float32 values.  x is float32 [rows, cols];
+ * every other argument and rule is mxfp8_quantize's.
+ */
+mxfp8_status mxfp8_quantize_f32(const void *x, int64_t rows, int64_t cols,
+                                void *q_row, void *s_row, void *q_col,
+                                void *s_col, void *stream);
+
+/*
  * mxfp8_rmsnorm_quantize - RMSNorm, then the rowwise plane of its bf16 output.
  *
  * The fused norm-and-quantize of the Mojo DistributedAllGatherRMSNormQuantMXFP8
@@ -179,6 +192,9 @@ typedef struct {
 
 mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc *descs, int32_t n,
                                     void *stream);
+/* Grouped mxfp8_quantize_f32: each descriptor's x points to float32. */
+mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc *descs, int32_t n,
+                                        void *stream);
 mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc *descs,
                                             int32_t n, void *stream);
 mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc *descs, int32_t n,

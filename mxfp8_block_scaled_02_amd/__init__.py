@@ -78,11 +78,13 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_rmsnorm_quantize.argtypes = [p, p, f32, f32, i64, i64, p, p, p, p]
     L.mxfp8_dequantize.argtypes = [p, p, i64, i64, ctypes.c_int, p, ctypes.c_int, p]
     L.mxfp8_quantize_grouped.argtypes = [ctypes.POINTER(_QuantDesc), i32, p]
+    L.mxfp8_quantize_f32.argtypes = [p, i64, i64, p, p, p, p, p]
+    L.mxfp8_quantize_f32_grouped.argtypes = [ctypes.POINTER(_QuantDesc), i32, p]
     L.mxfp8_rmsnorm_quantize_grouped.argtypes = [ctypes.POINTER(_NormDesc), i32, p]
     L.mxfp8_dequantize_grouped.argtypes = [ctypes.POINTER(_DeqDesc), i32, ctypes.c_int, p]
     for name in ("mxfp8_quantize", "mxfp8_rmsnorm_quantize", "mxfp8_dequantize",
                  "mxfp8_quantize_grouped", "mxfp8_rmsnorm_quantize_grouped",
-                 "mxfp8_dequantize_grouped"):
+                 "mxfp8_dequantize_grouped", "mxfp8_quantize_f32", "mxfp8_quantize_f32_grouped"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -145,7 +147,9 @@ def _out(t, shape, dtype, device, name):
 
 
 def _quant_desc(x, rowwise, columnwise, out):
-    x2 = _as2d(x, "x")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("x must be bfloat16 or float32, got %s" % x.dtype)
+    x2 = _as2d(x, "x", x.dtype)
     rows, cols = x2.shape
     o = out or MXFP8Planes(None, None, None, None)
     dev = x.device
@@ -159,33 +163,35 @@ def _quant_desc(x, rowwise, columnwise, out):
 
 def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
              out: Optional[MXFP8Planes] = None) -> MXFP8Planes:
-    """Quantize bf16 x [rows, cols] into the requested planes in one launch.
+    """Quantize x [rows, cols] (bf16, or a float32 master weight) into the
+    requested planes in one launch.
 
     ``out`` supplies persistent plane buffers that are overwritten in place
     (Megatron-Core quantization.utils page, quantize_params_to_mxfp8)."""
     d, planes = _quant_desc(x, rowwise, columnwise, out)
+    fn = lib().mxfp8_quantize if x.dtype == torch.bfloat16 else lib().mxfp8_quantize_f32
     with torch.cuda.device(x.device):
-        _check(lib().mxfp8_quantize(d.x, d.rows, d.cols, d.q_row, d.s_row, d.q_col,
-                                    d.s_col, _stream(x.device)))
+        _check(fn(d.x, d.rows, d.cols, d.q_row, d.s_row, d.q_col, d.s_col, _stream(x.device)))
     return planes
 
 
 def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwise: bool = False,
                      outs: Optional[Sequence[MXFP8Planes]] = None) -> list:
-    """Quantize a list of bf16 tensors of any shapes in one launch."""
+    """Quantize a list of tensors of any shapes (all bf16 or all float32) in one launch."""
     if not xs:
         return []
-    dev = xs[0].device
+    dev, dt = xs[0].device, xs[0].dtype
     descs, planes = [], []
     for i, x in enumerate(xs):
-        if x.device != dev:
-            raise ValueError("all tensors must be on one device")
+        if x.device != dev or x.dtype != dt:
+            raise ValueError("all tensors must share one device and one dtype")
         d, p = _quant_desc(x, rowwise, columnwise, outs[i] if outs else None)
         descs.append(d)
         planes.append(p)
     arr = (_QuantDesc * len(descs))(*descs)
+    fn = lib().mxfp8_quantize_grouped if dt == torch.bfloat16 else lib().mxfp8_quantize_f32_grouped
     with torch.cuda.device(dev):
-        _check(lib().mxfp8_quantize_grouped(arr, len(descs), _stream(dev)))
+        _check(fn(arr, len(descs), _stream(dev)))
     return planes
 
 

@@ -168,6 +168,30 @@ mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc* descs, int32_t n, vo
                     a);
 }
 
+mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc* descs, int32_t n,
+                                        void* stream) {
+  if (n < 0) return MXFP8_ERR_ARG;
+  if (n == 0) return MXFP8_OK;
+  if (!descs) return MXFP8_ERR_NULL;
+  std::vector<mx::QuantDesc> v;
+  v.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (mxfp8_status st = check_quant(descs[i])) return st;
+    v.push_back(to_internal(descs[i]));
+  }
+  mx::QuantArgs a;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run_groups(v, mx::quant_f32_tasks,
+                    [&](const mx::QuantArgs& args, int64_t t) { return mx::launch_quantize_f32(args, t, s); },
+                    a);
+}
+
+mxfp8_status mxfp8_quantize_f32(const void* x, int64_t rows, int64_t cols, void* q_row,
+                                void* s_row, void* q_col, void* s_col, void* stream) {
+  mxfp8_quant_desc d = {x, rows, cols, q_row, s_row, q_col, s_col};
+  return mxfp8_quantize_f32_grouped(&d, 1, stream);
+}
+
 mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, void* q_row,
                             void* s_row, void* q_col, void* s_col, void* stream) {
   mxfp8_quant_desc d = {x, rows, cols, q_row, s_row, q_col, s_col};

@@ -44,6 +44,10 @@ struct QuantArgs {
 // tensor.
 int64_t quant_tasks(const QuantDesc& d);
 hipError_t launch_quantize(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
+// The same for float32 input (QuantDesc::x points to float): 32 x 256 tiles
+// or 256 x kFlatUnroll 4-element pieces.
+int64_t quant_f32_tasks(const QuantDesc& d);
+hipError_t launch_quantize_f32(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
 
 // ---- RMSNorm + rowwise quantize ------------------------------------------
 struct NormDesc {

@@ -1,0 +1,221 @@
+// float32 -> MXFP8 quantize: the planes of a float32 master weight.
+//
+// The same planes and rule as the bf16 quantize (quantize.hip), applied to
+// float32 values: quantizing a local float32 master shard into its planes is
+// the Megatron-Core quantized_dbuffer page's QuantizedDBuffer.quantize_.
+//
+// A lane holds 4 consecutive float32 of a row (one 16-byte load, so every
+// load instruction reads 1 KiB of contiguous memory); a rowwise block is 8
+// lanes and its amax takes three DPP steps.  Tile tasks (any columnwise
+// request) are 32 rows x 256 columns per workgroup, 8 rows per wave; flat
+// tasks (rowwise only) walk 256 x kFlatUnroll pieces of 4 elements.
+//
+// Scaling and rounding use v_cvt_scalef32_pk_fp8_f32 with scale operand
+// 2^(S-127), which divides by the scale and rounds to nearest even; like the
+// bf16 form it turns magnitudes >= 464 into NaN, so every input is first
+// clamped to +-448 * 2^(S-127) with v_med3_f32.  A NaN/Inf block or column is
+// reduced to signed zeros before the clamp (so med3 never sees a NaN) and
+// its bytes become sign | 0x7F.
+#include "mx_device.h"
+#include "mx_kernels.h"
+
+namespace mx {
+
+namespace {
+
+constexpr int kF32Lane = 4;                       // float32 per lane per row
+constexpr int kF32TileCols = kWave * kF32Lane;    // 256
+
+__device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t task) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= task) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr u32x4 kZero4 = {0, 0, 0, 0};
+
+__device__ __forceinline__ uint32_t f32_key4(const u32x4& v) {
+  return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+}
+
+// Max over each aligned group of 8 lanes: two quad permutes, then the mirror
+// within 8 lanes, which pairs lane i with lane 7 - i.
+__device__ __forceinline__ uint32_t oct_max(uint32_t k) {
+  k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+  k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
+  k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x141, 0xF, 0xF, true));  // half mirror
+  return k;
+}
+
+// Scale parameters of a float32 block from its magnitude key (float32 bits
+// & 0x7FFFFFFF).  S = exponent field - 8, clamped at 0; NaN/Inf -> 0xFF.
+struct F32Scale {
+  float div;       // scale operand 2^(S-127) (S == 0: the subnormal 2^-127)
+  float lim;       // 448 * 2^(S-127)
+  uint32_t nan;    // 1 for a NaN/Inf block
+  uint32_t sbyte;  // stored scale byte
+};
+
+__device__ __forceinline__ F32Scale f32_scale_key(uint32_t key) {
+  const uint32_t e = min(key, 0x7F7FFFFFu) >> 23;
+  const uint32_t s = e > 8u ? e - 8u : 0u;
+  F32Scale r;
+  r.div = __builtin_bit_cast(float, s ? (s << 23) : 0x00400000u);
+  r.lim = __builtin_bit_cast(float, (max(e, 8u) << 23) | 0x00600000u);  // 1.75 * 2^(S+8-127)
+  r.nan = key >= 0x7F800000u ? 1u : 0u;
+  r.sbyte = r.nan ? 0xFFu : s;
+  return r;
+}
+
+__device__ __forceinline__ float med(uint32_t bits, float lim) {
+  return __builtin_amdgcn_fmed3f(__builtin_bit_cast(float, bits), -lim, lim);
+}
+
+// 4 e4m3 bytes of 4 float32 sharing one block scale.
+__device__ __forceinline__ uint32_t encode4_row(u32x4 v, const F32Scale& sc) {
+  if (sc.nan) v &= 0x80000000u;   // keep only the signs; the bytes become sign | 0x7F
+  v2i16 a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+      __builtin_bit_cast(v2i16, v.x), med(v.x, sc.lim), med(v.y, sc.lim), sc.div, false);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(a, med(v.z, sc.lim), med(v.w, sc.lim), sc.div, true);
+  return __builtin_bit_cast(uint32_t, a) | (sc.nan ? 0x7F7F7F7Fu : 0u);
+}
+
+__device__ void quant_f32_flat_task(const QuantDesc& d, int64_t task, int tid) {
+  const float* x = reinterpret_cast<const float*>(d.x);
+  const int64_t npieces = d.rows * d.cols / kF32Lane;    // whole blocks: cols % 32 == 0
+  const int64_t base = task * (int64_t)(kThreads * kFlatUnroll) + tid;
+  u32x4 v[kFlatUnroll];
+#pragma unroll
+  for (int u = 0; u < kFlatUnroll; ++u) {
+    const int64_t p = base + u * kThreads;
+    v[u] = p < npieces ? load16(x + p * kF32Lane) : kZero4;
+  }
+#pragma unroll
+  for (int u = 0; u < kFlatUnroll; ++u) {
+    const int64_t p = base + u * kThreads;
+    const F32Scale sc = f32_scale_key(oct_max(f32_key4(v[u])));
+    const uint32_t q = encode4_row(v[u], sc);
+    if (p < npieces) {
+      __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(d.q_row) + p);
+      if ((tid & 7) == 0) d.s_row[p >> 3] = (uint8_t)sc.sbyte;
+    }
+  }
+}
+
+__device__ void quant_f32_tile_task(const QuantDesc& d, int64_t task, int wave, int lane,
+                                    u32x4* colmax) {
+  const float* x = reinterpret_cast<const float*>(d.x);
+  const int64_t cols = d.cols;
+  const int64_t col_tiles = (cols + kF32TileCols - 1) / kF32TileCols;
+  const int64_t rb = task / col_tiles;
+  const int64_t r0 = rb * kTileRows + wave * kRowsPerWave;
+  const int64_t c = (task % col_tiles) * kF32TileCols + (int64_t)lane * kF32Lane;
+  const bool ok = c < cols;                          // cols % 8 == 0: whole lanes only
+  const float* xp = x + r0 * cols + c;
+
+  u32x4 v[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) v[r] = ok ? load16(xp + r * cols) : kZero4;
+
+  if (d.q_row) {
+    const int64_t sb_per_row = cols / kBlock;
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const F32Scale sc = f32_scale_key(oct_max(f32_key4(v[r])));
+      const uint32_t q = encode4_row(v[r], sc);
+      if (ok) {
+        __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(d.q_row + (r0 + r) * cols + c));
+        if ((lane & 7) == 0) d.s_row[(r0 + r) * sb_per_row + (c >> 5)] = (uint8_t)sc.sbyte;
+      }
+    }
+  }
+
+  if (d.q_col) {
+    u32x4 m = kZero4;
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) m = __builtin_elementwise_max(m, v[r] & 0x7FFFFFFFu);
+    colmax[wave * kWave + lane] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w)
+      if (w != wave) m = __builtin_elementwise_max(m, colmax[w * kWave + lane]);
+    F32Scale sc[kF32Lane];
+    uint32_t any_nan = 0, nanq = 0, sbytes = 0;
+#pragma unroll
+    for (int k = 0; k < kF32Lane; ++k) {
+      sc[k] = f32_scale_key(m[k]);
+      any_nan |= sc[k].nan;
+      nanq |= (sc[k].nan ? 0x7Fu : 0u) << (8 * k);
+      sbytes |= sc[k].sbyte << (8 * k);
+    }
+    if (ok && wave == 0)
+      *reinterpret_cast<uint32_t*>(d.s_col + rb * cols + c) = sbytes;
+    if (any_nan) {
+      // a NaN/Inf column keeps only each element's sign bit
+      u32x4 keep;
+#pragma unroll
+      for (int k = 0; k < kF32Lane; ++k) keep[k] = sc[k].nan ? 0x80000000u : 0xFFFFFFFFu;
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r) v[r] &= keep;
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; r += 2) {
+      // columns k = 0..3 of rows r, r+1: one conversion per column (two rows)
+      uint32_t dd[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k0 = 2 * h, k1 = 2 * h + 1;
+        v2i16 t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+            __builtin_bit_cast(v2i16, v[r][k0]), med(v[r][k0], sc[k0].lim),
+            med(v[r + 1][k0], sc[k0].lim), sc[k0].div, false);
+        t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(t, med(v[r][k1], sc[k1].lim),
+                                                     med(v[r + 1][k1], sc[k1].lim), sc[k1].div, true);
+        dd[h] = __builtin_bit_cast(uint32_t, t);   // bytes (r,k0) (r+1,k0) (r,k1) (r+1,k1)
+      }
+      const uint32_t q0 = __builtin_amdgcn_perm(dd[1], dd[0], 0x06040200u) | nanq;
+      const uint32_t q1 = __builtin_amdgcn_perm(dd[1], dd[0], 0x07050301u) | nanq;
+      if (ok) {
+        uint8_t* qp = d.q_col + (r0 + r) * cols + c;
+        __builtin_nontemporal_store(q0, reinterpret_cast<uint32_t*>(qp));
+        __builtin_nontemporal_store(q1, reinterpret_cast<uint32_t*>(qp + cols));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const QuantArgs a) {
+  __shared__ u32x4 colmax[kThreads];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t task = (int32_t)blockIdx.x;
+  const int i = find_desc(a.task_start, a.n, task);
+  const QuantDesc& d = a.d[i];
+  const int64_t local = task - a.task_start[i];
+  if (d.q_col)
+    quant_f32_tile_task(d, local, wave, lane, colmax);
+  else
+    quant_f32_flat_task(d, local, tid);
+}
+
+}  // namespace
+
+int64_t quant_f32_tasks(const QuantDesc& d) {
+  if (d.rows == 0 || d.cols == 0) return 0;
+  if (d.q_col)
+    return (d.rows / kTileRows) * ((d.cols + kF32TileCols - 1) / kF32TileCols);
+  const int64_t pieces = d.rows * d.cols / kF32Lane;
+  const int64_t per = (int64_t)kThreads * kFlatUnroll;
+  return (pieces + per - 1) / per;
+}
+
+hipError_t launch_quantize_f32(const QuantArgs& a, int64_t total_tasks, hipStream_t s) {
+  if (total_tasks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_quantize_f32_kernel, dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mx

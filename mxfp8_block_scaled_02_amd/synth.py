@@ -23,6 +23,8 @@ Workloads (sizes are one GPU's share at its real shape):
 5. RMSNorm + rowwise quantize at decode [16, 7168] and prefill [65536, 7168]:
    x = N(0, 3) * 10^u with u ~ U(-2, 2) drawn once per row, gamma ~ N(1, 0.1),
    offset 0.0, eps 1e-5
+6. rowwise + columnwise quantize of a float32 master weight [4096, 4096]: the
+   recipe of 2 kept in float32, with float32 subnormal tiles
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ SHAPES = {
     "grouped_64x2048x7168": (64, 2048, 7168),
     "rmsnorm_decode_16x7168": (16, 7168),
     "rmsnorm_prefill_65536x7168": (65536, 7168),
+    "rowcol_f32_4096x4096": (4096, 4096),
 }
 SEEDS = {
     "rowwise_256x1024": 1001,
@@ -45,6 +48,7 @@ SEEDS = {
     "grouped_64x2048x7168": 1004,
     "rmsnorm_decode_16x7168": 1005,
     "rmsnorm_prefill_65536x7168": 1005,
+    "rowcol_f32_4096x4096": 1006,
 }
 
 
@@ -100,6 +104,40 @@ def weight_with_outliers(rows=4096, cols=4096, seed=1002, device="cpu",
     return x
 
 
+def master_weight_f32(rows=4096, cols=4096, seed=1006, device="cpu", std=0.02,
+                      outlier_frac=0.001, outlier_gain=1000.0, zero_tile_frac=0.01,
+                      subnormal_tile_frac=0.01) -> torch.Tensor:
+    """The weight recipe kept in float32 (a master weight): N(0, std) with
+    outliers, all-zero 32x32 tiles and tiles of float32 subnormals (exponent
+    field 0, random mantissa and sign)."""
+    g = generator(seed, device)
+    n = rows * cols
+    x = torch.randn((n,), generator=g, device=device, dtype=torch.float32) * std
+    n_out = int(round(outlier_frac * n))
+    if n_out:
+        idx = torch.randperm(n, generator=g, device=device)[:n_out]
+        x[idx] *= outlier_gain
+    x = x.view(rows, cols)
+    bits = x.view(torch.int32)
+    tr, tc = rows // TILE, cols // TILE
+    n_tiles = tr * tc
+    n_zero = int(round(zero_tile_frac * n_tiles))
+    n_sub = int(round(subnormal_tile_frac * n_tiles))
+    if n_tiles and (n_zero or n_sub):
+        pick = torch.randperm(n_tiles, generator=g, device=device)[: n_zero + n_sub]
+        for k, t in enumerate(pick.tolist()):
+            r0, c0 = (t // tc) * TILE, (t % tc) * TILE
+            if k < n_zero:
+                bits[r0:r0 + TILE, c0:c0 + TILE] = 0
+            else:
+                mant = torch.randint(1, 1 << 23, (TILE, TILE), generator=g, device=device,
+                                     dtype=torch.int32)
+                sign = torch.randint(0, 2, (TILE, TILE), generator=g, device=device,
+                                     dtype=torch.int32)
+                bits[r0:r0 + TILE, c0:c0 + TILE] = mant | (sign << 31)
+    return x
+
+
 def rmsnorm_inputs(rows, cols, seed, device="cpu", x_std=1.0, row_decades=0.0,
                    gamma_std=0.1):
     """(x, gamma): x ~ N(0, x_std) times 10^u per row with u ~ U(-d, d), gamma ~ N(1, gamma_std)."""
@@ -135,6 +173,9 @@ def workload(name: str, device="cpu", **overrides):
     if name == "grouped_64x2048x7168":
         n, r, c = overrides.get("shape", SHAPES[name])
         return {"xs": expert_weights(n, r, c, seed, device)}
+    if name == "rowcol_f32_4096x4096":
+        r, c = overrides.get("shape", SHAPES[name])
+        return {"x": master_weight_f32(r, c, seed, device)}
     if name in ("rmsnorm_decode_16x7168", "rmsnorm_prefill_65536x7168"):
         r, c = overrides.get("shape", SHAPES[name])
         x, gamma = rmsnorm_inputs(r, c, seed, device, x_std=3.0, row_decades=2.0)

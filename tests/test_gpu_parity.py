@@ -163,6 +163,77 @@ def test_empty_tensor_is_a_no_op():
     assert p.rowwise_data.shape == (0, 1024)
 
 
+# ------------------------------------------------ float32 master weights --
+
+def f32_specials(rows, cols, seed):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((rows, cols)) * np.ldexp(1.0, g.integers(-30, 30, (rows, 1)))).astype(np.float32)
+    bits = x.view(np.uint32)
+    for _ in range(max(1, rows * cols // 512)):
+        r, c = g.integers(rows), g.integers(cols)
+        bits[r, c] = g.choice([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x00000001, 0x80000001,
+                               0x00000000, 0x80000000, 0x7F7FFFFF, 0xFF7FFFFF, 0x00400000, 0x007FFFFF])
+    return x
+
+
+def dev_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def check_quantize_f32(orc, x, rowwise=True, columnwise=True, what=""):
+    say("quantize_f32", what, x.shape, "row" if rowwise else "", "col" if columnwise else "")
+    planes = mx.quantize(dev_f32(x), rowwise=rowwise, columnwise=columnwise)
+    torch.cuda.synchronize()
+    if rowwise:
+        qr, sr = orc.quantize_rowwise(x)
+        assert_same(host(planes.rowwise_data), qr, what + " q_row")
+        assert_same(host(planes.rowwise_scale), sr, what + " s_row")
+    if columnwise:
+        qc, sc = orc.quantize_colwise(x)
+        assert_same(host(planes.columnwise_data), qc, what + " q_col")
+        assert_same(host(planes.columnwise_scale), sc, what + " s_col")
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (64, 544), (96, 1056), (32, 4128), (160, 96)])
+def test_f32_row_and_col(orc, shape):
+    check_quantize_f32(orc, f32_specials(*shape, seed=shape[1]), True, True, "f32 specials")
+    for i, b in enumerate(P.random_tensors(seed=3, rows=shape[0], cols=shape[1])):
+        check_quantize_f32(orc, P.bf16_values(b).astype(np.float32), True, True, "f32 from bf16 %d" % i)
+
+
+def test_f32_ties_and_wide_range(orc):
+    x = P.f32_blocks()
+    rows = x.shape[0] - x.shape[0] % 32
+    check_quantize_f32(orc, x[:rows], True, False, "f32 blocks rowwise")
+    check_quantize_f32(orc, np.ascontiguousarray(x[:rows].T), False, True, "f32 blocks columnwise")
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (3, 96), (7, 4128), (1000, 64)])
+def test_f32_rowwise_only_ragged(orc, shape):
+    check_quantize_f32(orc, f32_specials(*shape, seed=11), True, False, "f32 rowonly")
+
+
+@pytest.mark.parametrize("shape", [(32, 8), (64, 40), (96, 1000)])
+def test_f32_columnwise_only(orc, shape):
+    check_quantize_f32(orc, f32_specials(*shape, seed=12), False, True, "f32 colonly")
+
+
+def test_f32_master_weight_4096(orc):
+    x = synth.workload("rowcol_f32_4096x4096", device=DEV)["x"]
+    check_quantize_f32(orc, x.cpu().numpy(), True, True, "rowcol_f32_4096x4096")
+
+
+def test_f32_grouped_equals_single(orc):
+    shapes = [(32, 256), (64, 544), (96, 7168), (32, 40)]
+    xs = [f32_specials(*sh, seed=60 + i) for i, sh in enumerate(shapes)]
+    planes = mx.quantize_grouped([dev_f32(x) for x in xs], False, True)
+    torch.cuda.synchronize()
+    for x, p in zip(xs, planes):
+        qc, sc = orc.quantize_colwise(x)
+        assert_same(host(p.columnwise_data), qc, "grouped f32 q_col")
+        assert_same(host(p.columnwise_scale), sc, "grouped f32 s_col")
+
+
 # ------------------------------------------------------------------ grouped --
 
 def test_grouped_mixed_shapes_equal_single_calls(orc):
