@@ -78,6 +78,8 @@ class Oracle:
         "mxfp8_oracle_rmsnorm_f64": "p p f32 f32 i64 i64 p",
         "mxfp8_oracle_rmsnorm": "p p f32 f32 i64 i64 p",
         "mxfp8_oracle_rmsnorm_quantize": "p p f32 f32 i64 i64 p p p",
+        "mxfp8_oracle_gemm": "p p p p i64 i64 i64 p p",
+        "mxfp8_oracle_gemm_at": "p p p p i64 p p i64 p p",
         "mxfp8_oracle_set_threads": "i32",
         "mxfp8_oracle_max_threads": "",
     }
@@ -134,6 +136,35 @@ class Oracle:
         out = np.empty((rows, cols), np.float64)
         self.lib.mxfp8_oracle_dequantize(_ptr(q), _ptr(s), rows, cols, int(axis), _ptr(out))
         return out
+
+    def gemm(self, qa, sa, qb, sb):
+        """(C, abs_sum): C[m, n] = sum_k A[m, k] B[n, k] in float64 for rowwise
+        planes A (qa [M, K], sa [M, K/32]) and B (qb [N, K], sb [N, K/32]);
+        abs_sum[m, n] = sum_k |A[m, k] B[n, k]|."""
+        qa, sa, qb, sb = (np.ascontiguousarray(t, np.uint8) for t in (qa, sa, qb, sb))
+        M, K = qa.shape
+        N = qb.shape[0]
+        if qb.shape[1] != K or K % BLOCK or sa.shape != (M, K // BLOCK) or sb.shape != (N, K // BLOCK):
+            raise ValueError("bad plane shapes")
+        out = np.empty((M, N), np.float64)
+        mag = np.empty((M, N), np.float64)
+        self.lib.mxfp8_oracle_gemm(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, _ptr(out), _ptr(mag))
+        return out, mag
+
+    def gemm_at(self, qa, sa, qb, sb, ms, ns):
+        """The same product at positions (ms[i], ns[i]) only."""
+        qa, sa, qb, sb = (np.ascontiguousarray(t, np.uint8) for t in (qa, sa, qb, sb))
+        M, K = qa.shape
+        N = qb.shape[0]
+        ms = np.ascontiguousarray(ms, np.int64)
+        ns = np.ascontiguousarray(ns, np.int64)
+        if qb.shape[1] != K or ms.shape != ns.shape or (ms >= M).any() or (ns >= N).any():
+            raise ValueError("bad plane shapes or positions")
+        out = np.empty(ms.shape, np.float64)
+        mag = np.empty(ms.shape, np.float64)
+        self.lib.mxfp8_oracle_gemm_at(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), K, _ptr(ms), _ptr(ns),
+                                      ms.size, _ptr(out), _ptr(mag))
+        return out, mag
 
     def round_bf16(self, v):
         """bf16 bit patterns of float64 values, round to nearest even."""
@@ -196,6 +227,7 @@ def default() -> Oracle:
 def __getattr__(name):
     # Module-level access (oracle.quantize_rowwise, ...) goes to the default build.
     if name in ("set_threads", "max_threads", "quantize_rowwise", "quantize_colwise",
-                "dequantize", "round_bf16", "rmsnorm_f64", "rmsnorm", "rmsnorm_quantize"):
+                "dequantize", "round_bf16", "rmsnorm_f64", "rmsnorm", "rmsnorm_quantize",
+                "gemm", "gemm_at"):
         return getattr(default(), name)
     raise AttributeError(name)

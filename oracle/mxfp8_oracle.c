@@ -215,6 +215,45 @@ void mxfp8_oracle_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows,
         }
 }
 
+/* One entry of the MXFP8 matrix product: sum over k of the exact values of
+ * A[m, k] and B[n, k], both given as rowwise planes (scales one per 32 k).
+ * *abs_sum receives the sum of |A[m, k] * B[n, k]| (for error bounds). */
+static double gemm_entry(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb,
+                         const uint8_t *sb, int64_t K, int64_t m, int64_t n,
+                         double *abs_sum) {
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double a = e4m3_value(qa[m * K + k]) * e8m0_value(sa[m * (K / MX_BLOCK) + k / MX_BLOCK]);
+        double b = e4m3_value(qb[n * K + k]) * e8m0_value(sb[n * (K / MX_BLOCK) + k / MX_BLOCK]);
+        acc += a * b;
+        mag += fabs(a * b);
+    }
+    *abs_sum = mag;
+    return acc;
+}
+
+/* out[m, n] = sum_k A[m, k] * B[n, k] for A [M, K] and B [N, K] in MXFP8
+ * rowwise planes (the product a linear layer computes from a quantized
+ * activation and a quantized weight: quantization.utils page, mm_mxfp8). */
+void mxfp8_oracle_gemm(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb,
+                       const uint8_t *sb, int64_t M, int64_t N, int64_t K,
+                       double *out, double *abs_sum) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            out[m * N + n] = gemm_entry(qa, sa, qb, sb, K, m, n, &abs_sum[m * N + n]);
+}
+
+/* The same product at count chosen positions (ms[i], ns[i]). */
+void mxfp8_oracle_gemm_at(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb,
+                          const uint8_t *sb, int64_t K, const int64_t *ms,
+                          const int64_t *ns, int64_t count, double *out,
+                          double *abs_sum) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = gemm_entry(qa, sa, qb, sb, K, ms[i], ns[i], &abs_sum[i]);
+}
+
 /* Round doubles to bf16 bit patterns: nearest, ties to even; NaN -> 0x7FC0
  * with the input's sign; overflow past the largest finite bf16 -> infinity. */
 void mxfp8_oracle_round_bf16(const double *in, int64_t n, uint16_t *out) {

@@ -448,6 +448,41 @@ def check_f32_input(orc):
     assert (qb == qf).all() and (sb == sf).all(), "float32 and bf16 paths disagree"
 
 
+def check_gemm(orc, seed=23):
+    """The MXFP8 product against numpy's float64 matmul of the dequantized
+    planes, a brute-force loop on a tiny case, and exact special cases."""
+    g = torch.Generator().manual_seed(seed)
+    M, N, K = 48, 40, 160
+    a = (torch.randn(M, K, generator=g) * torch.pow(2.0, torch.randint(-6, 7, (M, 1), generator=g))).to(torch.bfloat16)
+    b = (torch.randn(N, K, generator=g) * 0.05).to(torch.bfloat16)
+    qa, sa = orc.quantize_rowwise(a.view(torch.int16).numpy().view(np.uint16))
+    qb, sb = orc.quantize_rowwise(b.view(torch.int16).numpy().view(np.uint16))
+    C, mag = orc.gemm(qa, sa, qb, sb)
+    da, db = orc.dequantize(qa, sa, 0), orc.dequantize(qb, sb, 0)
+    ref = da @ db.T
+    assert np.allclose(C, ref, rtol=1e-12, atol=1e-300), "product against numpy"
+    assert np.allclose(mag, np.abs(da) @ np.abs(db).T, rtol=1e-12), "abs sums"
+    # brute force on a corner
+    for m in (0, 7, M - 1):
+        for n in (0, 13, N - 1):
+            s_ = sum(da[m, k] * db[n, k] for k in range(K))
+            assert math.isclose(C[m, n], s_, rel_tol=1e-12, abs_tol=1e-300)
+    # positions
+    ms, ns = np.array([0, 5, M - 1]), np.array([N - 1, 3, 0])
+    v, _ = orc.gemm_at(qa, sa, qb, sb, ms, ns)
+    assert (v == C[ms, ns]).all()
+    # exact special case: one-hot blocks with known scales
+    q1 = np.zeros((2, 64), np.uint8); s1 = np.full((2, 2), 127, np.uint8)
+    q1[0, 3] = 0x38; q1[1, 40] = 0x40          # 1.0 at k = 3; 2.0 at k = 40
+    s1[1, 1] = 130                              # second block of row 1 scaled by 2^3
+    q2 = np.zeros((3, 64), np.uint8); s2 = np.full((3, 2), 127, np.uint8)
+    q2[0, 3] = 0x38; q2[1, 40] = 0xC4; q2[2, 3] = 0x7E   # 1.0, -3.0 (0xC4), 448
+    s2[1, 1] = 126
+    C1, _ = orc.gemm(q1, s1, q2, s2)
+    want = np.array([[1.0, 0.0, 448.0], [0.0, 2.0 * 8 * -3.0 * 0.5, 0.0]])
+    assert (C1 == want).all(), C1
+
+
 QUICK_CHECKS = [
     ("golden", check_golden),
     ("single_value_blocks", lambda o: check_single_value_blocks(o, stride=1)),
@@ -458,4 +493,5 @@ QUICK_CHECKS = [
     ("col_is_row_of_transpose", lambda o: check_col_is_row_of_transpose(o, random_tensors(rows=64, cols=64))),
     ("error_bound", lambda o: check_error_bound(o, random_tensors(rows=64, cols=64))),
     ("f32_input", check_f32_input),
+    ("gemm", check_gemm),
 ]

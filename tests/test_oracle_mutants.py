@@ -43,6 +43,9 @@ MUTANTS = {
     "dequant_col_index": ("s[(r / MX_BLOCK) * cols + c]", "s[(r / MX_BLOCK) * cols + (cols - 1 - c)]"),
     "bf16_precision": ("round_half_even_to(a, ldexp(1.0, e - 7))",
                        "round_half_even_to(a, ldexp(1.0, e - 8))"),
+    "gemm_b_scale_index": ("e8m0_value(sb[n * (K / MX_BLOCK) + k / MX_BLOCK])",
+                           "e8m0_value(sb[m * (K / MX_BLOCK) + k / MX_BLOCK])"),
+    "gemm_reversed_k": ("e4m3_value(qb[n * K + k])", "e4m3_value(qb[n * K + (K - 1 - k)])"),
     "f32_through_bf16": ("for (int i = 0; i < n; ++i) v[i] = (double)x[(int64_t)i * stride];",
                          "for (int i = 0; i < n; ++i) { uint32_t u; memcpy(&u, &x[(int64_t)i * stride], 4);"
                          " v[i] = bf16_value((uint16_t)(u >> 16)); }"),

@@ -23,6 +23,10 @@ def test_float32_input_against_torch_and_ties(orc):
     P.check_f32_input(orc)
 
 
+def test_gemm_against_numpy_and_closed_forms(orc):
+    P.check_gemm(orc)
+
+
 def test_dequant_decode_tables(orc):
     P.check_dequant_tables(orc)
 
