@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix-core peak
 MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mxfp8_block_scaled_02_amd", "csrc")
@@ -195,10 +196,35 @@ def bench_other_rows(torch, mx, synth, steps):
         out = mx.dequantize(q, s, axis)
         ms, _ = T.run(lambda i: mx.dequantize(q, s, axis, out=out), steps, 5)
         res["dequantize_f32_%s_4096x4096" % ("row" if axis == 0 else "col")] = (ms, alg, r * c)
-    return {k: {"ms_per_launch": round(ms, 5), "GB_s": round(b / (ms * 1e-3) / 1e9, 1),
-                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "Gelem_s": round(e / (ms * 1e-3) / 1e9, 2), "alg_bytes": b}
-            for k, (ms, b, e) in res.items()}
+    out = {k: {"ms_per_launch": round(ms, 5), "GB_s": round(b / (ms * 1e-3) / 1e9, 1),
+               "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "Gelem_s": round(e / (ms * 1e-3) / 1e9, 2), "alg_bytes": b}
+           for k, (ms, b, e) in res.items()}
+    out.update(bench_gemm(torch, mx, steps))
+    return out
+
+
+def bench_gemm(torch, mx, steps):
+    """The MXFP8 product of a quantized activation and a quantized weight:
+    TFLOP/s (2 M N K per launch) against the dense fp8 matrix-core peak."""
+    dev = torch.device("cuda:0")
+    T = Timed(torch, EAGER)
+    res = {}
+    for M, N, K in ((8192, 8192, 8192), (16, 7168, 7168)):
+        g = torch.Generator(device=dev).manual_seed(M + N + K)
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        b = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        pa, pb = mx.quantize(a, True, False), mx.quantize(b, True, False)
+        del a, b
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fn = lambda i: mx.gemm(pa.rowwise_data, pa.rowwise_scale, pb.rowwise_data, pb.rowwise_scale,
+                               torch.bfloat16, out=out)
+        ms, _ = T.run(fn, max(steps // 4, 10), 3)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        res["gemm_bf16out_%dx%dx%d" % (M, N, K)] = {
+            "ms_per_launch": round(ms, 5), "TFLOP_s": round(tf, 1),
+            "frac_mfma_fp8": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)}
+    return res
 
 
 def cpu_baseline(synth, target_s=10.0):

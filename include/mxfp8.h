@@ -160,6 +160,31 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
                               mxfp8_out_dtype out_dtype, void *stream);
 
 /*
+ * mxfp8_gemm - out[M, N] = A . B^T from two rowwise planes.
+ *
+ * The consumer the planes exist for: a linear layer that quantizes its bf16
+ * activation on the fly and multiplies it by a pre-quantized weight
+ * (quantization.utils page, mm_mxfp8), on gfx950's block-scaled MFMA, which
+ * takes the plain rank-2 scale layout (Mojo page, Limitations: the scale
+ * layout block_scaled_matmul_amd takes as a_scales).
+ *
+ *   qa  uint8 e4m3 [M, K]   sa  uint8 e8m0 [M, K/32]   (A rowwise plane)
+ *   qb  uint8 e4m3 [N, K]   sb  uint8 e8m0 [N, K/32]   (B rowwise plane, e.g.
+ *                                                        a weight [out, in])
+ *   out float32 or bf16 [M, N]
+ *
+ * out[m, n] = sum_k A[m, k] B[n, k] with the element and scale values of the
+ * planes, accumulated by the matrix cores in float32 (each 64-deep step
+ * aligns its products and keeps about 12 bits below the largest one; the
+ * result is within 2^-10 * sum_k |A[m,k] B[n,k]| of the exact sum), then
+ * rounded to the output type.  K must be a positive multiple of 128
+ * (MXFP8_ERR_SHAPE otherwise); M == 0 or N == 0 is a no-op.
+ */
+mxfp8_status mxfp8_gemm(const void *qa, const void *sa, const void *qb,
+                        const void *sb, int64_t M, int64_t N, int64_t K,
+                        void *out, mxfp8_out_dtype out_dtype, void *stream);
+
+/*
  * Grouped calls: one launch over a list of independent 2D tensors of any
  * shapes, such as the experts of an MoE layer (quantized_dbuffer page,
  * QuantizedDBuffer.empty takes a list of logical 2D shapes; quantization.utils

@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "MXFP8Planes", "quantize", "rmsnorm_quantize", "dequantize", "quantize_grouped",
-    "rmsnorm_quantize_grouped", "dequantize_grouped", "as_fp8", "library_path", "lib",
+    "rmsnorm_quantize_grouped", "dequantize_grouped", "gemm", "as_fp8", "library_path", "lib",
     "BLOCK", "ROWWISE", "COLUMNWISE",
 ]
 
@@ -81,10 +81,12 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_quantize_f32.argtypes = [p, i64, i64, p, p, p, p, p]
     L.mxfp8_quantize_f32_grouped.argtypes = [ctypes.POINTER(_QuantDesc), i32, p]
     L.mxfp8_rmsnorm_quantize_grouped.argtypes = [ctypes.POINTER(_NormDesc), i32, p]
+    L.mxfp8_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, ctypes.c_int, p]
     L.mxfp8_dequantize_grouped.argtypes = [ctypes.POINTER(_DeqDesc), i32, ctypes.c_int, p]
     for name in ("mxfp8_quantize", "mxfp8_rmsnorm_quantize", "mxfp8_dequantize",
                  "mxfp8_quantize_grouped", "mxfp8_rmsnorm_quantize_grouped",
-                 "mxfp8_dequantize_grouped", "mxfp8_quantize_f32", "mxfp8_quantize_f32_grouped"):
+                 "mxfp8_dequantize_grouped", "mxfp8_quantize_f32", "mxfp8_quantize_f32_grouped",
+                 "mxfp8_gemm"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -287,3 +289,22 @@ def dequantize_grouped(qs, ss, axes, dtype=torch.float32, outs=None) -> list:
     with torch.cuda.device(dev):
         _check(lib().mxfp8_dequantize_grouped(arr, len(descs), code, _stream(dev)))
     return res
+
+
+def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
+         dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[M, N] = A . B^T from rowwise planes A = (qa [M, K], sa [M, K/32]) and
+    B = (qb [N, K], sb [N, K/32]) (quantization.utils page, mm_mxfp8: a
+    quantized activation times a pre-quantized weight [out, in])."""
+    code = _out_code(dtype)
+    qa2, sa2 = _as2d(qa, "qa", torch.uint8), _as2d(sa, "sa", torch.uint8)
+    qb2, sb2 = _as2d(qb, "qb", torch.uint8), _as2d(sb, "sb", torch.uint8)
+    M, K = qa2.shape
+    N = qb2.shape[0]
+    if qb2.shape[1] != K or tuple(sa2.shape) != (M, K // BLOCK) or tuple(sb2.shape) != (N, K // BLOCK):
+        raise ValueError("gemm: planes must be qa [M, K], sa [M, K/32], qb [N, K], sb [N, K/32]")
+    o = _out(out, (M, N), dtype, qa.device, "out")
+    with torch.cuda.device(qa.device):
+        _check(lib().mxfp8_gemm(_ptr(qa2), _ptr(sa2), _ptr(qb2), _ptr(sb2), M, N, K, _ptr(o), code,
+                                _stream(qa.device)))
+    return o

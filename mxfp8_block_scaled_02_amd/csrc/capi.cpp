@@ -253,6 +253,24 @@ mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc* descs, int32_t n,
                     a);
 }
 
+mxfp8_status mxfp8_gemm(const void* qa, const void* sa, const void* qb, const void* sb,
+                        int64_t M, int64_t N, int64_t K, void* out, mxfp8_out_dtype out_dtype,
+                        void* stream) {
+  if (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16) return MXFP8_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0 || !fits(M, K) || !fits(N, K) || !fits(M, N)) return MXFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (K == 0 || K % 128) return MXFP8_ERR_SHAPE;
+  if (!qa || !sa || !qb || !sb || !out) return MXFP8_ERR_NULL;
+  if (misaligned(qa) || misaligned(sa) || misaligned(qb) || misaligned(sb) || misaligned(out))
+    return MXFP8_ERR_ALIGN;
+  if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return MXFP8_ERR_SHAPE;
+  (void)hipGetLastError();
+  return hip_status(mx::launch_gemm(static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa),
+                                    static_cast<const uint8_t*>(qb), static_cast<const uint8_t*>(sb),
+                                    M, N, K, out, out_dtype == MXFP8_OUT_BF16,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 mxfp8_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t cols,
                               mxfp8_axis axis, void* out, mxfp8_out_dtype out_dtype,
                               void* stream) {

@@ -89,4 +89,10 @@ struct DeqArgs {
 int64_t deq_tasks(const DeqDesc& d);
 hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s);
 
+// ---- MXFP8 matrix product -------------------------------------------------
+// out[M, N] (float32, or bf16 if out_bf16) = A . B^T for rowwise planes
+// A = (qa [M, K], sa [M, K/32]), B = (qb [N, K], sb [N, K/32]); K % 128 == 0.
+hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                       int64_t M, int64_t N, int64_t K, void* out, bool out_bf16, hipStream_t s);
+
 }  // namespace mx

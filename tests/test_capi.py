@@ -35,7 +35,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), "missing export " + n
 
@@ -85,6 +85,17 @@ def test_dequantize_argument_checks(L):
     assert d(A, None, 4, 32, 0, C, 0, None) == ERR_NULL
     assert d(A, B, 4, 32, 0, MIS, 1, None) == ERR_ALIGN
     assert d(None, None, 0, 0, 1, None, 1, None) == OK
+
+
+def test_gemm_argument_checks(L):
+    g = L.mxfp8_gemm
+    assert g(A, B, C, D, 4, 4, 96, A, 0, None) == ERR_SHAPE       # K % 128
+    assert g(A, B, C, D, 4, 4, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, -1, 4, 128, A, 0, None) == ERR_SHAPE
+    assert g(A, None, C, D, 4, 4, 128, A, 0, None) == ERR_NULL
+    assert g(A, B, C, D, 4, 4, 128, MIS, 0, None) == ERR_ALIGN
+    assert g(A, B, C, D, 4, 4, 128, A, 5, None) == ERR_ARG
+    assert g(None, None, None, None, 0, 4, 128, None, 0, None) == OK
 
 
 def test_grouped_checks_every_descriptor_first(L):
