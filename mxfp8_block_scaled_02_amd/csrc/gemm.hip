@@ -12,18 +12,35 @@
 // lane l holds row l % 32 of its operand; lane group h = l / 32 holds
 // k = 16h .. 16h+15 in bytes 0-15 and k = 32+16h .. 32+16h+15 in bytes 16-31,
 // and lane l supplies the scale of k block h of its row (block 0 is k 0..31,
-// block 1 is k 32..63).  Output register r of lane l is row
-// 8 (r / 4) + 4 h + r % 4, column l % 32.  This layout was established by a
-// lane-layout probe of the instruction on the GPU; the parity tests check it
-// end to end.
+// block 1 is k 32..63) in the low byte of its scale register.  Output register
+// r of lane l is row 8 (r / 4) + 4 h + r % 4, column l % 32.  This layout was
+// established by a lane-layout probe of the instruction on the GPU; the parity
+// tests check it end to end.
 //
-// Tiling: a workgroup computes a 128 x 128 tile with 4 waves of 64 x 64 (2 x 2
-// MFMA tiles each).  K advances in tiles of 128 bytes staged through LDS: the
-// next tile is loaded from HBM into registers while the current one feeds the
-// MFMAs, then written to the other LDS buffer.  LDS rows are padded to 144
-// bytes so that the 16-byte fragment reads of 8 consecutive rows fall on
-// distinct banks.  Rows and columns past M or N read as zero and are not
-// stored; K must be a multiple of 128.
+// Two tilings share that fragment layout:
+//
+// * tile256 (K % 512 == 0 and at least 256 tiles): a workgroup computes a
+//   256 x 256 tile with four waves of 128 x 128 (4 x 4 MFMA tiles, 256
+//   accumulators per lane), one workgroup per CU.  K advances in stages of 64
+//   bytes through a ring of four LDS slots that the loads fill directly
+//   (global_load_lds_dwordx4, no register staging): the loads of stage s + 4
+//   go out while stage s computes, and the fragments of stage s + 1 are read
+//   into a second register set meanwhile, so a stage waits only for data
+//   requested three stages earlier.  Scales travel the same way, 16 bytes (512
+//   k) per row and operand every eight stages.  Waits count the loads still
+//   allowed in flight (s_waitcnt vmcnt(n)) instead of draining them all at
+//   each barrier.  Workgroups are mapped to tiles so that each XCD works on a
+//   compact block of the output (its L2 holds the shared panels), and XCD
+//   pairs start K at different quarters.
+// * tile128: 128 x 128 tiles (four waves of 64 x 64) staged through registers
+//   into padded LDS rows; it takes problems with too few 256 x 256 tiles to
+//   fill the chip, or K not a multiple of 512.
+//
+// Rows of A or B past M or N read a valid row (the last one) and their
+// outputs are not stored.  K must be a multiple of 128.  The order in which
+// the 64-deep MFMA steps accumulate depends on the tiling and, for tile256, on
+// the tile's starting quarter; every order stays within the tolerance that
+// the tests derive for the instruction.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -34,11 +51,6 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kGT = 128;              // workgroup tile side (M and N)
-constexpr int kGK = 128;              // K bytes per LDS tile
-constexpr int kLdsStride = kGK + 16;  // padded LDS row
-constexpr int kLdsTile = kGT * kLdsStride;
-
 struct GemmParams {
   const uint8_t* qa;
   const uint8_t* sa;
@@ -47,15 +59,312 @@ struct GemmParams {
   void* out;
   int64_t M, N, K;
   int32_t out_bf16;
-  int32_t tiles_n;
+  int32_t tiles_m, tiles_n;
 };
+
+__device__ __forceinline__ v8i frag(const u32x4& lo, const u32x4& hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, uint32_t sa,
+                                     uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
+}
+
+// store register r of an MFMA tile whose top-left output is (row0, col0)
+__device__ __forceinline__ void store_tile(const GemmParams& p, const v16f& acc, int64_t row0,
+                                           int64_t col, int h) {
+  if (col >= p.N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = row0 + 8 * (r / 4) + 4 * h + (r % 4);
+    if (row >= p.M) continue;
+    if (p.out_bf16)
+      reinterpret_cast<uint16_t*>(p.out)[row * p.N + col] = (uint16_t)f32_to_bf16(acc[r]);
+    else
+      __builtin_nontemporal_store(acc[r], reinterpret_cast<float*>(p.out) + row * p.N + col);
+  }
+}
+
+// ---- tile256 ---------------------------------------------------------------
+
+constexpr int kBT = 256;                // workgroup tile side
+constexpr int kBK = 64;                 // K bytes per stage (one MFMA step)
+constexpr int kStages = 4;              // LDS ring depth
+constexpr int kOpBytes = kBT * kBK;     // one operand's stage in LDS (16 KiB)
+constexpr int kGroup = 8;               // stages per scale group (512 k, 16 scale bytes a row)
+constexpr int kScBytes = kBT * 16;      // one operand's scale group in LDS (4 KiB)
+constexpr int kGroupM = 8;              // tile rows per group of the tile order
+constexpr int64_t kGemmFillTiles = 256; // one 256 x 256 tile per CU fills the chip
+
+// one LDS array per ring slot (A then B) and per scale buffer (A then B): the
+// compiler tells in-flight LDS loads apart by the array they write, and only
+// for a handful of arrays
+__shared__ __attribute__((aligned(1024))) uint8_t s_slot0[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_slot1[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_slot2[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_slot3[2 * kOpBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_scale0[2 * kScBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_scale1[2 * kScBytes];
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+template <int N> __device__ __forceinline__ uint8_t* slot_a() {
+  return N == 0 ? s_slot0 : N == 1 ? s_slot1 : N == 2 ? s_slot2 : s_slot3;
+}
+template <int N> __device__ __forceinline__ uint8_t* slot_b() { return slot_a<N>() + kOpBytes; }
+
+// LDS placement of a 64-byte row: its 16-byte chunk c sits at chunk
+// c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 16-byte fragment
+// reads of 32 consecutive rows hit distinct banks in 8- and 16-lane phases
+__device__ __forceinline__ int row_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// rows r0 .. r0+255, k0 .. k0+63 of one operand into a ring slot: wave w's
+// load u covers the 16 rows of group g = 4u + w, lane L the physical chunk
+// L % 4 of row 16 g + L / 4 (1 KiB per load, written lane after lane)
+__device__ __forceinline__ void load_stage(const uint8_t* base, int64_t rows, int64_t r0, int64_t K,
+                                           int64_t k0, uint8_t* lds, int wave, int lane) {
+  const int lr = lane >> 2;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int g = 4 * u + wave;
+    const int c = (lane & 3) ^ row_swizzle(16 * g + lr);
+    int64_t row = r0 + 16 * g + lr;
+    row = row < rows ? row : rows - 1;
+    __builtin_amdgcn_global_load_lds(base + row * K + k0 + 16 * c, (lds_ptr)(lds + 1024 * g), 16, 0, 0);
+  }
+}
+
+// the 16 scale bytes of 512 k (k blocks kb0 .. kb0+15) of rows r0 .. r0+255,
+// one row per lane: wave w loads rows 64 w .. 64 w + 63
+__device__ __forceinline__ void load_scales(const uint8_t* s, int64_t rows, int64_t r0,
+                                            int64_t kblocks, int64_t kb0, uint8_t* lds, int wave,
+                                            int lane) {
+  int64_t row = r0 + 64 * wave + lane;
+  row = row < rows ? row : rows - 1;
+  __builtin_amdgcn_global_load_lds(s + row * kblocks + kb0, (lds_ptr)(lds + 1024 * wave), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt left alone)
+template <int N> __device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// this wave's loads up to the N most recent have landed and its LDS reads
+// have returned; then the workgroup meets.  A plain workgroup barrier would
+// also wait for every LDS load still in flight (its release fence covers
+// them); the empty asm keeps the compiler from moving memory accesses across.
+template <int N> __device__ __forceinline__ void ring_barrier() {
+  wait_loads<N>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct Tile256 {
+  const GemmParams& p;
+  int wave, lane, fr, h;
+  int64_t m0, n0, K, kblocks, stages;
+  int64_t kstart;               // first stage of this tile (K order rotated per tile)
+  int swz;                      // row_swizzle of this lane's fragment rows
+  int arow, brow;               // LDS byte offset of this lane's row in tile 0
+  v16f acc[4][4];
+  v8i fa[2][4], fb[2][4];       // fragments, double-buffered by stage parity
+  u32x4 sca[2][4], scb[2][4];   // scale groups, double-buffered by group parity
+
+  __device__ Tile256(const GemmParams& pp, int64_t mm0, int64_t nn0, int w, int l, int64_t ks)
+      : p(pp), wave(w), lane(l), m0(mm0), n0(nn0), kstart(ks) {
+    fr = lane & 31;
+    h = lane >> 5;
+    K = p.K;
+    kblocks = K / kBlock;
+    stages = K / kBK;
+    swz = row_swizzle(fr);
+    arow = ((wave >> 1) * 128 + fr) * kBK;
+    brow = ((wave & 1) * 128 + fr) * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  }
+
+  // loads of stage t into ring slot t % 4 (stages past the end reload the
+  // last one, into a slot nobody reads again); a stage that opens a scale
+  // group also brings that group's scales
+  template <int SLOT, bool GROUP_START>
+  __device__ __forceinline__ void issue(int64_t t) {
+    int64_t tt = t < stages ? t : stages - 1;
+    tt += kstart;
+    if (tt >= stages) tt -= stages;
+    load_stage(p.qa, p.M, m0, K, tt * kBK, slot_a<SLOT>(), wave, lane);
+    load_stage(p.qb, p.N, n0, K, tt * kBK, slot_b<SLOT>(), wave, lane);
+    if (GROUP_START) {
+      const int64_t kb0 = (tt / kGroup) * 16;
+      const int gpar = (int)((t / kGroup) & 1);
+      uint8_t* sc = gpar ? s_scale1 : s_scale0;
+      load_scales(p.sa, p.M, m0, kblocks, kb0, sc, wave, lane);
+      load_scales(p.sb, p.N, n0, kblocks, kb0, sc + kScBytes, wave, lane);
+    }
+  }
+
+  // fragment reads of ring slot SLOT into fragment buffer FB
+  template <int SLOT, int FB>
+  __device__ __forceinline__ void read_frags() {
+    const uint8_t* la = slot_a<SLOT>();
+    const uint8_t* lb = slot_b<SLOT>();
+    const int o0 = 16 * (h ^ swz), o1 = 16 * ((h + 2) ^ swz);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* pa = la + arow + 32 * kBK * i;
+      const uint8_t* pb = lb + brow + 32 * kBK * i;
+      fa[FB][i] = frag(*reinterpret_cast<const u32x4*>(pa + o0), *reinterpret_cast<const u32x4*>(pa + o1));
+      fb[FB][i] = frag(*reinterpret_cast<const u32x4*>(pb + o0), *reinterpret_cast<const u32x4*>(pb + o1));
+    }
+  }
+
+  template <int GP>
+  __device__ __forceinline__ void read_scales() {
+    const uint8_t* la = GP ? s_scale1 : s_scale0;
+    const uint8_t* lb = la + kScBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sca[GP][i] = *reinterpret_cast<const u32x4*>(la + 16 * ((wave >> 1) * 128 + 32 * i + fr));
+      scb[GP][i] = *reinterpret_cast<const u32x4*>(lb + 16 * ((wave & 1) * 128 + 32 * i + fr));
+    }
+  }
+
+  // the 16 MFMAs of a stage at position POS of its scale group
+  template <int FB, int GP, int POS>
+  __device__ __forceinline__ void mma() {
+    const int sh = 16 * (POS & 1) + 8 * h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = mfma(fa[FB][i], fb[FB][j], acc[i][j], sca[GP][i][POS >> 1] >> sh,
+                         scb[GP][j][POS >> 1] >> sh);
+  }
+
+  // one stage s = 8 q + POS (POS = s % 8, group parity GP = q % 2):
+  // barrier, loads of stage s + 4, reads of stage s + 1, MFMAs of stage s
+  template <int POS, int GP>
+  __device__ __forceinline__ void step(int64_t s) {
+    // loads issued after those of stage s + 1: stages s + 2 and s + 3, eight
+    // DMA loads each plus two for a stage that opens a scale group
+    constexpr int kAfter = 16 + (((POS + 2) % kGroup) == 0 ? 2 : 0) + (((POS + 3) % kGroup) == 0 ? 2 : 0);
+    ring_barrier<kAfter>();     // stage s+1 is in LDS; every read of stage s has returned
+    issue<(POS + 4) % kStages, ((POS + 4) % kGroup) == 0>(s + 4);
+    read_frags<(POS + 1) % kStages, (POS + 1) & 1>();
+    if (POS == kGroup - 1) read_scales<GP ^ 1>();
+    mma<POS & 1, GP, POS>();
+    // order: reads first, then the MFMAs with the loads between them
+#pragma unroll
+    for (int n = 0; n < 16; ++n) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  template <int GP>
+  __device__ __forceinline__ void group(int64_t s) {
+    step<0, GP>(s);
+    step<1, GP>(s + 1);
+    step<2, GP>(s + 2);
+    step<3, GP>(s + 3);
+    step<4, GP>(s + 4);
+    step<5, GP>(s + 5);
+    step<6, GP>(s + 6);
+    step<7, GP>(s + 7);
+  }
+
+  __device__ __forceinline__ void run() {
+    issue<0, true>(0);
+    issue<1, false>(1);
+    issue<2, false>(2);
+    issue<3, false>(3);
+    ring_barrier<24>();         // stage 0 and scale group 0 have landed
+    read_frags<0, 0>();
+    read_scales<0>();
+    // stages come in groups of 8 (K % 512 == 0); two groups per trip so that
+    // the scale buffers are named statically
+    int64_t s = 0;
+    for (; s + 2 * kGroup <= stages; s += 2 * kGroup) {
+      group<0>(s);
+      group<1>(s + kGroup);
+    }
+    if (s < stages) group<0>(s);
+    wait_loads<0>();            // no load may land after the workgroup ends
+  }
+};
+
+__global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile256_kernel(const GemmParams p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // workgroups go round-robin over the 8 XCDs: give XCD x the x-th contiguous
+  // run of the tile order, then walk groups of kGroupM tile rows column by column
+  const uint32_t T = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n;
+  const uint32_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const uint32_t per = T / 8, rem = T % 8;
+  const uint32_t v = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const uint32_t gsize = (uint32_t)kGroupM * (uint32_t)p.tiles_n;
+  const uint32_t grp = v / gsize, first_m = grp * kGroupM;
+  const uint32_t gm = min((uint32_t)p.tiles_m - first_m, (uint32_t)kGroupM);
+  const uint32_t idx = v - grp * gsize;
+  const int64_t m0 = (int64_t)(first_m + idx % gm) * kBT;
+  const int64_t n0 = (int64_t)(idx / gm) * kBT;
+
+  // XCD pairs start K at different quarters (whole scale groups) so that
+  // concurrent tiles on different XCDs do not stream the same K columns,
+  // whose rows sit a power-of-two stride apart, at the same time
+  const int64_t ngroups = p.K / (kBK * kGroup);
+  const int64_t ks = ((int64_t)((xcd / 2) % 4) * ngroups / 4) * kGroup;
+  Tile256 t(p, m0, n0, wave, lane, ks);
+  t.run();
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, fr = lane & 31;
+  const int64_t r0 = m0 + wm * 128, c0 = n0 + wn * 128 + fr;
+  if (m0 + kBT <= p.M && n0 + kBT <= p.N) {
+    // a full tile: no bounds to check
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t at = (r0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4)) * p.N + c0 + 32 * j;
+          if (p.out_bf16)
+            reinterpret_cast<uint16_t*>(p.out)[at] = (uint16_t)f32_to_bf16(t.acc[i][j][r]);
+          else
+            __builtin_nontemporal_store(t.acc[i][j][r], reinterpret_cast<float*>(p.out) + at);
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store_tile(p, t.acc[i][j], r0 + 32 * i, c0 + 32 * j, h);
+  }
+}
+
+// ---- tile128 ---------------------------------------------------------------
+
+constexpr int kGT = 128;              // workgroup tile side (M and N)
+constexpr int kGK = 128;              // K bytes per LDS tile
+constexpr int kLdsStride = kGK + 16;  // padded LDS row
+constexpr int kLdsTile = kGT * kLdsStride;
 
 __device__ __forceinline__ u32x4 ld_global(const uint8_t* base, int64_t rows, int64_t row,
                                            int64_t K, int64_t k) {
   return row < rows ? load16_cached(base + row * K + k) : u32x4{0, 0, 0, 0};
 }
 
-__global__ __launch_bounds__(kThreads) void mxfp8_gemm_kernel(const GemmParams p) {
+__global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kLdsTile];   // [buffer][A, B]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,19 +441,13 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_kernel(const GemmParams p
       for (int i = 0; i < 2; ++i) {
         const uint8_t* la = &lds[buf][0][(wm * 64 + 32 * i + fr) * kLdsStride + 64 * st + 16 * h];
         const uint8_t* lb = &lds[buf][1][(wn * 64 + 32 * i + fr) * kLdsStride + 64 * st + 16 * h];
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(la);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(la + 32);
-        const u32x4 b0 = *reinterpret_cast<const u32x4*>(lb);
-        const u32x4 b1 = *reinterpret_cast<const u32x4*>(lb + 32);
-        fa[i] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        fb[i] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        fa[i] = frag(*reinterpret_cast<const u32x4*>(la), *reinterpret_cast<const u32x4*>(la + 32));
+        fb[i] = frag(*reinterpret_cast<const u32x4*>(lb), *reinterpret_cast<const u32x4*>(lb + 32));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[i], fb[j], acc[i][j], 0, 0, 0, (int)sa_cur[i][st], 0, (int)sb_cur[j][st]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j], sa_cur[i][st], sb_cur[j][st]);
     }
     if (more) {
       // the other buffer was last read in the previous iteration, which every
@@ -161,23 +464,11 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_kernel(const GemmParams p
     }
   }
 
-  // store: register r of tile (i, j) is row 8 (r/4) + 4 h + r % 4, column fr
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 64 + 32 * j + fr;
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-        if (row >= p.M) continue;
-        if (p.out_bf16)
-          reinterpret_cast<uint16_t*>(p.out)[row * p.N + col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
-        else
-          __builtin_nontemporal_store(acc[i][j][r], reinterpret_cast<float*>(p.out) + row * p.N + col);
-      }
-    }
+    for (int j = 0; j < 2; ++j)
+      store_tile(p, acc[i][j], m0 + wm * 64 + 32 * i, n0 + wn * 64 + 32 * j + fr, h);
 }
 
 }  // namespace
@@ -189,9 +480,17 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.qa = qa; p.sa = sa; p.qb = qb; p.sb = sb; p.out = out;
   p.M = M; p.N = N; p.K = K;
   p.out_bf16 = out_bf16 ? 1 : 0;
-  p.tiles_n = (int32_t)((N + kGT - 1) / kGT);
-  const int64_t tiles = ((M + kGT - 1) / kGT) * p.tiles_n;
-  hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3((uint32_t)tiles), dim3(kThreads), 0, s, p);
+  const int64_t big = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
+  if (big >= kGemmFillTiles && K % (kBK * kGroup) == 0) {
+    p.tiles_m = (int32_t)((M + kBT - 1) / kBT);
+    p.tiles_n = (int32_t)((N + kBT - 1) / kBT);
+    hipLaunchKernelGGL(mxfp8_gemm_tile256_kernel, dim3((uint32_t)big), dim3(kThreads), 0, s, p);
+  } else {
+    p.tiles_m = (int32_t)((M + kGT - 1) / kGT);
+    p.tiles_n = (int32_t)((N + kGT - 1) / kGT);
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL(mxfp8_gemm_tile128_kernel, dim3((uint32_t)tiles), dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -109,3 +109,28 @@ def test_gemm_nan_scale(orc):
     qb, sb = quantized(128, 256, 0.05, seed=11)
     sa[3, 2] = 0xFF                                       # a NaN scale in row 3
     run(orc, qa, sa, qb, sb, "NaN scale")
+
+
+@pytest.mark.parametrize("mnk", [
+    # enough 256 x 256 tiles to fill the chip and K % 512 == 0: ragged M and N,
+    # one, two, three (odd: the trailing group) and four 512-deep scale groups,
+    # so that the XCD pairs start at different quarters of K
+    (4096 - 37, 4096 + 100, 512), (4096, 4096 + 256, 1024), (4352, 3840, 1536), (4096 + 1, 4096, 2048),
+    # many tiles but K % 512 != 0: the 128 x 128 tiling, odd 128-deep stage counts
+    (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (4352, 3840, 640)])
+def test_gemm_large_tiles_ragged_sampled(orc, mnk):
+    """Large problems: sampled outputs, every column of the last row and every
+    row of the last column."""
+    M, N, K = mnk
+    qa, sa = quantized(M, K, 1.0, seed=M + 3 * K)
+    qb, sb = quantized(N, K, 0.05, seed=N + 5 * K)
+    g = np.random.default_rng(M + N + K)
+    ms = np.concatenate([g.integers(0, M, 6000), np.full(N, M - 1), np.arange(M)])
+    ns = np.concatenate([g.integers(0, N, 6000), np.arange(N), np.full(M, N - 1)])
+    C, mag = orc.gemm_at(host(qa), host(sa), host(qb), host(sb), ms, ns)
+    for dtype in (torch.float32, torch.bfloat16):
+        say("gemm large tiles", (M, N, K), dtype)
+        out = mx.gemm(qa, sa, qb, sb, dtype)
+        torch.cuda.synchronize()
+        got = host(out.float())[ms, ns].astype(np.float64)
+        check_close(got, C, mag, dtype == torch.bfloat16, "large tiles %s" % ((M, N, K),))
