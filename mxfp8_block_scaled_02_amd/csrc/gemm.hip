@@ -471,6 +471,162 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
       store_tile(p, acc[i][j], m0 + wm * 64 + 32 * i, n0 + wn * 64 + 32 * j + fr, h);
 }
 
+// ---- skinny (M <= 32) ---------------------------------------------------------
+//
+// A few activation rows against a large weight (decode): the product is bound
+// by streaming B once from HBM.  A workgroup owns 32 output columns and its
+// eight waves split K into contiguous ranges of 128-deep units.  Each wave
+// streams its B rows into two private LDS buffers with coalesced direct loads
+// (one 1 KiB load covers 8 rows x 128 bytes), reads the MFMA fragments back
+// (16-byte chunk c of row r stored at chunk c ^ (r % 8) ^ ((r / 8) % 2)), and
+// loads the A fragments (only the M real rows; the padding rows are zero)
+// straight from cache.  The eight partial 32 x 32 tiles meet in LDS and are
+// summed in wave order.
+
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyUnits = 2;                       // 128-deep units per chunk
+constexpr int kSkinnyChunk = 32 * 128 * kSkinnyUnits;  // one wave's chunk of B in LDS
+
+// the two chunk buffers of every wave, as two arrays so that the compiler
+// can tell a chunk in flight from the one being read
+__shared__ __attribute__((aligned(1024))) uint8_t s_skinny0[kSkinnyWaves * kSkinnyChunk];
+__shared__ __attribute__((aligned(1024))) uint8_t s_skinny1[kSkinnyWaves * kSkinnyChunk];
+
+__device__ __forceinline__ int skinny_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// loads one chunk issues: per unit four LDS loads of B, four A fragment
+// loads and two scale words
+constexpr int kSkinnyLoads = kSkinnyUnits * 10;
+
+__device__ __forceinline__ void skinny_pin() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+struct SkinnyChunk {
+  u32x4 a[kSkinnyUnits][4];
+  uint32_t sa[kSkinnyUnits], sb[kSkinnyUnits];
+};
+
+struct Skinny {
+  const GemmParams& p;
+  int wave, lane, fr, h;
+  int64_t n0, K, kblocks, u1;
+  uint32_t amask;               // ~0 for a real A row, 0 for a padding row
+  const uint8_t* pa;
+  const uint8_t* psa;
+  const uint8_t* psb;
+
+  // units u .. u + kSkinnyUnits - 1 (past u1: the last unit again) of B into
+  // this wave's part of buf, and the matching A fragments and scales
+  __device__ __forceinline__ void load(uint8_t* buf, int64_t u, SkinnyChunk& c) {
+    uint8_t* mine = buf + wave * kSkinnyChunk;
+    const int lr = lane >> 3;
+#pragma unroll
+    for (int v = 0; v < kSkinnyUnits; ++v) {
+      const int64_t uu = min(u + v, u1 - 1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = 8 * g + lr;
+        const int chunk = (lane & 7) ^ skinny_swizzle(r);
+        const int64_t row = min(n0 + r, p.N - 1);
+        __builtin_amdgcn_global_load_lds(p.qb + row * K + uu * 128 + 16 * chunk,
+                                         (lds_ptr)(mine + 4096 * v + 1024 * g), 16, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        c.a[v][q] = load16_cached(pa + uu * 128 + 32 * q) & amask;
+      c.sa[v] = *reinterpret_cast<const uint32_t*>(psa + uu * 4);
+      c.sb[v] = *reinterpret_cast<const uint32_t*>(psb + uu * 4);
+    }
+  }
+
+  __device__ __forceinline__ void compute(const uint8_t* buf, int64_t u, const SkinnyChunk& c, v16f& acc) {
+    const uint8_t* mine = buf + wave * kSkinnyChunk + fr * 128;
+    const int f = skinny_swizzle(fr);
+#pragma unroll
+    for (int v = 0; v < kSkinnyUnits; ++v) {
+      // a unit past the end repeats the last one: its B fragments become zero
+      const uint32_t keep = u + v < u1 ? ~0u : 0u;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4 b0 = *reinterpret_cast<const u32x4*>(mine + 4096 * v + 16 * ((4 * j + h) ^ f));
+        u32x4 b1 = *reinterpret_cast<const u32x4*>(mine + 4096 * v + 16 * ((4 * j + h + 2) ^ f));
+        b0 &= keep;
+        b1 &= keep;
+        acc = mfma(frag(c.a[v][2 * j], c.a[v][2 * j + 1]), frag(b0, b1), acc, c.sa[v] >> (16 * j + 8 * h),
+                   c.sb[v] >> (16 * j + 8 * h));
+      }
+    }
+  }
+};
+
+__global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 31, h = lane >> 5;
+  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const int64_t K = p.K, kblocks = K / kBlock, units = K / 128;
+  const int64_t u0 = units * wave / kSkinnyWaves, u1 = units * (wave + 1) / kSkinnyWaves;
+
+  Skinny sk{p, wave, lane, fr, h, n0, K, kblocks, u1, fr < p.M ? ~0u : 0u,
+            p.qa + min((int64_t)fr, p.M - 1) * K + 16 * h,
+            p.sa + min((int64_t)fr, p.M - 1) * kblocks,
+            p.sb + min(n0 + fr, p.N - 1) * kblocks};
+
+  // Chunk pipeline, explicit about waits: each block of loads and each block
+  // of MFMAs is pinned in place (compiler memory fence + scheduling barrier),
+  // a chunk is read once only the next chunk's kSkinnyLoads loads remain in
+  // flight, and a buffer is refilled only after its LDS reads have returned.
+  v16f acc = v16f{};
+  if (u0 < u1) {
+    SkinnyChunk c0, c1;
+    sk.load(s_skinny0, u0, c0);
+    for (int64_t u = u0; u < u1; u += 2 * kSkinnyUnits) {
+      skinny_pin();
+      wait_loads<kSkinnyLoads>();                  // vmcnt(n) lgkmcnt(0)
+      skinny_pin();
+      sk.load(s_skinny1, u + kSkinnyUnits, c1);
+      skinny_pin();
+      wait_loads<kSkinnyLoads>();                  // chunk u has landed
+      skinny_pin();
+      sk.compute(s_skinny0, u, c0, acc);
+      skinny_pin();
+      wait_loads<kSkinnyLoads>();                  // reads of chunk u returned
+      skinny_pin();
+      sk.load(s_skinny0, u + 2 * kSkinnyUnits, c0);
+      skinny_pin();
+      wait_loads<kSkinnyLoads>();                  // chunk u + kSkinnyUnits has landed
+      skinny_pin();
+      sk.compute(s_skinny1, u + kSkinnyUnits, c1, acc);
+    }
+    skinny_pin();
+    wait_loads<0>();                               // no load may land after the workgroup ends
+  }
+
+  // the partial tiles reuse the first chunk buffer once every wave is done
+  __syncthreads();
+  float (*part)[32][33] = reinterpret_cast<float (*)[32][33]>(s_skinny0);
+  static_assert(sizeof(float) * kSkinnyWaves * 32 * 33 <= sizeof(s_skinny0), "partials fit");
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part[wave][8 * (r / 4) + 4 * h + (r % 4)][fr] = acc[r];
+  __syncthreads();
+  for (int e = tid; e < 32 * 32; e += kSkinnyWaves * 64) {
+    const int row = e >> 5, col = e & 31;
+    float sum = part[0][row][col];
+#pragma unroll
+    for (int w = 1; w < kSkinnyWaves; ++w) sum += part[w][row][col];
+    if (row < p.M && n0 + col < p.N) {
+      const int64_t at = row * p.N + n0 + col;
+      if (p.out_bf16)
+        reinterpret_cast<uint16_t*>(p.out)[at] = (uint16_t)f32_to_bf16(sum);
+      else
+        reinterpret_cast<float*>(p.out)[at] = sum;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
@@ -481,7 +637,10 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.M = M; p.N = N; p.K = K;
   p.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t big = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
-  if (big >= kGemmFillTiles && K % (kBK * kGroup) == 0) {
+  if (M <= 32) {
+    const int64_t tiles = (N + 31) / 32;
+    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
+  } else if (big >= kGemmFillTiles && K % (kBK * kGroup) == 0) {
     p.tiles_m = (int32_t)((M + kBT - 1) / kBT);
     p.tiles_n = (int32_t)((N + kBT - 1) / kBT);
     hipLaunchKernelGGL(mxfp8_gemm_tile256_kernel, dim3((uint32_t)big), dim3(kThreads), 0, s, p);

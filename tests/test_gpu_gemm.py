@@ -134,3 +134,14 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
         torch.cuda.synchronize()
         got = host(out.float())[ms, ns].astype(np.float64)
         check_close(got, C, mag, dtype == torch.bfloat16, "large tiles %s" % ((M, N, K),))
+
+
+@pytest.mark.parametrize("mnk", [(16, 7168, 7168), (1, 4096, 4096), (32, 1000, 384), (5, 96, 128),
+                                 (31, 33, 640), (17, 2048, 1152)])
+def test_gemm_skinny_decode(orc, mnk):
+    """A few activation rows (decode): the K-split skinny path, including K
+    with fewer 128-deep units than waves and N not a multiple of 32."""
+    M, N, K = mnk
+    qa, sa = quantized(M, K, 1.0, seed=M + 11 * K)
+    qb, sb = quantized(N, K, 0.02, seed=N + 13 * K)
+    run(orc, qa, sa, qb, sb, "skinny")
