@@ -475,16 +475,16 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
 //
 // A few activation rows against a large weight (decode): the product is bound
 // by streaming B once from HBM.  A workgroup owns 32 output columns and its
-// eight waves split K into contiguous ranges of 128-deep units.  Each wave
+// four waves split K into contiguous ranges of 128-deep units.  Each wave
 // streams its B rows into two private LDS buffers with coalesced direct loads
 // (one 1 KiB load covers 8 rows x 128 bytes), reads the MFMA fragments back
 // (16-byte chunk c of row r stored at chunk c ^ (r % 8) ^ ((r / 8) % 2)), and
 // loads the A fragments (only the M real rows; the padding rows are zero)
-// straight from cache.  The eight partial 32 x 32 tiles meet in LDS and are
+// straight from cache.  The four partial 32 x 32 tiles meet in LDS and are
 // summed in wave order.
 
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyUnits = 2;                       // 128-deep units per chunk
+constexpr int kSkinnyWaves = 4;
+constexpr int kSkinnyUnits = 1;                       // 128-deep units per chunk
 constexpr int kSkinnyChunk = 32 * 128 * kSkinnyUnits;  // one wave's chunk of B in LDS
 
 // the two chunk buffers of every wave, as two arrays so that the compiler
@@ -607,8 +607,8 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
 
   // the partial tiles reuse the first chunk buffer once every wave is done
   __syncthreads();
-  float (*part)[32][33] = reinterpret_cast<float (*)[32][33]>(s_skinny0);
-  static_assert(sizeof(float) * kSkinnyWaves * 32 * 33 <= sizeof(s_skinny0), "partials fit");
+  float (*part)[32][32] = reinterpret_cast<float (*)[32][32]>(s_skinny0);
+  static_assert(sizeof(float) * kSkinnyWaves * 32 * 32 <= sizeof(s_skinny0), "partials fit");
 #pragma unroll
   for (int r = 0; r < 16; ++r) part[wave][8 * (r / 4) + 4 * h + (r % 4)][fr] = acc[r];
   __syncthreads();
