@@ -24,8 +24,11 @@
  * Both data planes are [rows, cols] row-major, the input's own layout, not
  * transposed (quantized_dbuffer page, Functions: _rowwise_scale_layout and
  * _columnwise_scale_layout derive both scale layouts from one data layout).
- * Every plane is compact and unswizzled, with no padding (quantized_dbuffer
- * page, API: QuantizedDBuffer and get_tensor_view).
+ * By default every plane is compact and unswizzled, with no padding
+ * (quantized_dbuffer page, API: QuantizedDBuffer and get_tensor_view).  A
+ * scale plane may instead be written into, and read from, a padded
+ * allocation whose rows are a caller-chosen pitch apart (see "Scale pitches"
+ * below).
  *
  * Conventions shared by every entry point:
  *   - Tensors are 2D, row-major and contiguous.  rows and cols count
@@ -55,11 +58,14 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 1
+#define MXFP8_ABI_VERSION 2
 #define MXFP8_BLOCK 32
 /* Descriptors handled by one kernel launch in the grouped calls; longer
- * lists are processed in consecutive launches of at most this many. */
+ * lists are processed in consecutive launches of at most this many.  A list
+ * in which any scale plane has a pitch of its own goes in launches of at most
+ * MXFP8_PITCHED_GROUP_PER_LAUNCH. */
 #define MXFP8_GROUP_PER_LAUNCH 64
+#define MXFP8_PITCHED_GROUP_PER_LAUNCH 32
 
 typedef enum {
     MXFP8_OK = 0,
@@ -160,6 +166,28 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
                               mxfp8_out_dtype out_dtype, void *stream);
 
 /*
+ * Scale pitches - scale planes in a consumer's padded allocation.
+ *
+ * Consumers may keep scales in a larger, padded allocation ("TE's physical
+ * allocation shape": quantized_dbuffer page, _pad_rowwise_scale and
+ * _pad_columnwise_scale; TE-only padding is added when a wrapper for compute
+ * is materialized).  The pages give neither the padded shape nor any other
+ * consumer order, so the library takes the plainest reading that covers
+ * them: the scale plane's rows are `pitch` bytes apart instead of the plane's
+ * width, and the kernels write (or read) the scale bytes there directly, in
+ * the same pass, with no extra copy.  Bytes between the end of a scale row and
+ * the next row's start, and rows past the plane, are never written or read.
+ * A pitch of 0 means compact.  Required:
+ *
+ *   rowwise scales     pitch >= cols/32 (any value), and rows * cols/32 < 2^32
+ *                      when the rowwise plane is the only one requested;
+ *   columnwise scales  pitch >= cols and a multiple of 8 (MXFP8_ERR_ALIGN);
+ *   matrix product     pitch >= K/32 and a multiple of 4.
+ *
+ * A pitch below the plane's width is MXFP8_ERR_SHAPE.
+ */
+
+/*
  * mxfp8_gemm - out[M, N] = A . B^T from two rowwise planes.
  *
  * The consumer the planes exist for: a linear layer that quantizes its bf16
@@ -178,11 +206,14 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
  * aligns its products and keeps about 12 bits below the largest one; the
  * result is within 2^-10 * sum_k |A[m,k] B[n,k]| of the exact sum), then
  * rounded to the output type.  K must be a positive multiple of 128
- * (MXFP8_ERR_SHAPE otherwise); M == 0 or N == 0 is a no-op.
+ * (MXFP8_ERR_SHAPE otherwise); M == 0 or N == 0 is a no-op.  sa_pitch and
+ * sb_pitch are the bytes between scale rows of A and of B (0: compact, K/32;
+ * see "Scale pitches").
  */
 mxfp8_status mxfp8_gemm(const void *qa, const void *sa, const void *qb,
                         const void *sb, int64_t M, int64_t N, int64_t K,
-                        void *out, mxfp8_out_dtype out_dtype, void *stream);
+                        int64_t sa_pitch, int64_t sb_pitch, void *out,
+                        mxfp8_out_dtype out_dtype, void *stream);
 
 /*
  * Grouped calls: one launch over a list of independent 2D tensors of any
@@ -192,13 +223,16 @@ mxfp8_status mxfp8_gemm(const void *qa, const void *sa, const void *qb,
  * follows the rules of the matching single call and the results equal n
  * single calls.  descs is a host array of n entries, read before the call
  * returns.  n == 0 is a no-op; n < 0 is MXFP8_ERR_ARG.  Each launch takes at
- * most MXFP8_GROUP_PER_LAUNCH descriptors.
+ * most MXFP8_GROUP_PER_LAUNCH descriptors.  The descriptors also carry scale
+ * pitches (0: compact; see "Scale pitches"), so a single tensor with padded
+ * scale planes is a grouped call with n == 1.
  */
 typedef struct {
     const void *x;
     int64_t rows, cols;
     void *q_row, *s_row; /* both NULL: rowwise plane not requested */
     void *q_col, *s_col; /* both NULL: columnwise plane not requested */
+    int64_t s_row_pitch, s_col_pitch; /* bytes between scale rows; 0: compact */
 } mxfp8_quant_desc;
 
 typedef struct {
@@ -206,6 +240,7 @@ typedef struct {
     float weight_offset, eps;
     int64_t rows, cols;
     void *normed, *q_row, *s_row;
+    int64_t s_row_pitch; /* bytes between scale rows; 0: compact */
 } mxfp8_norm_desc;
 
 typedef struct {
@@ -213,6 +248,7 @@ typedef struct {
     int64_t rows, cols;
     mxfp8_axis axis;
     void *out;
+    int64_t s_pitch; /* bytes between scale rows; 0: compact */
 } mxfp8_deq_desc;
 
 mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc *descs, int32_t n,

@@ -29,6 +29,7 @@ __all__ = [
 ]
 
 BLOCK = 32
+ABI_VERSION = 2
 ROWWISE, COLUMNWISE = 0, 1
 _OUT_F32, _OUT_BF16 = 0, 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +43,8 @@ _STATUS = {0: "MXFP8_OK", 1: "MXFP8_ERR_NULL", 2: "MXFP8_ERR_SHAPE", 3: "MXFP8_E
 class _QuantDesc(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("q_row", ctypes.c_void_p), ("s_row", ctypes.c_void_p),
-                ("q_col", ctypes.c_void_p), ("s_col", ctypes.c_void_p)]
+                ("q_col", ctypes.c_void_p), ("s_col", ctypes.c_void_p),
+                ("s_row_pitch", ctypes.c_int64), ("s_col_pitch", ctypes.c_int64)]
 
 
 class _NormDesc(ctypes.Structure):
@@ -50,12 +52,13 @@ class _NormDesc(ctypes.Structure):
                 ("weight_offset", ctypes.c_float), ("eps", ctypes.c_float),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("normed", ctypes.c_void_p), ("q_row", ctypes.c_void_p),
-                ("s_row", ctypes.c_void_p)]
+                ("s_row", ctypes.c_void_p), ("s_row_pitch", ctypes.c_int64)]
 
 
 class _DeqDesc(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("rows", ctypes.c_int64),
-                ("cols", ctypes.c_int64), ("axis", ctypes.c_int), ("out", ctypes.c_void_p)]
+                ("cols", ctypes.c_int64), ("axis", ctypes.c_int), ("out", ctypes.c_void_p),
+                ("s_pitch", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -73,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(_LIB_PATH)
     p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     L.mxfp8_abi_version.argtypes, L.mxfp8_abi_version.restype = [], ctypes.c_int
+    if L.mxfp8_abi_version() != ABI_VERSION:
+        raise RuntimeError("libmxfp8.so has ABI version %d, this binding expects %d; rebuild it"
+                           % (L.mxfp8_abi_version(), ABI_VERSION))
     L.mxfp8_status_string.argtypes, L.mxfp8_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     L.mxfp8_quantize.argtypes = [p, i64, i64, p, p, p, p, p]
     L.mxfp8_rmsnorm_quantize.argtypes = [p, p, f32, f32, i64, i64, p, p, p, p]
@@ -81,7 +87,7 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_quantize_f32.argtypes = [p, i64, i64, p, p, p, p, p]
     L.mxfp8_quantize_f32_grouped.argtypes = [ctypes.POINTER(_QuantDesc), i32, p]
     L.mxfp8_rmsnorm_quantize_grouped.argtypes = [ctypes.POINTER(_NormDesc), i32, p]
-    L.mxfp8_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, ctypes.c_int, p]
+    L.mxfp8_gemm.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, ctypes.c_int, p]
     L.mxfp8_dequantize_grouped.argtypes = [ctypes.POINTER(_DeqDesc), i32, ctypes.c_int, p]
     for name in ("mxfp8_quantize", "mxfp8_rmsnorm_quantize", "mxfp8_dequantize",
                  "mxfp8_quantize_grouped", "mxfp8_rmsnorm_quantize_grouped",
@@ -148,6 +154,38 @@ def _out(t, shape, dtype, device, name):
     return t
 
 
+def _scale_pitch(t, shape, device, name, allocate=True):
+    """A scale plane [rows, width] as (tensor, pitch).  The tensor may be a view
+    of a larger, padded allocation whose rows are stride(0) bytes apart: that
+    stride goes to the library as the plane's pitch (0 when compact)."""
+    if t is None:
+        if not allocate:
+            raise ValueError("%s is required" % name)
+        return torch.empty(shape, dtype=torch.uint8, device=device), 0
+    if t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError("%s must be a uint8 tensor of shape %s on %s" % (name, tuple(shape), device))
+    if t.dim() != 2 or (shape[0] > 1 and shape[1] > 0 and (t.stride(1) != 1 or t.stride(0) < shape[1])):
+        raise ValueError("%s must have unit column stride and a row stride >= its width" % name)
+    pitch = t.stride(0) if shape[0] > 1 else shape[1]
+    return t, (0 if pitch == shape[1] else pitch)
+
+
+def padded_scale_plane(rows: int, cols: int, axis: int = 0, row_multiple: int = 1,
+                       col_multiple: int = 1, device=None, fill: int = 0):
+    """A scale plane for a [rows, cols] tensor inside a padded allocation.
+
+    The plane ([rows, cols/32] rowwise, [rows/32, cols] columnwise) is the
+    top-left view of a uint8 buffer whose shape is rounded up to multiples of
+    (row_multiple, col_multiple) and filled with `fill`; pass the view as an
+    output (or input) plane and the kernels use the buffer's row pitch
+    directly.  Returns (buffer, view)."""
+    shape = (rows, cols // BLOCK) if axis == ROWWISE else (rows // BLOCK, cols)
+    r = -(-shape[0] // row_multiple) * row_multiple
+    c = -(-shape[1] // col_multiple) * col_multiple
+    buf = torch.full((r, c), fill, dtype=torch.uint8, device=device)
+    return buf, buf[:shape[0], :shape[1]]
+
+
 def _quant_desc(x, rowwise, columnwise, out):
     if x.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("x must be bfloat16 or float32, got %s" % x.dtype)
@@ -156,10 +194,11 @@ def _quant_desc(x, rowwise, columnwise, out):
     o = out or MXFP8Planes(None, None, None, None)
     dev = x.device
     qr = _out(o.rowwise_data, (rows, cols), torch.uint8, dev, "rowwise_data") if rowwise else None
-    sr = _out(o.rowwise_scale, (rows, cols // BLOCK), torch.uint8, dev, "rowwise_scale") if rowwise else None
     qc = _out(o.columnwise_data, (rows, cols), torch.uint8, dev, "columnwise_data") if columnwise else None
-    sc = _out(o.columnwise_scale, (rows // BLOCK, cols), torch.uint8, dev, "columnwise_scale") if columnwise else None
-    d = _QuantDesc(_ptr(x2), rows, cols, _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc))
+    sr, pr = _scale_pitch(o.rowwise_scale, (rows, cols // BLOCK), dev, "rowwise_scale") if rowwise else (None, 0)
+    sc, pc = (_scale_pitch(o.columnwise_scale, (rows // BLOCK, cols), dev, "columnwise_scale")
+              if columnwise else (None, 0))
+    d = _QuantDesc(_ptr(x2), rows, cols, _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc), pr, pc)
     return d, MXFP8Planes(qr, qc, sr, sc)
 
 
@@ -171,9 +210,14 @@ def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
     ``out`` supplies persistent plane buffers that are overwritten in place
     (Megatron-Core quantization.utils page, quantize_params_to_mxfp8)."""
     d, planes = _quant_desc(x, rowwise, columnwise, out)
-    fn = lib().mxfp8_quantize if x.dtype == torch.bfloat16 else lib().mxfp8_quantize_f32
     with torch.cuda.device(x.device):
-        _check(fn(d.x, d.rows, d.cols, d.q_row, d.s_row, d.q_col, d.s_col, _stream(x.device)))
+        if d.s_row_pitch or d.s_col_pitch:
+            # padded scale planes: a one-entry grouped call carries the pitches
+            fn = lib().mxfp8_quantize_grouped if x.dtype == torch.bfloat16 else lib().mxfp8_quantize_f32_grouped
+            _check(fn((_QuantDesc * 1)(d), 1, _stream(x.device)))
+        else:
+            fn = lib().mxfp8_quantize if x.dtype == torch.bfloat16 else lib().mxfp8_quantize_f32
+            _check(fn(d.x, d.rows, d.cols, d.q_row, d.s_row, d.q_col, d.s_col, _stream(x.device)))
     return planes
 
 
@@ -207,9 +251,9 @@ def _norm_desc(x, gamma, weight_offset, eps, out):
     o = out or (None, None, None)
     normed = _out(o[0], (rows, cols), torch.bfloat16, dev, "normed")
     q = _out(o[1], (rows, cols), torch.uint8, dev, "q")
-    s = _out(o[2], (rows, cols // BLOCK), torch.uint8, dev, "s")
+    s, pitch = _scale_pitch(o[2], (rows, cols // BLOCK), dev, "s")
     d = _NormDesc(_ptr(x2), _ptr(g), float(weight_offset), float(eps), rows, cols,
-                  _ptr(normed), _ptr(q), _ptr(s))
+                  _ptr(normed), _ptr(q), _ptr(s), pitch)
     return d, (normed, q, s)
 
 
@@ -221,9 +265,12 @@ def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, weight_offset: float 
     [rows, cols/32]); the bytes equal ``quantize(normed)``."""
     d, res = _norm_desc(x, gamma, weight_offset, eps, out)
     with torch.cuda.device(x.device):
-        _check(lib().mxfp8_rmsnorm_quantize(d.x, d.gamma, d.weight_offset, d.eps, d.rows,
-                                            d.cols, d.normed, d.q_row, d.s_row,
-                                            _stream(x.device)))
+        if d.s_row_pitch:
+            _check(lib().mxfp8_rmsnorm_quantize_grouped((_NormDesc * 1)(d), 1, _stream(x.device)))
+        else:
+            _check(lib().mxfp8_rmsnorm_quantize(d.x, d.gamma, d.weight_offset, d.eps, d.rows,
+                                                d.cols, d.normed, d.q_row, d.s_row,
+                                                _stream(x.device)))
     return res
 
 
@@ -247,13 +294,13 @@ def rmsnorm_quantize_grouped(xs, gammas, weight_offsets, epss, outs=None) -> lis
 
 def _deq_desc(q, s, axis, dtype, out):
     q2 = _as2d(q, "q", torch.uint8)
-    s2 = _as2d(s, "s", torch.uint8)
     rows, cols = q2.shape
     want = (rows, cols // BLOCK) if axis == ROWWISE else (rows // BLOCK, cols)
-    if tuple(s2.shape) != want:
-        raise ValueError("scale shape %s, expected %s" % (tuple(s2.shape), want))
+    if not s.is_cuda:
+        raise ValueError("s must be a GPU tensor")
+    s2, pitch = _scale_pitch(s, want, q.device, "s", allocate=False)
     o = _out(out, (rows, cols), dtype, q.device, "out")
-    return _DeqDesc(_ptr(q2), _ptr(s2), rows, cols, int(axis), _ptr(o)), o
+    return _DeqDesc(_ptr(q2), _ptr(s2), rows, cols, int(axis), _ptr(o), pitch), o
 
 
 def _out_code(dtype):
@@ -270,8 +317,11 @@ def dequantize(q: torch.Tensor, s: torch.Tensor, axis: int = ROWWISE,
     code = _out_code(dtype)
     d, o = _deq_desc(q, s, axis, dtype, out)
     with torch.cuda.device(q.device):
-        _check(lib().mxfp8_dequantize(d.q, d.s, d.rows, d.cols, d.axis, d.out, code,
-                                      _stream(q.device)))
+        if d.s_pitch:
+            _check(lib().mxfp8_dequantize_grouped((_DeqDesc * 1)(d), 1, code, _stream(q.device)))
+        else:
+            _check(lib().mxfp8_dequantize(d.q, d.s, d.rows, d.cols, d.axis, d.out, code,
+                                          _stream(q.device)))
     return o
 
 
@@ -297,14 +347,16 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
     B = (qb [N, K], sb [N, K/32]) (quantization.utils page, mm_mxfp8: a
     quantized activation times a pre-quantized weight [out, in])."""
     code = _out_code(dtype)
-    qa2, sa2 = _as2d(qa, "qa", torch.uint8), _as2d(sa, "sa", torch.uint8)
-    qb2, sb2 = _as2d(qb, "qb", torch.uint8), _as2d(sb, "sb", torch.uint8)
+    qa2, qb2 = _as2d(qa, "qa", torch.uint8), _as2d(qb, "qb", torch.uint8)
     M, K = qa2.shape
     N = qb2.shape[0]
-    if qb2.shape[1] != K or tuple(sa2.shape) != (M, K // BLOCK) or tuple(sb2.shape) != (N, K // BLOCK):
+    if qb2.shape[1] != K:
         raise ValueError("gemm: planes must be qa [M, K], sa [M, K/32], qb [N, K], sb [N, K/32]")
+    # scale planes may be views of padded allocations (rows a pitch apart)
+    sa2, pa = _scale_pitch(sa, (M, K // BLOCK), qa.device, "sa", allocate=False)
+    sb2, pb = _scale_pitch(sb, (N, K // BLOCK), qa.device, "sb", allocate=False)
     o = _out(out, (M, N), dtype, qa.device, "out")
     with torch.cuda.device(qa.device):
-        _check(lib().mxfp8_gemm(_ptr(qa2), _ptr(sa2), _ptr(qb2), _ptr(sb2), M, N, K, _ptr(o), code,
+        _check(lib().mxfp8_gemm(_ptr(qa2), _ptr(sa2), _ptr(qb2), _ptr(sb2), M, N, K, pa, pb, _ptr(o), code,
                                 _stream(qa.device)))
     return o

@@ -12,7 +12,6 @@
 
 namespace {
 
-using mx::kGroupMax;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -23,8 +22,13 @@ bool fits(int64_t rows, int64_t cols) {
   return rows >= 0 && cols >= 0 && (cols == 0 || rows <= INT64_MAX / 4 / cols);
 }
 
+// A flat (rowwise-only) task finds a block's scale row by 32-bit division
+// when its plane has a pitch of its own.
+bool flat_blocks_fit(int64_t rows, int64_t cols) { return rows * (cols / MXFP8_BLOCK) <= (int64_t)UINT32_MAX; }
+
 mxfp8_status check_quant(const mxfp8_quant_desc& d) {
   if (d.rows < 0 || d.cols < 0 || !fits(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
+  if (d.s_row_pitch < 0 || d.s_col_pitch < 0) return MXFP8_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   const bool row = d.q_row || d.s_row, col = d.q_col || d.s_col;
   if ((d.q_row == nullptr) != (d.s_row == nullptr)) return MXFP8_ERR_NULL;
@@ -36,6 +40,15 @@ mxfp8_status check_quant(const mxfp8_quant_desc& d) {
   if (misaligned(d.x) || misaligned(d.q_row) || misaligned(d.s_row) ||
       misaligned(d.q_col) || misaligned(d.s_col))
     return MXFP8_ERR_ALIGN;
+  if (row && d.s_row_pitch) {
+    if (d.s_row_pitch < d.cols / MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
+    if (!col && d.s_row_pitch != d.cols / MXFP8_BLOCK && !flat_blocks_fit(d.rows, d.cols))
+      return MXFP8_ERR_SHAPE;
+  }
+  if (col && d.s_col_pitch) {
+    if (d.s_col_pitch < d.cols) return MXFP8_ERR_SHAPE;
+    if (d.s_col_pitch % 8) return MXFP8_ERR_ALIGN;
+  }
   return MXFP8_OK;
 }
 
@@ -43,56 +56,95 @@ mxfp8_status check_norm(const mxfp8_norm_desc& d) {
   if (d.rows < 0 || d.cols < 0 || d.rows > INT32_MAX || d.cols > INT32_MAX)
     return MXFP8_ERR_SHAPE;
   if (!isfinite(d.eps) || d.eps < 0.0f) return MXFP8_ERR_ARG;
+  if (d.s_row_pitch < 0) return MXFP8_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   if (!d.x || !d.gamma || !d.normed || !d.q_row || !d.s_row) return MXFP8_ERR_NULL;
   if (d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
   if (misaligned(d.x) || misaligned(d.gamma) || misaligned(d.normed) ||
       misaligned(d.q_row) || misaligned(d.s_row))
     return MXFP8_ERR_ALIGN;
+  if (d.s_row_pitch && d.s_row_pitch < d.cols / MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
   return MXFP8_OK;
 }
 
 mxfp8_status check_deq(const mxfp8_deq_desc& d) {
   if (d.axis != MXFP8_ROWWISE && d.axis != MXFP8_COLUMNWISE) return MXFP8_ERR_ARG;
   if (d.rows < 0 || d.cols < 0 || !fits(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
+  if (d.s_pitch < 0) return MXFP8_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   if (!d.q || !d.s || !d.out) return MXFP8_ERR_NULL;
   if (d.axis == MXFP8_ROWWISE && d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
   if (d.axis == MXFP8_COLUMNWISE && (d.rows % MXFP8_BLOCK || d.cols % 8))
     return MXFP8_ERR_SHAPE;
   if (misaligned(d.q) || misaligned(d.s) || misaligned(d.out)) return MXFP8_ERR_ALIGN;
+  if (d.s_pitch) {
+    if (d.axis == MXFP8_ROWWISE) {
+      if (d.s_pitch < d.cols / MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
+      if (d.s_pitch != d.cols / MXFP8_BLOCK && !flat_blocks_fit(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
+    } else {
+      if (d.s_pitch < d.cols) return MXFP8_ERR_SHAPE;
+      if (d.s_pitch % 8) return MXFP8_ERR_ALIGN;
+    }
+  }
   return MXFP8_OK;
 }
 
 mxfp8_status hip_status(hipError_t e) { return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_HIP; }
 
-// Packs non-empty tensors into argument blocks of at most kGroupMax entries
+// A tensor of a launch with the pitches of its scale planes.
+template <class Desc, class Pitch>
+struct Item {
+  Desc d;
+  Pitch p;
+  bool pitched;  // some pitch differs from the compact one
+};
+
+template <class Args, class It>
+void put(Args& a, int i, const It& it) {
+  a.d[i] = it.d;
+  if constexpr (Args::kPitched) a.p[i] = it.p;
+}
+
+// Packs non-empty tensors into argument blocks of at most Args::kMax entries
 // and kMaxTasksPerLaunch tasks, launching each block as it fills.
-template <class Args, class Desc, class TaskFn, class LaunchFn>
-mxfp8_status run_groups(const std::vector<Desc>& descs, TaskFn tasks, LaunchFn launch,
-                        Args& a) {
+template <class Args, class It, class TaskFn, class LaunchFn>
+mxfp8_status run_groups(const std::vector<It>& items, TaskFn tasks, LaunchFn launch, Args& a) {
   a.n = 0;
   a.task_start[0] = 0;
   int64_t total = 0;
   bool cleared = false;
-  for (const Desc& d : descs) {
-    const int64_t t = tasks(d);
+  for (const It& it : items) {
+    const int64_t t = tasks(it.d);
     if (t == 0) continue;
     if (!cleared) {
       (void)hipGetLastError();  // report only errors raised by this call's launches
       cleared = true;
     }
-    if (a.n == kGroupMax || total + t > kMaxTasksPerLaunch) {
+    if (a.n == Args::kMax || total + t > kMaxTasksPerLaunch) {
       if (mxfp8_status st = hip_status(launch(a, total))) return st;
       a.n = 0;
       total = 0;
     }
-    a.d[a.n] = d;
+    put(a, a.n, it);
     total += t;
     a.task_start[++a.n] = (int32_t)total;
   }
   if (a.n) return hip_status(launch(a, total));
   return MXFP8_OK;
+}
+
+// Runs the items through the compact argument block, or through the pitched
+// one when any plane has a pitch of its own.
+template <class Compact, class Pitched, class It, class TaskFn, class LaunchFn>
+mxfp8_status run_items(const std::vector<It>& items, TaskFn tasks, LaunchFn launch) {
+  bool pitched = false;
+  for (const It& it : items) pitched |= it.pitched;
+  if (pitched) {
+    Pitched a;
+    return run_groups(items, tasks, [&](const Pitched& args, int64_t t) { return launch(args, t); }, a);
+  }
+  Compact a;
+  return run_groups(items, tasks, [&](const Compact& args, int64_t t) { return launch(args, t); }, a);
 }
 
 mx::QuantDesc to_internal(const mxfp8_quant_desc& d) {
@@ -132,6 +184,38 @@ mx::DeqDesc to_internal(const mxfp8_deq_desc& d) {
   return q;
 }
 
+using QuantItem = Item<mx::QuantDesc, mx::QuantPitch>;
+using NormItem = Item<mx::NormDesc, int64_t>;
+using DeqItem = Item<mx::DeqDesc, int64_t>;
+
+QuantItem to_item(const mxfp8_quant_desc& d) {
+  QuantItem it;
+  it.d = to_internal(d);
+  const int64_t wr = d.cols / MXFP8_BLOCK, wc = d.cols;
+  it.p.s_row = d.s_row_pitch ? d.s_row_pitch : wr;
+  it.p.s_col = d.s_col_pitch ? d.s_col_pitch : wc;
+  it.pitched = (d.s_row && it.p.s_row != wr) || (d.s_col && it.p.s_col != wc);
+  return it;
+}
+
+NormItem to_item(const mxfp8_norm_desc& d) {
+  NormItem it;
+  it.d = to_internal(d);
+  const int64_t w = d.cols / MXFP8_BLOCK;
+  it.p = d.s_row_pitch ? d.s_row_pitch : w;
+  it.pitched = it.p != w;
+  return it;
+}
+
+DeqItem to_item(const mxfp8_deq_desc& d) {
+  DeqItem it;
+  it.d = to_internal(d);
+  const int64_t w = d.axis == MXFP8_COLUMNWISE ? d.cols : d.cols / MXFP8_BLOCK;
+  it.p = d.s_pitch ? d.s_pitch : w;
+  it.pitched = it.p != w;
+  return it;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,17 +239,15 @@ mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc* descs, int32_t n, vo
   if (n < 0) return MXFP8_ERR_ARG;
   if (n == 0) return MXFP8_OK;
   if (!descs) return MXFP8_ERR_NULL;
-  std::vector<mx::QuantDesc> v;
+  std::vector<QuantItem> v;
   v.reserve(n);
   for (int32_t i = 0; i < n; ++i) {
     if (mxfp8_status st = check_quant(descs[i])) return st;
-    v.push_back(to_internal(descs[i]));
+    v.push_back(to_item(descs[i]));
   }
-  mx::QuantArgs a;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return run_groups(v, mx::quant_tasks,
-                    [&](const mx::QuantArgs& args, int64_t t) { return mx::launch_quantize(args, t, s); },
-                    a);
+  return run_items<mx::QuantArgs, mx::QuantArgsPitched>(
+      v, mx::quant_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize(args, t, s); });
 }
 
 mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc* descs, int32_t n,
@@ -173,28 +255,26 @@ mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc* descs, int32_t n
   if (n < 0) return MXFP8_ERR_ARG;
   if (n == 0) return MXFP8_OK;
   if (!descs) return MXFP8_ERR_NULL;
-  std::vector<mx::QuantDesc> v;
+  std::vector<QuantItem> v;
   v.reserve(n);
   for (int32_t i = 0; i < n; ++i) {
     if (mxfp8_status st = check_quant(descs[i])) return st;
-    v.push_back(to_internal(descs[i]));
+    v.push_back(to_item(descs[i]));
   }
-  mx::QuantArgs a;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return run_groups(v, mx::quant_f32_tasks,
-                    [&](const mx::QuantArgs& args, int64_t t) { return mx::launch_quantize_f32(args, t, s); },
-                    a);
+  return run_items<mx::QuantArgs, mx::QuantArgsPitched>(
+      v, mx::quant_f32_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize_f32(args, t, s); });
 }
 
 mxfp8_status mxfp8_quantize_f32(const void* x, int64_t rows, int64_t cols, void* q_row,
                                 void* s_row, void* q_col, void* s_col, void* stream) {
-  mxfp8_quant_desc d = {x, rows, cols, q_row, s_row, q_col, s_col};
+  mxfp8_quant_desc d = {x, rows, cols, q_row, s_row, q_col, s_col, 0, 0};
   return mxfp8_quantize_f32_grouped(&d, 1, stream);
 }
 
 mxfp8_status mxfp8_quantize(const void* x, int64_t rows, int64_t cols, void* q_row,
                             void* s_row, void* q_col, void* s_col, void* stream) {
-  mxfp8_quant_desc d = {x, rows, cols, q_row, s_row, q_col, s_col};
+  mxfp8_quant_desc d = {x, rows, cols, q_row, s_row, q_col, s_col, 0, 0};
   return mxfp8_quantize_grouped(&d, 1, stream);
 }
 
@@ -203,12 +283,12 @@ mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc* descs, int32_
   if (n < 0) return MXFP8_ERR_ARG;
   if (n == 0) return MXFP8_OK;
   if (!descs) return MXFP8_ERR_NULL;
-  std::vector<mx::NormDesc> v;
+  std::vector<NormItem> v;
   v.reserve(n);
   int64_t max_cols = 0, total_rows = 0;
   for (int32_t i = 0; i < n; ++i) {
     if (mxfp8_status st = check_norm(descs[i])) return st;
-    v.push_back(to_internal(descs[i]));
+    v.push_back(to_item(descs[i]));
     if (descs[i].rows > 0 && descs[i].cols > 0) {
       if (descs[i].cols > max_cols) max_cols = descs[i].cols;
       total_rows += descs[i].rows;
@@ -216,20 +296,16 @@ mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc* descs, int32_
   }
   const int variant = mx::norm_variant(max_cols);
   const int rpt = mx::norm_rows_per_task(total_rows, variant);
-  mx::NormArgs a;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return run_groups(
+  return run_items<mx::NormArgs, mx::NormArgsPitched>(
       v, [rpt](const mx::NormDesc& d) -> int64_t { return d.cols ? (d.rows + rpt - 1) / rpt : 0; },
-      [&](const mx::NormArgs& args, int64_t t) {
-        return mx::launch_rmsnorm_quantize(args, t, variant, rpt, s);
-      },
-      a);
+      [&](const auto& args, int64_t t) { return mx::launch_rmsnorm_quantize(args, t, variant, rpt, s); });
 }
 
 mxfp8_status mxfp8_rmsnorm_quantize(const void* x, const void* gamma, float weight_offset,
                                     float eps, int64_t rows, int64_t cols, void* normed,
                                     void* q_row, void* s_row, void* stream) {
-  mxfp8_norm_desc d = {x, gamma, weight_offset, eps, rows, cols, normed, q_row, s_row};
+  mxfp8_norm_desc d = {x, gamma, weight_offset, eps, rows, cols, normed, q_row, s_row, 0};
   return mxfp8_rmsnorm_quantize_grouped(&d, 1, stream);
 }
 
@@ -239,42 +315,48 @@ mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc* descs, int32_t n,
   if (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16) return MXFP8_ERR_ARG;
   if (n == 0) return MXFP8_OK;
   if (!descs) return MXFP8_ERR_NULL;
-  std::vector<mx::DeqDesc> v;
+  std::vector<DeqItem> v;
   v.reserve(n);
   for (int32_t i = 0; i < n; ++i) {
     if (mxfp8_status st = check_deq(descs[i])) return st;
-    v.push_back(to_internal(descs[i]));
+    v.push_back(to_item(descs[i]));
   }
-  mx::DeqArgs a;
-  a.out_bf16 = out_dtype == MXFP8_OUT_BF16;
+  const int32_t bf16 = out_dtype == MXFP8_OUT_BF16;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return run_groups(v, mx::deq_tasks,
-                    [&](const mx::DeqArgs& args, int64_t t) { return mx::launch_dequantize(args, t, s); },
-                    a);
+  return run_items<mx::DeqArgs, mx::DeqArgsPitched>(v, mx::deq_tasks, [&](auto args, int64_t t) {
+    args.out_bf16 = bf16;
+    return mx::launch_dequantize(args, t, s);
+  });
 }
 
 mxfp8_status mxfp8_gemm(const void* qa, const void* sa, const void* qb, const void* sb,
-                        int64_t M, int64_t N, int64_t K, void* out, mxfp8_out_dtype out_dtype,
-                        void* stream) {
+                        int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
+                        void* out, mxfp8_out_dtype out_dtype, void* stream) {
   if (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16) return MXFP8_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || !fits(M, K) || !fits(N, K) || !fits(M, N)) return MXFP8_ERR_SHAPE;
+  if (sa_pitch < 0 || sb_pitch < 0) return MXFP8_ERR_SHAPE;
   if (M == 0 || N == 0) return MXFP8_OK;
   if (K == 0 || K % 128) return MXFP8_ERR_SHAPE;
   if (!qa || !sa || !qb || !sb || !out) return MXFP8_ERR_NULL;
   if (misaligned(qa) || misaligned(sa) || misaligned(qb) || misaligned(sb) || misaligned(out))
     return MXFP8_ERR_ALIGN;
+  const int64_t kb = K / MXFP8_BLOCK;
+  if (!sa_pitch) sa_pitch = kb;
+  if (!sb_pitch) sb_pitch = kb;
+  if (sa_pitch < kb || sb_pitch < kb || !fits(M, sa_pitch) || !fits(N, sb_pitch)) return MXFP8_ERR_SHAPE;
+  if (sa_pitch % 4 || sb_pitch % 4) return MXFP8_ERR_ALIGN;
   if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return MXFP8_ERR_SHAPE;
   (void)hipGetLastError();
   return hip_status(mx::launch_gemm(static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa),
                                     static_cast<const uint8_t*>(qb), static_cast<const uint8_t*>(sb),
-                                    M, N, K, out, out_dtype == MXFP8_OUT_BF16,
+                                    M, N, K, sa_pitch, sb_pitch, out, out_dtype == MXFP8_OUT_BF16,
                                     static_cast<hipStream_t>(stream)));
 }
 
 mxfp8_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t cols,
                               mxfp8_axis axis, void* out, mxfp8_out_dtype out_dtype,
                               void* stream) {
-  mxfp8_deq_desc d = {q, s, rows, cols, axis, out};
+  mxfp8_deq_desc d = {q, s, rows, cols, axis, out, 0};
   return mxfp8_dequantize_grouped(&d, 1, out_dtype, stream);
 }
 

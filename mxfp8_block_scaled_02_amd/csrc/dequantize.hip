@@ -48,7 +48,7 @@ __device__ __forceinline__ void put4(void* out, bool bf16, int64_t e, uint32_t q
 
 // Rowwise planes, walked flat in 4-element units: unit u of a wave task is
 // lane + 64 u, so every load and store instruction covers contiguous memory.
-__device__ void deq_flat_task(const DeqDesc& d, bool bf16, int64_t task, int lane) {
+__device__ void deq_flat_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int64_t task, int lane) {
   const int64_t nunits = d.rows * d.cols / 4;
   const int64_t base = task * (int64_t)(kWave * kDeqUnroll) + lane;
   uint32_t q[kDeqUnroll], s[kDeqUnroll];
@@ -57,7 +57,7 @@ __device__ void deq_flat_task(const DeqDesc& d, bool bf16, int64_t task, int lan
     const int64_t p = base + u * kWave;
     const bool ok = p < nunits;
     q[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(d.q) + p) : 0u;
-    s[u] = ok ? d.s[p >> 3] : 0u;                    // 8 units per 32-element block
+    s[u] = ok ? d.s[pitched_block(p >> 3, d.cols >> 5, s_pitch)] : 0u;   // 8 units per block
   }
 #pragma unroll
   for (int u = 0; u < kDeqUnroll; ++u) {
@@ -72,14 +72,14 @@ __device__ void deq_flat_task(const DeqDesc& d, bool bf16, int64_t task, int lan
 
 // Columnwise planes: kDeqRows rows x 256 columns per wave task; lane l owns
 // columns 4l .. 4l+3 and reads their scale bytes once.
-__device__ void deq_col_task(const DeqDesc& d, bool bf16, int64_t task, int lane) {
+__device__ void deq_col_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int64_t task, int lane) {
   const int64_t cols = d.cols;
   const int64_t col_tiles = (cols + kDeqTileCols - 1) / kDeqTileCols;
   const int64_t r0 = (task / col_tiles) * kDeqRows;
   const int64_t c = (task % col_tiles) * kDeqTileCols + (int64_t)lane * 4;
   if (c >= cols) return;                              // cols % 8 == 0: whole units only
   // rows r0 .. r0 + kDeqRows - 1 lie in one 32-row block (kDeqRows divides 32)
-  const uint32_t sb = *reinterpret_cast<const uint32_t*>(d.s + (r0 / kBlock) * cols + c);
+  const uint32_t sb = *reinterpret_cast<const uint32_t*>(d.s + (r0 / kBlock) * s_pitch + c);
   float sc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) sc[k] = e8m0_value((sb >> (8 * k)) & 0xFFu);
@@ -91,7 +91,8 @@ __device__ void deq_col_task(const DeqDesc& d, bool bf16, int64_t task, int lane
   for (int r = 0; r < kDeqRows; ++r) put4(d.out, bf16, (r0 + r) * cols + c, q[r], sc);
 }
 
-__global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const DeqArgs a) {
+template <class Args>
+__global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const Args a) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t task = (int32_t)blockIdx.x * kWavesPerGroup + wave;
@@ -99,24 +100,31 @@ __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const DeqArg
   // table size (the empty asm keeps those loads ahead of the branch)
   DeqDesc d0 = a.d[0];
   int32_t total0 = a.task_start[1];
+  int64_t p0 = 0;
+  if constexpr (Args::kPitched) {
+    p0 = a.pitch(0);
+    asm volatile("" : "+s"(p0));
+  }
   asm volatile("" : "+s"(d0.q), "+s"(d0.s), "+s"(d0.out), "+s"(d0.rows), "+s"(d0.cols), "+s"(d0.axis),
                "+s"(total0));
+  if constexpr (!Args::kPitched) p0 = d0.axis ? d0.cols : d0.cols >> 5;
   if (a.n == 1) {
     if (task >= total0) return;
     if (d0.axis == 0)
-      deq_flat_task(d0, a.out_bf16 != 0, task, lane);
+      deq_flat_task(d0, p0, a.out_bf16 != 0, task, lane);
     else
-      deq_col_task(d0, a.out_bf16 != 0, task, lane);
+      deq_col_task(d0, p0, a.out_bf16 != 0, task, lane);
     return;
   }
   if (task >= a.task_start[a.n]) return;
   const int i = find_desc(a.task_start, a.n, task);
-  const DeqDesc& d = a.d[i];
+  const DeqDesc d = a.d[i];
+  const int64_t pi = Args::kPitched ? a.pitch(i) : (d.axis ? d.cols : d.cols >> 5);
   const int64_t local = task - a.task_start[i];
   if (d.axis == 0)
-    deq_flat_task(d, a.out_bf16 != 0, local, lane);
+    deq_flat_task(d, pi, a.out_bf16 != 0, local, lane);
   else
-    deq_col_task(d, a.out_bf16 != 0, local, lane);
+    deq_col_task(d, pi, a.out_bf16 != 0, local, lane);
 }
 
 }  // namespace
@@ -134,7 +142,14 @@ int64_t deq_tasks(const DeqDesc& d) {
 hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
   const int64_t groups = (total_tasks + kWavesPerGroup - 1) / kWavesPerGroup;
-  hipLaunchKernelGGL(mxfp8_dequantize_kernel, dim3((uint32_t)groups), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(mxfp8_dequantize_kernel<DeqArgs>, dim3((uint32_t)groups), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipStream_t s) {
+  if (total_tasks <= 0) return hipSuccess;
+  const int64_t groups = (total_tasks + kWavesPerGroup - 1) / kWavesPerGroup;
+  hipLaunchKernelGGL(mxfp8_dequantize_kernel<DeqArgsPitched>, dim3((uint32_t)groups), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -34,10 +34,12 @@
 //   pairs start K at different quarters.
 // * tile128: 128 x 128 tiles (four waves of 64 x 64) staged through registers
 //   into padded LDS rows; it takes problems with too few 256 x 256 tiles to
-//   fill the chip, or K not a multiple of 512.
+//   fill the chip, K not a multiple of 512 or scale pitches not multiples of 16.
 //
 // Rows of A or B past M or N read a valid row (the last one) and their
-// outputs are not stored.  K must be a multiple of 128.  The order in which
+// outputs are not stored.  K must be a multiple of 128, and the scale planes'
+// rows are a caller-given pitch apart (a multiple of 4; tile256 also wants a
+// multiple of 16, as compact planes with K % 512 == 0 have).  The order in which
 // the 64-deep MFMA steps accumulate depends on the tiling and, for tile256, on
 // the tile's starting quarter; every order stays within the tolerance that
 // the tests derive for the instruction.
@@ -58,6 +60,7 @@ struct GemmParams {
   const uint8_t* sb;
   void* out;
   int64_t M, N, K;
+  int64_t sa_ld, sb_ld;       // bytes between scale rows of A and of B
   int32_t out_bf16;
   int32_t tiles_m, tiles_n;
 };
@@ -135,14 +138,14 @@ __device__ __forceinline__ void load_stage(const uint8_t* base, int64_t rows, in
   }
 }
 
-// the 16 scale bytes of 512 k (k blocks kb0 .. kb0+15) of rows r0 .. r0+255,
-// one row per lane: wave w loads rows 64 w .. 64 w + 63
+// the 16 scale bytes of 512 k (k blocks kb0 .. kb0+15) of rows r0 .. r0+255
+// (rows ld bytes apart), one row per lane: wave w loads rows 64 w .. 64 w + 63
 __device__ __forceinline__ void load_scales(const uint8_t* s, int64_t rows, int64_t r0,
-                                            int64_t kblocks, int64_t kb0, uint8_t* lds, int wave,
+                                            int64_t ld, int64_t kb0, uint8_t* lds, int wave,
                                             int lane) {
   int64_t row = r0 + 64 * wave + lane;
   row = row < rows ? row : rows - 1;
-  __builtin_amdgcn_global_load_lds(s + row * kblocks + kb0, (lds_ptr)(lds + 1024 * wave), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(s + row * ld + kb0, (lds_ptr)(lds + 1024 * wave), 16, 0, 0);
 }
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt left alone)
@@ -164,7 +167,7 @@ template <int N> __device__ __forceinline__ void ring_barrier() {
 struct Tile256 {
   const GemmParams& p;
   int wave, lane, fr, h;
-  int64_t m0, n0, K, kblocks, stages;
+  int64_t m0, n0, K, stages;
   int64_t kstart;               // first stage of this tile (K order rotated per tile)
   int swz;                      // row_swizzle of this lane's fragment rows
   int arow, brow;               // LDS byte offset of this lane's row in tile 0
@@ -177,7 +180,6 @@ struct Tile256 {
     fr = lane & 31;
     h = lane >> 5;
     K = p.K;
-    kblocks = K / kBlock;
     stages = K / kBK;
     swz = row_swizzle(fr);
     arow = ((wave >> 1) * 128 + fr) * kBK;
@@ -202,8 +204,8 @@ struct Tile256 {
       const int64_t kb0 = (tt / kGroup) * 16;
       const int gpar = (int)((t / kGroup) & 1);
       uint8_t* sc = gpar ? s_scale1 : s_scale0;
-      load_scales(p.sa, p.M, m0, kblocks, kb0, sc, wave, lane);
-      load_scales(p.sb, p.N, n0, kblocks, kb0, sc + kScBytes, wave, lane);
+      load_scales(p.sa, p.M, m0, p.sa_ld, kb0, sc, wave, lane);
+      load_scales(p.sb, p.N, n0, p.sb_ld, kb0, sc + kScBytes, wave, lane);
     }
   }
 
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = (int64_t)(blockIdx.x / p.tiles_n) * kGT;
   const int64_t n0 = (int64_t)(blockIdx.x % p.tiles_n) * kGT;
-  const int64_t K = p.K, kblocks = K / kBlock;
+  const int64_t K = p.K;
 
   // global -> LDS: thread t moves 16-byte chunks t + 256 u (u < 4) of each
   // 128 x 128-byte tile: row (t >> 3) + 32 u, k offset 16 (t & 7)
@@ -403,13 +405,13 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
     brow[i] = n0 + wn * 64 + 32 * i + fr;
   }
   // scale bytes of this lane for k tile k0: index [tile i][64-k step s]
-  auto scales = [&](const uint8_t* s, const int64_t* rows, int64_t nrows, int64_t k0,
+  auto scales = [&](const uint8_t* s, int64_t ld, const int64_t* rows, int64_t nrows, int64_t k0,
                     uint32_t (&out)[2][2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int st = 0; st < 2; ++st)
-        out[i][st] = rows[i] < nrows ? s[rows[i] * kblocks + k0 / kBlock + 2 * st + h] : 127u;
+        out[i][st] = rows[i] < nrows ? s[rows[i] * ld + k0 / kBlock + 2 * st + h] : 127u;
   };
 
   v16f acc[2][2];
@@ -420,8 +422,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
 
   uint32_t sa_cur[2][2], sb_cur[2][2], sa_nxt[2][2], sb_nxt[2][2];
   fetch(0);
-  scales(p.sa, arow, p.M, 0, sa_cur);
-  scales(p.sb, brow, p.N, 0, sb_cur);
+  scales(p.sa, p.sa_ld, arow, p.M, 0, sa_cur);
+  scales(p.sb, p.sb_ld, brow, p.N, 0, sb_cur);
   stash(0);
   __syncthreads();
 
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
     const bool more = kt + 1 < ktiles;
     if (more) {
       fetch((kt + 1) * kGK);
-      scales(p.sa, arow, p.M, (kt + 1) * kGK, sa_nxt);
-      scales(p.sb, brow, p.N, (kt + 1) * kGK, sb_nxt);
+      scales(p.sa, p.sa_ld, arow, p.M, (kt + 1) * kGK, sa_nxt);
+      scales(p.sb, p.sb_ld, brow, p.N, (kt + 1) * kGK, sb_nxt);
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -511,7 +513,7 @@ struct SkinnyChunk {
 struct Skinny {
   const GemmParams& p;
   int wave, lane, fr, h;
-  int64_t n0, K, kblocks, u1;
+  int64_t n0, K, u1;
   uint32_t amask;               // ~0 for a real A row, 0 for a padding row
   const uint8_t* pa;
   const uint8_t* psa;
@@ -567,13 +569,13 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, h = lane >> 5;
   const int64_t n0 = (int64_t)blockIdx.x * 32;
-  const int64_t K = p.K, kblocks = K / kBlock, units = K / 128;
+  const int64_t K = p.K, units = K / 128;
   const int64_t u0 = units * wave / kSkinnyWaves, u1 = units * (wave + 1) / kSkinnyWaves;
 
-  Skinny sk{p, wave, lane, fr, h, n0, K, kblocks, u1, fr < p.M ? ~0u : 0u,
+  Skinny sk{p, wave, lane, fr, h, n0, K, u1, fr < p.M ? ~0u : 0u,
             p.qa + min((int64_t)fr, p.M - 1) * K + 16 * h,
-            p.sa + min((int64_t)fr, p.M - 1) * kblocks,
-            p.sb + min(n0 + fr, p.N - 1) * kblocks};
+            p.sa + min((int64_t)fr, p.M - 1) * p.sa_ld,
+            p.sb + min(n0 + fr, p.N - 1) * p.sb_ld};
 
   // Chunk pipeline, explicit about waits: each block of loads and each block
   // of MFMAs is pinned in place (compiler memory fence + scheduling barrier),
@@ -630,17 +632,20 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
-                       int64_t M, int64_t N, int64_t K, void* out, bool out_bf16, hipStream_t s) {
+                       int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
+                       void* out, bool out_bf16, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmParams p;
   p.qa = qa; p.sa = sa; p.qb = qb; p.sb = sb; p.out = out;
   p.M = M; p.N = N; p.K = K;
+  p.sa_ld = sa_pitch; p.sb_ld = sb_pitch;
   p.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t big = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
   if (M <= 32) {
     const int64_t tiles = (N + 31) / 32;
     hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
-  } else if (big >= kGemmFillTiles && K % (kBK * kGroup) == 0) {
+  } else if (big >= kGemmFillTiles && K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 &&
+             sb_pitch % 16 == 0) {
     p.tiles_m = (int32_t)((M + kBT - 1) / kBT);
     p.tiles_n = (int32_t)((N + kBT - 1) / kBT);
     hipLaunchKernelGGL(mxfp8_gemm_tile256_kernel, dim3((uint32_t)big), dim3(kThreads), 0, s, p);

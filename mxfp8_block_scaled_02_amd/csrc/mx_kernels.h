@@ -14,6 +14,7 @@
 namespace mx {
 
 constexpr int kGroupMax = 64;        // tensors per launch (argument block < 4 KiB)
+constexpr int kPitchedGroupMax = 32; // the same with per-tensor scale pitches
 constexpr int kWavesPerGroup = 4;    // waves per workgroup
 constexpr int kThreads = 64 * kWavesPerGroup;
 constexpr int kLaneCols = 8;         // consecutive row elements a lane holds (8 or 16)
@@ -34,20 +35,42 @@ struct QuantDesc {
   uint8_t* s_col;  // NULL: columnwise plane not requested
   int64_t rows, cols;
 };
+// Bytes from one row of a scale plane to the next.  Compact planes have the
+// plane's width; a padded allocation (a consumer's layout) has more.
+struct QuantPitch {
+  int64_t s_row, s_col;
+};
+// Compact planes: the pitch follows from the shape.
 struct QuantArgs {
+  static constexpr int kMax = kGroupMax;
+  static constexpr bool kPitched = false;
   int32_t n;
-  int32_t task_start[kGroupMax + 1];
-  QuantDesc d[kGroupMax];
+  int32_t task_start[kMax + 1];
+  QuantDesc d[kMax];
+  __device__ QuantPitch pitch(int i) const { return {d[i].cols >> 5, d[i].cols}; }
+};
+// Planes with pitches of their own (fewer tensors per launch: the argument
+// block stays under 4 KiB).
+struct QuantArgsPitched {
+  static constexpr int kMax = kPitchedGroupMax;
+  static constexpr bool kPitched = true;
+  int32_t n;
+  int32_t task_start[kMax + 1];
+  QuantDesc d[kMax];
+  QuantPitch p[kMax];
+  __device__ QuantPitch pitch(int i) const { return p[i]; }
 };
 // Workgroup tasks a tensor needs: 32 x 1024 tiles when a columnwise plane is
 // requested, otherwise 256 x kFlatUnroll 16-element pieces of the flattened
 // tensor.
 int64_t quant_tasks(const QuantDesc& d);
 hipError_t launch_quantize(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
+hipError_t launch_quantize(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s);
 // The same for float32 input (QuantDesc::x points to float): 32 x 256 tiles
 // or 256 x kFlatUnroll 4-element pieces.
 int64_t quant_f32_tasks(const QuantDesc& d);
 hipError_t launch_quantize_f32(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
+hipError_t launch_quantize_f32(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s);
 
 // ---- RMSNorm + rowwise quantize ------------------------------------------
 struct NormDesc {
@@ -60,9 +83,21 @@ struct NormDesc {
   float weight_offset, eps;
 };
 struct NormArgs {
+  static constexpr int kMax = kGroupMax;
+  static constexpr bool kPitched = false;
   int32_t n;
-  int32_t task_start[kGroupMax + 1];
-  NormDesc d[kGroupMax];
+  int32_t task_start[kMax + 1];
+  NormDesc d[kMax];
+  __device__ int64_t pitch(int i) const { return d[i].cols >> 5; }
+};
+struct NormArgsPitched {
+  static constexpr int kMax = kPitchedGroupMax;
+  static constexpr bool kPitched = true;
+  int32_t n;
+  int32_t task_start[kMax + 1];
+  NormDesc d[kMax];
+  int64_t p[kMax];   // bytes between rows of the scale plane
+  __device__ int64_t pitch(int i) const { return p[i]; }
 };
 // Kernel shape for the longest row of a launch: waves per row and chunks
 // per lane (see rmsnorm_quantize.hip).  A task is rows_per_task consecutive
@@ -70,6 +105,8 @@ struct NormArgs {
 int norm_variant(int64_t cols);
 int norm_rows_per_task(int64_t total_rows, int variant);
 hipError_t launch_rmsnorm_quantize(const NormArgs& a, int64_t total_tasks, int variant,
+                                   int rows_per_task, hipStream_t s);
+hipError_t launch_rmsnorm_quantize(const NormArgsPitched& a, int64_t total_tasks, int variant,
                                    int rows_per_task, hipStream_t s);
 
 // ---- dequantize ----------------------------------------------------------
@@ -81,18 +118,43 @@ struct DeqDesc {
   int32_t axis;  // 0 rowwise scales, 1 columnwise scales
 };
 struct DeqArgs {
+  static constexpr int kMax = kGroupMax;
+  static constexpr bool kPitched = false;
   int32_t n;
   int32_t out_bf16;
-  int32_t task_start[kGroupMax + 1];
-  DeqDesc d[kGroupMax];
+  int32_t task_start[kMax + 1];
+  DeqDesc d[kMax];
+  __device__ int64_t pitch(int i) const { return d[i].axis ? d[i].cols : d[i].cols >> 5; }
+};
+struct DeqArgsPitched {
+  static constexpr int kMax = kPitchedGroupMax;
+  static constexpr bool kPitched = true;
+  int32_t n;
+  int32_t out_bf16;
+  int32_t task_start[kMax + 1];
+  DeqDesc d[kMax];
+  int64_t p[kMax];   // bytes between rows of the scale plane
+  __device__ int64_t pitch(int i) const { return p[i]; }
 };
 int64_t deq_tasks(const DeqDesc& d);
 hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s);
+hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipStream_t s);
 
 // ---- MXFP8 matrix product -------------------------------------------------
 // out[M, N] (float32, or bf16 if out_bf16) = A . B^T for rowwise planes
 // A = (qa [M, K], sa [M, K/32]), B = (qb [N, K], sb [N, K/32]); K % 128 == 0.
+// Scale rows are sa_pitch and sb_pitch bytes apart (multiples of 4).
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
-                       int64_t M, int64_t N, int64_t K, void* out, bool out_bf16, hipStream_t s);
+                       int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
+                       void* out, bool out_bf16, hipStream_t s);
+
+// Scale index of flat block b of a plane with bpr blocks per row, stored
+// with rows pitch bytes apart (b < 2^32 whenever pitch != bpr).
+__device__ __forceinline__ int64_t pitched_block(int64_t b, int64_t bpr, int64_t pitch) {
+  if (pitch == bpr) return b;
+  const uint32_t ub = (uint32_t)b, ubpr = (uint32_t)bpr;
+  const uint32_t r = ub / ubpr;
+  return (int64_t)r * pitch + (ub - r * ubpr);
+}
 
 }  // namespace mx

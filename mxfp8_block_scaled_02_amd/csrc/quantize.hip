@@ -48,7 +48,7 @@ __device__ __forceinline__ RowScale lane_row_scale(const u32x4* v) {
     return row_scale_key(pair_max(chunk16_key(v[0], v[1])));
 }
 
-__device__ void quant_flat_task(const QuantDesc& d, int64_t task, int tid) {
+__device__ void quant_flat_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid) {
   const int64_t npieces = d.rows * d.cols / kLaneCols;   // whole blocks: cols % 32 == 0
   const int64_t base = task * (int64_t)(kThreads * kFlatUnroll) + tid;
   u32x4 v[kFlatUnroll][kCh];
@@ -68,13 +68,13 @@ __device__ void quant_flat_task(const QuantDesc& d, int64_t task, int tid) {
       for (int h = 0; h < kCh; ++h)
         store8(d.q_row + p * kLaneCols + h * kChunk, encode_chunk_row(v[u][h], rs));
       if ((tid & (kBlock / kLaneCols - 1)) == 0)
-        d.s_row[p * kLaneCols / kBlock] = (uint8_t)rs.sbyte;
+        d.s_row[pitched_block(p * kLaneCols / kBlock, d.cols >> 5, pitch.s_row)] = (uint8_t)rs.sbyte;
     }
   }
 }
 
-__device__ void quant_tile_task(const QuantDesc& d, int64_t task, int wave, int lane,
-                                u32x4* colmax) {
+__device__ void quant_tile_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task,
+                                int wave, int lane, u32x4* colmax) {
   const int64_t cols = d.cols;
   const int64_t col_tiles = (cols + kTileCols - 1) / kTileCols;
   const int64_t rb = task / col_tiles;                       // 32-row block index
@@ -94,7 +94,7 @@ __device__ void quant_tile_task(const QuantDesc& d, int64_t task, int wave, int 
 
   if (d.q_row) {
     // cols % 32 == 0 here, so a block's lanes are either all present or absent
-    const int64_t sb_per_row = cols / kBlock;
+    const int64_t sb_per_row = pitch.s_row;
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       const RowScale rs = lane_row_scale(v[r]);
@@ -148,7 +148,7 @@ __device__ void quant_tile_task(const QuantDesc& d, int64_t task, int wave, int 
     if (wave == 0) {
 #pragma unroll
       for (int h = 0; h < kCh; ++h)
-        if (ok[h]) store8(d.s_col + rb * cols + c + h * kChunk, sb[h]);
+        if (ok[h]) store8(d.s_col + rb * pitch.s_col + c + h * kChunk, sb[h]);
     }
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; r += 2) {
@@ -173,7 +173,8 @@ __device__ void quant_tile_task(const QuantDesc& d, int64_t task, int wave, int 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const QuantArgs a) {
+template <class Args>
+__global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const Args a) {
   __shared__ u32x4 colmax[kThreads * kCh];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -183,22 +184,29 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const QuantArg
   // table size (the empty asm keeps those loads ahead of the branch), so the
   // first global load waits for one scalar round trip instead of two
   QuantDesc d0 = a.d[0];
+  QuantPitch p0 = {0, 0};
+  if constexpr (Args::kPitched) {
+    p0 = a.pitch(0);
+    asm volatile("" : "+s"(p0.s_row), "+s"(p0.s_col));
+  }
   asm volatile("" : "+s"(d0.x), "+s"(d0.q_row), "+s"(d0.s_row), "+s"(d0.q_col), "+s"(d0.s_col),
                "+s"(d0.rows), "+s"(d0.cols));
+  if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, d0.cols};
   if (a.n == 1) {
     if (d0.q_col)
-      quant_tile_task(d0, task, wave, lane, colmax);
+      quant_tile_task(d0, p0, task, wave, lane, colmax);
     else
-      quant_flat_task(d0, task, tid);
+      quant_flat_task(d0, p0, task, tid);
     return;
   }
   const int i = find_desc(a.task_start, a.n, task);
-  const QuantDesc& d = a.d[i];
+  const QuantDesc d = a.d[i];
+  const QuantPitch pi = Args::kPitched ? a.pitch(i) : QuantPitch{d.cols >> 5, d.cols};
   const int64_t local = task - a.task_start[i];
   if (d.q_col)
-    quant_tile_task(d, local, wave, lane, colmax);
+    quant_tile_task(d, pi, local, wave, lane, colmax);
   else
-    quant_flat_task(d, local, tid);
+    quant_flat_task(d, pi, local, tid);
 }
 
 }  // namespace
@@ -214,7 +222,14 @@ int64_t quant_tasks(const QuantDesc& d) {
 
 hipError_t launch_quantize(const QuantArgs& a, int64_t total_tasks, hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(mxfp8_quantize_kernel<QuantArgs>, dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s) {
+  if (total_tasks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_quantize_kernel<QuantArgsPitched>, dim3((uint32_t)total_tasks), dim3(kThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ __device__ __forceinline__ uint32_t encode4_row(u32x4 v, const F32Scale& sc) {
   return __builtin_bit_cast(uint32_t, a) | (sc.nan ? 0x7F7F7F7Fu : 0u);
 }
 
-__device__ void quant_f32_flat_task(const QuantDesc& d, int64_t task, int tid) {
+__device__ void quant_f32_flat_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid) {
   const float* x = reinterpret_cast<const float*>(d.x);
   const int64_t npieces = d.rows * d.cols / kF32Lane;    // whole blocks: cols % 32 == 0
   const int64_t base = task * (int64_t)(kThreads * kFlatUnroll) + tid;
@@ -100,12 +100,12 @@ __device__ void quant_f32_flat_task(const QuantDesc& d, int64_t task, int tid) {
     const uint32_t q = encode4_row(v[u], sc);
     if (p < npieces) {
       __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(d.q_row) + p);
-      if ((tid & 7) == 0) d.s_row[p >> 3] = (uint8_t)sc.sbyte;
+      if ((tid & 7) == 0) d.s_row[pitched_block(p >> 3, d.cols >> 5, pitch.s_row)] = (uint8_t)sc.sbyte;
     }
   }
 }
 
-__device__ void quant_f32_tile_task(const QuantDesc& d, int64_t task, int wave, int lane,
+__device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int wave, int lane,
                                     u32x4* colmax) {
   const float* x = reinterpret_cast<const float*>(d.x);
   const int64_t cols = d.cols;
@@ -121,7 +121,7 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, int64_t task, int wave, 
   for (int r = 0; r < kRowsPerWave; ++r) v[r] = ok ? load16(xp + r * cols) : kZero4;
 
   if (d.q_row) {
-    const int64_t sb_per_row = cols / kBlock;
+    const int64_t sb_per_row = pitch.s_row;
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       const F32Scale sc = f32_scale_key(oct_max(f32_key4(v[r])));
@@ -152,7 +152,7 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, int64_t task, int wave, 
       sbytes |= sc[k].sbyte << (8 * k);
     }
     if (ok && wave == 0)
-      *reinterpret_cast<uint32_t*>(d.s_col + rb * cols + c) = sbytes;
+      *reinterpret_cast<uint32_t*>(d.s_col + rb * pitch.s_col + c) = sbytes;
     if (any_nan) {
       // a NaN/Inf column keeps only each element's sign bit
       u32x4 keep;
@@ -186,7 +186,8 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, int64_t task, int wave, 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const QuantArgs a) {
+template <class Args>
+__global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const Args a) {
   __shared__ u32x4 colmax[kThreads];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -195,22 +196,29 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const Quan
   // one tensor: its descriptor is read together with the table size (the
   // empty asm keeps those loads ahead of the branch)
   QuantDesc d0 = a.d[0];
+  QuantPitch p0 = {0, 0};
+  if constexpr (Args::kPitched) {
+    p0 = a.pitch(0);
+    asm volatile("" : "+s"(p0.s_row), "+s"(p0.s_col));
+  }
   asm volatile("" : "+s"(d0.x), "+s"(d0.q_row), "+s"(d0.s_row), "+s"(d0.q_col), "+s"(d0.s_col),
                "+s"(d0.rows), "+s"(d0.cols));
+  if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, d0.cols};
   if (a.n == 1) {
     if (d0.q_col)
-      quant_f32_tile_task(d0, task, wave, lane, colmax);
+      quant_f32_tile_task(d0, p0, task, wave, lane, colmax);
     else
-      quant_f32_flat_task(d0, task, tid);
+      quant_f32_flat_task(d0, p0, task, tid);
     return;
   }
   const int i = find_desc(a.task_start, a.n, task);
-  const QuantDesc& d = a.d[i];
+  const QuantDesc d = a.d[i];
+  const QuantPitch pi = Args::kPitched ? a.pitch(i) : QuantPitch{d.cols >> 5, d.cols};
   const int64_t local = task - a.task_start[i];
   if (d.q_col)
-    quant_f32_tile_task(d, local, wave, lane, colmax);
+    quant_f32_tile_task(d, pi, local, wave, lane, colmax);
   else
-    quant_f32_flat_task(d, local, tid);
+    quant_f32_flat_task(d, pi, local, tid);
 }
 
 }  // namespace
@@ -226,7 +234,15 @@ int64_t quant_f32_tasks(const QuantDesc& d) {
 
 hipError_t launch_quantize_f32(const QuantArgs& a, int64_t total_tasks, hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mxfp8_quantize_f32_kernel, dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(mxfp8_quantize_f32_kernel<QuantArgs>, dim3((uint32_t)total_tasks), dim3(kThreads), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_f32(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s) {
+  if (total_tasks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_quantize_f32_kernel<QuantArgsPitched>, dim3((uint32_t)total_tasks), dim3(kThreads),
+                     0, s, a);
   return hipGetLastError();
 }
 

@@ -60,8 +60,8 @@ __device__ __forceinline__ uint32_t norm_pair(uint32_t xw, uint32_t gw, float rs
 
 // Normalize one chunk with its float32 weights w (gamma + offset), store
 // normed, quantize the stored words.
-__device__ __forceinline__ void finish_chunk(const NormDesc& d, int64_t row, int64_t c,
-                                             bool valid, const u32x4& v, const float* w,
+__device__ __forceinline__ void finish_chunk(const NormDesc& d, int64_t s_pitch, int64_t row,
+                                             int64_t c, bool valid, const u32x4& v, const float* w,
                                              float rstd, int t) {
   u32x4 y;
 #pragma unroll
@@ -73,7 +73,7 @@ __device__ __forceinline__ void finish_chunk(const NormDesc& d, int64_t row, int
     const int64_t e = row * (int64_t)d.cols + c * kChunk;
     store16(d.normed + e, y);
     store8(d.q + e, q);
-    if ((t & 3) == 0) d.s[e >> 5] = (uint8_t)rs.sbyte;
+    if ((t & 3) == 0) d.s[row * s_pitch + ((c * kChunk) >> 5)] = (uint8_t)rs.sbyte;
   }
 }
 
@@ -109,7 +109,7 @@ __device__ __forceinline__ float row_sum(float acc, int sub, int lane, float* pa
 // row's L = 64 * WPR lanes each hold NCH chunks (chunk j of lane t is chunk
 // t + L j).  The weights gamma + offset stay in registers across the rows.
 template <int WPR, int NCH>
-__device__ void norm_rows(const NormDesc& d, int64_t first_row, int step, int count,
+__device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row, int step, int count,
                           int sub, int lane, float* part) {
   constexpr int L = kWave * WPR;           // lanes per row
   const int t = sub * kWave + lane;        // this lane's index within the row
@@ -139,7 +139,7 @@ __device__ void norm_rows(const NormDesc& d, int64_t first_row, int step, int co
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int64_t c = t + (int64_t)j * L;
-        finish_chunk(d, row, c, c < nch, v[j], w[j], rstd, t);
+        finish_chunk(d, s_pitch, row, c, c < nch, v[j], w[j], rstd, t);
       }
     }
   } else {
@@ -162,7 +162,7 @@ __device__ void norm_rows(const NormDesc& d, int64_t first_row, int step, int co
         const u32x4 v = valid ? load16_cached(xr + c * kChunk) : u32x4{0, 0, 0, 0};
         float w[8];
         load_weights(d, c, valid, w);
-        finish_chunk(d, row, c, valid, v, w, rstd, t);
+        finish_chunk(d, s_pitch, row, c, valid, v, w, rstd, t);
       }
     }
   }
@@ -171,8 +171,8 @@ __device__ void norm_rows(const NormDesc& d, int64_t first_row, int step, int co
 // WPR waves per row (1 or 4), NCH chunks per lane (0: two passes).  A task
 // is rows_per_task consecutive rows of one tensor: with WPR == 4 the whole
 // workgroup walks them in order; with WPR == 1 wave w takes rows w, w + 4, ...
-template <int WPR, int NCH>
-__global__ __launch_bounds__(kThreads) void mxfp8_rmsnorm_quantize_kernel(const NormArgs a,
+template <class Args, int WPR, int NCH>
+__global__ __launch_bounds__(kThreads) void mxfp8_rmsnorm_quantize_kernel(const Args a,
                                                                          int rows_per_task) {
   __shared__ float part[2 * kWavesPerGroup];
   constexpr int kSlots = kWavesPerGroup / WPR;          // row slots per workgroup
@@ -183,23 +183,30 @@ __global__ __launch_bounds__(kThreads) void mxfp8_rmsnorm_quantize_kernel(const 
   // one tensor: its descriptor is read together with the table size (the
   // empty asm keeps those loads ahead of the branch)
   NormDesc d0 = a.d[0];
+  int64_t p0 = 0;
+  if constexpr (Args::kPitched) {
+    p0 = a.pitch(0);
+    asm volatile("" : "+s"(p0));
+  }
   asm volatile("" : "+s"(d0.x), "+s"(d0.gamma), "+s"(d0.normed), "+s"(d0.q), "+s"(d0.s),
                "+s"(d0.rows), "+s"(d0.cols), "+s"(d0.weight_offset), "+s"(d0.eps));
+  if constexpr (!Args::kPitched) p0 = d0.cols >> 5;
   if (a.n == 1) {
     const int64_t row0 = (int64_t)task * rows_per_task;
     const int64_t left = (int64_t)d0.rows - row0;
     const int in_task = (int)(left < rows_per_task ? left : rows_per_task);
     const int count = (in_task - slot + kSlots - 1) / kSlots;
-    norm_rows<WPR, NCH>(d0, row0 + slot, kSlots, count, wave % WPR, lane, part);
+    norm_rows<WPR, NCH>(d0, p0, row0 + slot, kSlots, count, wave % WPR, lane, part);
     return;
   }
   const int i = find_desc(a.task_start, a.n, task);
-  const NormDesc& d = a.d[i];
+  const NormDesc d = a.d[i];
+  const int64_t pi = Args::kPitched ? a.pitch(i) : (int64_t)(d.cols >> 5);
   const int64_t row0 = (int64_t)(task - a.task_start[i]) * rows_per_task;
   const int64_t left = (int64_t)d.rows - row0;
   const int in_task = (int)(left < rows_per_task ? left : rows_per_task);
   const int count = (in_task - slot + kSlots - 1) / kSlots;   // rows slot, slot + kSlots, ...
-  norm_rows<WPR, NCH>(d, row0 + slot, kSlots, count, wave % WPR, lane, part);
+  norm_rows<WPR, NCH>(d, pi, row0 + slot, kSlots, count, wave % WPR, lane, part);
 }
 
 }  // namespace
@@ -225,22 +232,33 @@ int norm_rows_per_task(int64_t total_rows, int variant) {
   return (int)(g * slots);
 }
 
-hipError_t launch_rmsnorm_quantize(const NormArgs& a, int64_t total_tasks, int variant,
-                                   int rows_per_task, hipStream_t s) {
+template <class Args>
+hipError_t launch_norm(const Args& a, int64_t total_tasks, int variant, int rows_per_task,
+                       hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
   const dim3 block(kThreads);
   const dim3 grid((uint32_t)total_tasks);
   const int r = rows_per_task;
   switch (variant) {
-    case 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<1, 1>), grid, block, 0, s, a, r); break;
-    case 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<1, 2>), grid, block, 0, s, a, r); break;
-    case 11: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 1>), grid, block, 0, s, a, r); break;
-    case 12: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 2>), grid, block, 0, s, a, r); break;
-    case 14: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 4>), grid, block, 0, s, a, r); break;
-    case 18: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 8>), grid, block, 0, s, a, r); break;
-    default: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<4, 0>), grid, block, 0, s, a, r); break;
+    case 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 1>), grid, block, 0, s, a, r); break;
+    case 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 2>), grid, block, 0, s, a, r); break;
+    case 11: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 1>), grid, block, 0, s, a, r); break;
+    case 12: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 2>), grid, block, 0, s, a, r); break;
+    case 14: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 4>), grid, block, 0, s, a, r); break;
+    case 18: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 8>), grid, block, 0, s, a, r); break;
+    default: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 0>), grid, block, 0, s, a, r); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quantize(const NormArgs& a, int64_t total_tasks, int variant,
+                                   int rows_per_task, hipStream_t s) {
+  return launch_norm(a, total_tasks, variant, rows_per_task, s);
+}
+
+hipError_t launch_rmsnorm_quantize(const NormArgsPitched& a, int64_t total_tasks, int variant,
+                                   int rows_per_task, hipStream_t s) {
+  return launch_norm(a, total_tasks, variant, rows_per_task, s);
 }
 
 }  // namespace mx

@@ -41,7 +41,7 @@ def test_every_declared_function_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mxfp8_abi_version() == 1
+    assert L.mxfp8_abi_version() == 2
     for code in range(7):
         assert L.mxfp8_status_string(code)
     assert b"unknown" in L.mxfp8_status_string(99)
@@ -89,13 +89,18 @@ def test_dequantize_argument_checks(L):
 
 def test_gemm_argument_checks(L):
     g = L.mxfp8_gemm
-    assert g(A, B, C, D, 4, 4, 96, A, 0, None) == ERR_SHAPE       # K % 128
-    assert g(A, B, C, D, 4, 4, 0, A, 0, None) == ERR_SHAPE
-    assert g(A, B, C, D, -1, 4, 128, A, 0, None) == ERR_SHAPE
-    assert g(A, None, C, D, 4, 4, 128, A, 0, None) == ERR_NULL
-    assert g(A, B, C, D, 4, 4, 128, MIS, 0, None) == ERR_ALIGN
-    assert g(A, B, C, D, 4, 4, 128, A, 5, None) == ERR_ARG
-    assert g(None, None, None, None, 0, 4, 128, None, 0, None) == OK
+    assert g(A, B, C, D, 4, 4, 96, 0, 0, A, 0, None) == ERR_SHAPE       # K % 128
+    assert g(A, B, C, D, 4, 4, 0, 0, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, -1, 4, 128, 0, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, None, C, D, 4, 4, 128, 0, 0, A, 0, None) == ERR_NULL
+    assert g(A, B, C, D, 4, 4, 128, 0, 0, MIS, 0, None) == ERR_ALIGN
+    assert g(A, B, C, D, 4, 4, 128, 0, 0, A, 5, None) == ERR_ARG
+    assert g(None, None, None, None, 0, 4, 128, 0, 0, None, 0, None) == OK
+    # scale pitches: at least K/32 bytes, a multiple of 4, not negative
+    assert g(A, B, C, D, 4, 4, 256, 4, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 256, 0, 6, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 256, 10, 0, A, 0, None) == ERR_ALIGN
+    assert g(A, B, C, D, 4, 4, 256, -8, 0, A, 0, None) == ERR_SHAPE
 
 
 def test_grouped_checks_every_descriptor_first(L):
@@ -115,11 +120,47 @@ def test_grouped_checks_every_descriptor_first(L):
     assert L.mxfp8_dequantize_grouped(dq, 1, 0, None) == ERR_SHAPE
 
 
+def test_scale_pitch_checks(L):
+    Q = mx._QuantDesc
+    def quant(*d):
+        return L.mxfp8_quantize_grouped((Q * 1)(Q(*d)), 1, None)
+    assert quant(A, 4, 64, B, C, None, None, 1, 0) == ERR_SHAPE           # rowwise pitch < 2
+    assert quant(A, 4, 64, B, C, None, None, -4, 0) == ERR_SHAPE
+    assert quant(A, 32, 64, None, None, B, C, 0, 60) == ERR_SHAPE        # columnwise pitch < 64
+    assert quant(A, 32, 64, None, None, B, C, 0, 68) == ERR_ALIGN        # not a multiple of 8
+    # rowwise only, pitched: the flat block index must fit 32 bits
+    assert quant(A, 1 << 30, 1024, B, C, None, None, 64, 0) == ERR_SHAPE
+    assert L.mxfp8_quantize_f32_grouped((Q * 1)(Q(A, 4, 64, B, C, None, None, 1, 0)), 1, None) == ERR_SHAPE
+    N = mx._NormDesc
+    assert L.mxfp8_rmsnorm_quantize_grouped((N * 1)(N(A, B, 0.0, 1e-6, 4, 64, C, D, A, 1)), 1, None) == ERR_SHAPE
+    Dq = mx._DeqDesc
+    assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 4, 64, 0, C, 1)), 1, 0, None) == ERR_SHAPE
+    assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 72 + 4)), 1, 0, None) == ERR_ALIGN
+    assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 32)), 1, 0, None) == ERR_SHAPE
+
+
+def test_padded_scale_plane_views():
+    """Host-side helper: the plane is the top-left view of a padded buffer and
+    its row stride is what the library receives as the pitch."""
+    import torch
+    buf, view = mx.padded_scale_plane(100, 1056, mx.ROWWISE, 128, 4, device="cpu", fill=0xA5)
+    assert tuple(buf.shape) == (128, 36) and tuple(view.shape) == (100, 33)
+    assert view.stride() == (36, 1) and view.data_ptr() == buf.data_ptr()
+    assert mx._scale_pitch(view, (100, 33), view.device, "s")[1] == 36
+    buf, view = mx.padded_scale_plane(64, 1056, mx.COLUMNWISE, 4, 128, device="cpu")
+    assert tuple(buf.shape) == (4, 1152) and tuple(view.shape) == (2, 1056)
+    assert mx._scale_pitch(view, (2, 1056), view.device, "s")[1] == 1152
+    compact = torch.zeros(2, 1056, dtype=torch.uint8)
+    assert mx._scale_pitch(compact, (2, 1056), compact.device, "s")[1] == 0
+    with pytest.raises(ValueError):
+        mx._scale_pitch(compact.t(), (1056, 2), compact.device, "s")
+
+
 def test_descriptor_layout_matches_header():
     # the ctypes mirrors must have the C structs' sizes (x86-64 ABI)
-    assert ctypes.sizeof(mx._QuantDesc) == 56
-    assert ctypes.sizeof(mx._NormDesc) == 64
-    assert ctypes.sizeof(mx._DeqDesc) == 48
+    assert ctypes.sizeof(mx._QuantDesc) == 72
+    assert ctypes.sizeof(mx._NormDesc) == 72
+    assert ctypes.sizeof(mx._DeqDesc) == 56
 
 
 def test_python_layer_rejects_cpu_tensors():
