@@ -194,9 +194,25 @@ def bench_other_rows(torch, mx, synth, steps):
     res["context_device_copy_32MiB"] = (ms, 2 * (32 << 20), 0)
     del srcs, dsts
 
+    # the headline workload with both scale planes in padded allocations whose
+    # rows are a pitch apart (136 and 4216 bytes instead of 128 and 4096):
+    # same algorithmic bytes, written in place
     x = synth.workload("rowcol_4096x4096", device=dev)["x"]
-    p = mx.quantize(x, True, True)
     r, c = x.shape
+    alg = r * c * 2 + 2 * r * c + r * c // 32 + (r // 32) * c
+    sets = rotation(alg)
+    xs = [x.clone() for _ in range(sets)]
+    outs = []
+    for _ in range(sets):
+        _, sr = mx.padded_scale_plane(r, c, mx.ROWWISE, 128, 136, device=dev)
+        _, sc = mx.padded_scale_plane(r, c, mx.COLUMNWISE, 4, 136, device=dev)
+        outs.append(mx.MXFP8Planes(None, None, sr, sc))
+    outs = [mx.quantize(xs[i], True, True, out=outs[i]) for i in range(sets)]
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets]), steps, 5)
+    res["rowcol_4096x4096_padded_scales"] = (ms, alg, r * c)
+    del xs, outs
+
+    p = mx.quantize(x, True, True)
     for axis, q, s in ((0, p.rowwise_data, p.rowwise_scale), (1, p.columnwise_data, p.columnwise_scale)):
         alg = r * c + s.numel() + r * c * 4
         out = mx.dequantize(q, s, axis)
@@ -370,7 +386,7 @@ def main():
     ms = main_run["ms"]
     gbs = main_run["bytes"] / (ms * 1e-3) / 1e9
     # the row+column launch on the 4096 x 4096 weight: (4096/32) x (4096/512) tiles
-    traffic = measured_traffic("mx::mxfp8_quantize_kernel/1024")
+    traffic = measured_traffic("mx::mxfp8_quantize_kernel<mx::QuantArgs>/1024")
     line = {
         "metric": "bf16->MXFP8 quantize GB/s (frac of MI355X HBM peak) + Gelem/s, 1 GPU",
         "value": round(gbs, 1),
