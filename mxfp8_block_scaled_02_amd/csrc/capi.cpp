@@ -41,12 +41,12 @@ mxfp8_status check_quant(const mxfp8_quant_desc& d) {
       misaligned(d.q_col) || misaligned(d.s_col))
     return MXFP8_ERR_ALIGN;
   if (row && d.s_row_pitch) {
-    if (d.s_row_pitch < d.cols / MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
+    if (d.s_row_pitch < d.cols / MXFP8_BLOCK || !fits(d.rows, d.s_row_pitch)) return MXFP8_ERR_SHAPE;
     if (!col && d.s_row_pitch != d.cols / MXFP8_BLOCK && !flat_blocks_fit(d.rows, d.cols))
       return MXFP8_ERR_SHAPE;
   }
   if (col && d.s_col_pitch) {
-    if (d.s_col_pitch < d.cols) return MXFP8_ERR_SHAPE;
+    if (d.s_col_pitch < d.cols || !fits(d.rows / MXFP8_BLOCK, d.s_col_pitch)) return MXFP8_ERR_SHAPE;
     if (d.s_col_pitch % 8) return MXFP8_ERR_ALIGN;
   }
   return MXFP8_OK;
@@ -63,7 +63,8 @@ mxfp8_status check_norm(const mxfp8_norm_desc& d) {
   if (misaligned(d.x) || misaligned(d.gamma) || misaligned(d.normed) ||
       misaligned(d.q_row) || misaligned(d.s_row))
     return MXFP8_ERR_ALIGN;
-  if (d.s_row_pitch && d.s_row_pitch < d.cols / MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
+  if (d.s_row_pitch && (d.s_row_pitch < d.cols / MXFP8_BLOCK || !fits(d.rows, d.s_row_pitch)))
+    return MXFP8_ERR_SHAPE;
   return MXFP8_OK;
 }
 
@@ -78,6 +79,8 @@ mxfp8_status check_deq(const mxfp8_deq_desc& d) {
     return MXFP8_ERR_SHAPE;
   if (misaligned(d.q) || misaligned(d.s) || misaligned(d.out)) return MXFP8_ERR_ALIGN;
   if (d.s_pitch) {
+    const int64_t srows = d.axis == MXFP8_ROWWISE ? d.rows : d.rows / MXFP8_BLOCK;
+    if (!fits(srows, d.s_pitch)) return MXFP8_ERR_SHAPE;
     if (d.axis == MXFP8_ROWWISE) {
       if (d.s_pitch < d.cols / MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
       if (d.s_pitch != d.cols / MXFP8_BLOCK && !flat_blocks_fit(d.rows, d.cols)) return MXFP8_ERR_SHAPE;

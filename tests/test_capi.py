@@ -128,15 +128,21 @@ def test_scale_pitch_checks(L):
     assert quant(A, 4, 64, B, C, None, None, -4, 0) == ERR_SHAPE
     assert quant(A, 32, 64, None, None, B, C, 0, 60) == ERR_SHAPE        # columnwise pitch < 64
     assert quant(A, 32, 64, None, None, B, C, 0, 68) == ERR_ALIGN        # not a multiple of 8
+    # a pitch whose last scale row would overflow 64-bit offsets
+    assert quant(A, 1 << 20, 64, B, C, None, None, 1 << 60, 0) == ERR_SHAPE
+    assert quant(A, 1 << 20, 64, None, None, B, C, 0, 1 << 60) == ERR_SHAPE
     # rowwise only, pitched: the flat block index must fit 32 bits
     assert quant(A, 1 << 30, 1024, B, C, None, None, 64, 0) == ERR_SHAPE
     assert L.mxfp8_quantize_f32_grouped((Q * 1)(Q(A, 4, 64, B, C, None, None, 1, 0)), 1, None) == ERR_SHAPE
     N = mx._NormDesc
     assert L.mxfp8_rmsnorm_quantize_grouped((N * 1)(N(A, B, 0.0, 1e-6, 4, 64, C, D, A, 1)), 1, None) == ERR_SHAPE
+    assert L.mxfp8_rmsnorm_quantize_grouped((N * 1)(N(A, B, 0.0, 1e-6, 1 << 20, 64, C, D, A, 1 << 60)), 1,
+                                            None) == ERR_SHAPE
     Dq = mx._DeqDesc
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 4, 64, 0, C, 1)), 1, 0, None) == ERR_SHAPE
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 72 + 4)), 1, 0, None) == ERR_ALIGN
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 32)), 1, 0, None) == ERR_SHAPE
+    assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 1 << 20, 64, 0, C, 1 << 60)), 1, 0, None) == ERR_SHAPE
 
 
 def test_padded_scale_plane_views():
