@@ -17,9 +17,10 @@
 // established by a lane-layout probe of the instruction on the GPU; the parity
 // tests check it end to end.
 //
-// Two tilings share that fragment layout:
+// Three tilings share that fragment layout:
 //
-// * tile256 (K % 512 == 0 and at least 256 tiles): a workgroup computes a
+// * tile256 (K % 512 == 0, and at least 256 tiles, or at least 16 with
+//   K >= 4096, where it beats twice as many 128 x 128 tiles): a workgroup computes a
 //   256 x 256 tile with four waves of 128 x 128 (4 x 4 MFMA tiles, 256
 //   accumulators per lane), one workgroup per CU.  K advances in stages of 64
 //   bytes through a ring of four LDS slots that the loads fill directly
@@ -33,8 +34,10 @@
 //   compact block of the output (its L2 holds the shared panels), and XCD
 //   pairs start K at different quarters.
 // * tile128: 128 x 128 tiles (four waves of 64 x 64) staged through registers
-//   into padded LDS rows; it takes problems with too few 256 x 256 tiles to
-//   fill the chip, K not a multiple of 512 or scale pitches not multiples of 16.
+//   into padded LDS rows; it takes the other problems with M > 64 (few tiles
+//   and short K, K not a multiple of 512, scale pitches not multiples of 16).
+// * skinny (M <= 64, decode): 32 output columns per workgroup, K split over
+//   its waves, B streamed once through LDS (see the section below).
 //
 // Rows of A or B past M or N read a valid row (the last one) and their
 // outputs are not stored.  K must be a multiple of 128, and the scale planes'
@@ -99,6 +102,8 @@ constexpr int kGroup = 8;               // stages per scale group (512 k, 16 sca
 constexpr int kScBytes = kBT * 16;      // one operand's scale group in LDS (4 KiB)
 constexpr int kGroupM = 8;              // tile rows per group of the tile order
 constexpr int64_t kGemmFillTiles = 256; // one 256 x 256 tile per CU fills the chip
+constexpr int64_t kGemmFewTiles = 16;   // ... or at least this many with K >= kGemmLongK
+constexpr int64_t kGemmLongK = 4096;
 
 // one LDS array per ring slot (A then B) and per scale buffer (A then B): the
 // compiler tells in-flight LDS loads apart by the array they write, and only
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
       store_tile(p, acc[i][j], m0 + wm * 64 + 32 * i, n0 + wn * 64 + 32 * j + fr, h);
 }
 
-// ---- skinny (M <= 32) ---------------------------------------------------------
+// ---- skinny (M <= 64) ---------------------------------------------------------
 //
 // A few activation rows against a large weight (decode): the product is bound
 // by streaming B once from HBM.  A workgroup owns 32 output columns and its
@@ -481,9 +486,9 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
 // streams its B rows into two private LDS buffers with coalesced direct loads
 // (one 1 KiB load covers 8 rows x 128 bytes), reads the MFMA fragments back
 // (16-byte chunk c of row r stored at chunk c ^ (r % 8) ^ ((r / 8) % 2)), and
-// loads the A fragments (only the M real rows; the padding rows are zero)
-// straight from cache.  The four partial 32 x 32 tiles meet in LDS and are
-// summed in wave order.
+// multiplies them by MT 32-row tiles of A (M <= 32 MT), whose fragments it
+// loads straight from cache (only the M real rows; padding rows are zero).
+// The four partial tiles meet in LDS and are summed in wave order.
 
 constexpr int kSkinnyWaves = 4;
 constexpr int kSkinnyUnits = 1;                       // 128-deep units per chunk
@@ -496,32 +501,47 @@ __shared__ __attribute__((aligned(1024))) uint8_t s_skinny1[kSkinnyWaves * kSkin
 
 __device__ __forceinline__ int skinny_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// loads one chunk issues: per unit four LDS loads of B, four A fragment
-// loads and two scale words
-constexpr int kSkinnyLoads = kSkinnyUnits * 10;
+// loads one chunk issues: per unit four LDS loads of B, a B scale word, and
+// per A tile four fragment loads and a scale word
+template <int MT> constexpr int skinny_loads() { return kSkinnyUnits * (5 + 5 * MT); }
 
 __device__ __forceinline__ void skinny_pin() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
+template <int MT>
 struct SkinnyChunk {
-  u32x4 a[kSkinnyUnits][4];
-  uint32_t sa[kSkinnyUnits], sb[kSkinnyUnits];
+  u32x4 a[kSkinnyUnits][MT][4];
+  uint32_t sa[kSkinnyUnits][MT], sb[kSkinnyUnits];
 };
 
+template <int MT>
 struct Skinny {
   const GemmParams& p;
   int wave, lane, fr, h;
   int64_t n0, K, u1;
-  uint32_t amask;               // ~0 for a real A row, 0 for a padding row
-  const uint8_t* pa;
-  const uint8_t* psa;
+  uint32_t amask[MT];           // ~0 for a real A row, 0 for a padding row
+  const uint8_t* pa[MT];
+  const uint8_t* psa[MT];
   const uint8_t* psb;
+
+  __device__ Skinny(const GemmParams& pp, int w, int l, int64_t nn0, int64_t uu1)
+      : p(pp), wave(w), lane(l), fr(l & 31), h(l >> 5), n0(nn0), K(pp.K), u1(uu1) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int64_t row = 32 * t + fr;
+      const int64_t rr = min(row, p.M - 1);
+      amask[t] = row < p.M ? ~0u : 0u;
+      pa[t] = p.qa + rr * K + 16 * h;
+      psa[t] = p.sa + rr * p.sa_ld;
+    }
+    psb = p.sb + min(n0 + fr, p.N - 1) * p.sb_ld;
+  }
 
   // units u .. u + kSkinnyUnits - 1 (past u1: the last unit again) of B into
   // this wave's part of buf, and the matching A fragments and scales
-  __device__ __forceinline__ void load(uint8_t* buf, int64_t u, SkinnyChunk& c) {
+  __device__ __forceinline__ void load(uint8_t* buf, int64_t u, SkinnyChunk<MT>& c) {
     uint8_t* mine = buf + wave * kSkinnyChunk;
     const int lr = lane >> 3;
 #pragma unroll
@@ -536,14 +556,17 @@ struct Skinny {
                                          (lds_ptr)(mine + 4096 * v + 1024 * g), 16, 0, 0);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        c.a[v][q] = load16_cached(pa + uu * 128 + 32 * q) & amask;
-      c.sa[v] = *reinterpret_cast<const uint32_t*>(psa + uu * 4);
+      for (int t = 0; t < MT; ++t) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c.a[v][t][q] = load16_cached(pa[t] + uu * 128 + 32 * q) & amask[t];
+        c.sa[v][t] = *reinterpret_cast<const uint32_t*>(psa[t] + uu * 4);
+      }
       c.sb[v] = *reinterpret_cast<const uint32_t*>(psb + uu * 4);
     }
   }
 
-  __device__ __forceinline__ void compute(const uint8_t* buf, int64_t u, const SkinnyChunk& c, v16f& acc) {
+  __device__ __forceinline__ void compute(const uint8_t* buf, int64_t u, const SkinnyChunk<MT>& c,
+                                          v16f (&acc)[MT]) {
     const uint8_t* mine = buf + wave * kSkinnyChunk + fr * 128;
     const int f = skinny_swizzle(fr);
 #pragma unroll
@@ -556,50 +579,54 @@ struct Skinny {
         u32x4 b1 = *reinterpret_cast<const u32x4*>(mine + 4096 * v + 16 * ((4 * j + h + 2) ^ f));
         b0 &= keep;
         b1 &= keep;
-        acc = mfma(frag(c.a[v][2 * j], c.a[v][2 * j + 1]), frag(b0, b1), acc, c.sa[v] >> (16 * j + 8 * h),
-                   c.sb[v] >> (16 * j + 8 * h));
+        const v8i fb = frag(b0, b1);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          acc[t] = mfma(frag(c.a[v][t][2 * j], c.a[v][t][2 * j + 1]), fb, acc[t], c.sa[v][t] >> (16 * j + 8 * h),
+                        c.sb[v] >> (16 * j + 8 * h));
       }
     }
   }
 };
 
+template <int MT>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, h = lane >> 5;
   const int64_t n0 = (int64_t)blockIdx.x * 32;
-  const int64_t K = p.K, units = K / 128;
+  const int64_t units = p.K / 128;
   const int64_t u0 = units * wave / kSkinnyWaves, u1 = units * (wave + 1) / kSkinnyWaves;
+  constexpr int kLoads = skinny_loads<MT>();
 
-  Skinny sk{p, wave, lane, fr, h, n0, K, u1, fr < p.M ? ~0u : 0u,
-            p.qa + min((int64_t)fr, p.M - 1) * K + 16 * h,
-            p.sa + min((int64_t)fr, p.M - 1) * p.sa_ld,
-            p.sb + min(n0 + fr, p.N - 1) * p.sb_ld};
+  Skinny<MT> sk(p, wave, lane, n0, u1);
 
   // Chunk pipeline, explicit about waits: each block of loads and each block
   // of MFMAs is pinned in place (compiler memory fence + scheduling barrier),
-  // a chunk is read once only the next chunk's kSkinnyLoads loads remain in
-  // flight, and a buffer is refilled only after its LDS reads have returned.
-  v16f acc = v16f{};
+  // a chunk is read once only the next chunk's kLoads loads remain in flight,
+  // and a buffer is refilled only after its LDS reads have returned.
+  v16f acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = v16f{};
   if (u0 < u1) {
-    SkinnyChunk c0, c1;
+    SkinnyChunk<MT> c0, c1;
     sk.load(s_skinny0, u0, c0);
     for (int64_t u = u0; u < u1; u += 2 * kSkinnyUnits) {
       skinny_pin();
-      wait_loads<kSkinnyLoads>();                  // vmcnt(n) lgkmcnt(0)
+      wait_loads<kLoads>();                        // vmcnt(n) lgkmcnt(0)
       skinny_pin();
       sk.load(s_skinny1, u + kSkinnyUnits, c1);
       skinny_pin();
-      wait_loads<kSkinnyLoads>();                  // chunk u has landed
+      wait_loads<kLoads>();                        // chunk u has landed
       skinny_pin();
       sk.compute(s_skinny0, u, c0, acc);
       skinny_pin();
-      wait_loads<kSkinnyLoads>();                  // reads of chunk u returned
+      wait_loads<kLoads>();                        // reads of chunk u returned
       skinny_pin();
       sk.load(s_skinny0, u + 2 * kSkinnyUnits, c0);
       skinny_pin();
-      wait_loads<kSkinnyLoads>();                  // chunk u + kSkinnyUnits has landed
+      wait_loads<kLoads>();                        // chunk u + kSkinnyUnits has landed
       skinny_pin();
       sk.compute(s_skinny1, u + kSkinnyUnits, c1, acc);
     }
@@ -607,24 +634,28 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
     wait_loads<0>();                               // no load may land after the workgroup ends
   }
 
-  // the partial tiles reuse the first chunk buffer once every wave is done
-  __syncthreads();
+  // the partial tiles reuse the first chunk buffer once every wave is done,
+  // one 32-row A tile at a time
   float (*part)[32][32] = reinterpret_cast<float (*)[32][32]>(s_skinny0);
   static_assert(sizeof(float) * kSkinnyWaves * 32 * 32 <= sizeof(s_skinny0), "partials fit");
 #pragma unroll
-  for (int r = 0; r < 16; ++r) part[wave][8 * (r / 4) + 4 * h + (r % 4)][fr] = acc[r];
-  __syncthreads();
-  for (int e = tid; e < 32 * 32; e += kSkinnyWaves * 64) {
-    const int row = e >> 5, col = e & 31;
-    float sum = part[0][row][col];
+  for (int t = 0; t < MT; ++t) {
+    __syncthreads();
 #pragma unroll
-    for (int w = 1; w < kSkinnyWaves; ++w) sum += part[w][row][col];
-    if (row < p.M && n0 + col < p.N) {
-      const int64_t at = row * p.N + n0 + col;
-      if (p.out_bf16)
-        reinterpret_cast<uint16_t*>(p.out)[at] = (uint16_t)f32_to_bf16(sum);
-      else
-        reinterpret_cast<float*>(p.out)[at] = sum;
+    for (int r = 0; r < 16; ++r) part[wave][8 * (r / 4) + 4 * h + (r % 4)][fr] = acc[t][r];
+    __syncthreads();
+    for (int e = tid; e < 32 * 32; e += kSkinnyWaves * 64) {
+      const int row = 32 * t + (e >> 5), col = e & 31;
+      float sum = part[0][e >> 5][col];
+#pragma unroll
+      for (int w = 1; w < kSkinnyWaves; ++w) sum += part[w][e >> 5][col];
+      if (row < p.M && n0 + col < p.N) {
+        const int64_t at = row * p.N + n0 + col;
+        if (p.out_bf16)
+          reinterpret_cast<uint16_t*>(p.out)[at] = (uint16_t)f32_to_bf16(sum);
+        else
+          reinterpret_cast<float*>(p.out)[at] = sum;
+      }
     }
   }
 }
@@ -641,11 +672,19 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.sa_ld = sa_pitch; p.sb_ld = sb_pitch;
   p.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t big = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
+  // the large tiling when it fills the chip, or when K is long enough that
+  // even a partly filled chip beats twice as many smaller tiles (measured)
+  const bool fills = big >= kGemmFillTiles || (big >= kGemmFewTiles && K >= kGemmLongK);
   if (M <= 32) {
     const int64_t tiles = (N + 31) / 32;
-    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
-  } else if (big >= kGemmFillTiles && K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 &&
-             sb_pitch % 16 == 0) {
+    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
+  } else if (M <= 64) {
+    const int64_t tiles = (N + 31) / 32;
+    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
+  } else if (M <= 128) {
+    const int64_t tiles = (N + 31) / 32;
+    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<4>, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
+  } else if (fills && K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 && sb_pitch % 16 == 0) {
     p.tiles_m = (int32_t)((M + kBT - 1) / kBT);
     p.tiles_n = (int32_t)((N + kBT - 1) / kBT);
     hipLaunchKernelGGL(mxfp8_gemm_tile256_kernel, dim3((uint32_t)big), dim3(kThreads), 0, s, p);
