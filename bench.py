@@ -388,7 +388,7 @@ def main():
     # the row+column launch on the 4096 x 4096 weight: (4096/32) x (4096/512) tiles
     traffic = measured_traffic("mx::mxfp8_quantize_kernel<mx::QuantArgs>/1024")
     line = {
-        "metric": "bf16->MXFP8 quantize GB/s (frac of MI355X HBM peak) + Gelem/s, 1 GPU",
+        "metric": "bf16\u2192MXFP8 quantize GB/s (frac of MI355X HBM peak) + Gelem/s, 1 GPU",
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -398,7 +398,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16->e4m3fn/e8m0",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "rowcol_4096x4096", "shape": [4096, 4096],
                    "planes": ["rowwise", "columnwise"], "alg_bytes_per_step": main_run["bytes"],
