@@ -17,35 +17,37 @@
 // established by a lane-layout probe of the instruction on the GPU; the parity
 // tests check it end to end.
 //
-// Three tilings share that fragment layout:
+// Three kinds of tiling share that fragment layout:
 //
-// * tile256 (K % 512 == 0, and at least 256 tiles, or at least 16 with
-//   K >= 4096, where it beats twice as many 128 x 128 tiles): a workgroup computes a
-//   256 x 256 tile with four waves of 128 x 128 (4 x 4 MFMA tiles, 256
-//   accumulators per lane), one workgroup per CU.  K advances in stages of 64
-//   bytes through a ring of four LDS slots that the loads fill directly
-//   (global_load_lds_dwordx4, no register staging): the loads of stage s + 4
-//   go out while stage s computes, and the fragments of stage s + 1 are read
-//   into a second register set meanwhile, so a stage waits only for data
-//   requested three stages earlier.  Scales travel the same way, 16 bytes (512
-//   k) per row and operand every eight stages.  Waits count the loads still
-//   allowed in flight (s_waitcnt vmcnt(n)) instead of draining them all at
-//   each barrier.  Workgroups are mapped to tiles so that each XCD works on a
-//   compact block of the output (its L2 holds the shared panels), and XCD
-//   pairs start K at different quarters.
+// * ring tiles (K % 512 == 0, scale pitches multiples of 16): a workgroup of
+//   four waves (2 x 2) computes a 256 x 256, 128 x 256 or 128 x 128 tile, one
+//   workgroup per CU.  K advances in stages of 64 bytes through a ring of four
+//   LDS slots that the loads fill directly (global_load_lds_dwordx4, no
+//   register staging): the loads of stage s + 4 go out while stage s
+//   computes, and the fragments of stage s + 1 are read into a second
+//   register set meanwhile, so a stage waits only for data requested three
+//   stages earlier.  Scales travel the same way, 16 bytes (512 k) per row and
+//   operand every eight stages.  Waits count the loads still allowed in
+//   flight (s_waitcnt vmcnt(n)) instead of draining them all at each barrier.
+//   Workgroups are mapped to tiles so that each XCD works on a compact block
+//   of the output (its L2 holds the shared panels), and XCD pairs start K at
+//   different quarters.  The tile size is the one whose rounds of tiles over
+//   the 256 CUs take least time: large tiles move fewer bytes per MFMA, small
+//   ones keep more CUs busy when M or N is small.
 // * tile128: 128 x 128 tiles (four waves of 64 x 64) staged through registers
-//   into padded LDS rows; it takes the other problems with M > 64 (few tiles
-//   and short K, K not a multiple of 512, scale pitches not multiples of 16).
-// * skinny (M <= 64, decode): 32 output columns per workgroup, K split over
-//   its waves, B streamed once through LDS (see the section below).
+//   into padded LDS rows; it takes the problems with M > 128 that the ring
+//   tiles do not (K not a multiple of 512, scale pitches not multiples of 16).
+// * skinny (decode: M <= 64, or M <= 128 where the ring tiles do not apply):
+//   32 output columns per workgroup, K split over its waves, B streamed once
+//   through LDS (see the section below).
 //
 // Rows of A or B past M or N read a valid row (the last one) and their
 // outputs are not stored.  K must be a multiple of 128, and the scale planes'
-// rows are a caller-given pitch apart (a multiple of 4; tile256 also wants a
-// multiple of 16, as compact planes with K % 512 == 0 have).  The order in which
-// the 64-deep MFMA steps accumulate depends on the tiling and, for tile256, on
-// the tile's starting quarter; every order stays within the tolerance that
-// the tests derive for the instruction.
+// rows are a caller-given pitch apart (a multiple of 4; the ring tiles also
+// want a multiple of 16, as compact planes with K % 512 == 0 have).  The
+// order in which the 64-deep MFMA steps accumulate depends on the tiling and,
+// for the ring tiles, on the tile's starting quarter; every order stays
+// within the tolerance that the tests derive for the instruction.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -92,18 +94,16 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v16f& acc,
   }
 }
 
-// ---- tile256 ---------------------------------------------------------------
+// ---- ring tiles (256 x 256, 128 x 256, 128 x 128) -------------------------
 
-constexpr int kBT = 256;                // workgroup tile side
+constexpr int kBT = 256;                // largest workgroup tile side
 constexpr int kBK = 64;                 // K bytes per stage (one MFMA step)
 constexpr int kStages = 4;              // LDS ring depth
-constexpr int kOpBytes = kBT * kBK;     // one operand's stage in LDS (16 KiB)
+constexpr int kOpBytes = kBT * kBK;     // one operand's stage in LDS at most (16 KiB)
 constexpr int kGroup = 8;               // stages per scale group (512 k, 16 scale bytes a row)
 constexpr int kScBytes = kBT * 16;      // one operand's scale group in LDS (4 KiB)
 constexpr int kGroupM = 8;              // tile rows per group of the tile order
-constexpr int64_t kGemmFillTiles = 256; // one 256 x 256 tile per CU fills the chip
-constexpr int64_t kGemmFewTiles = 16;   // ... or at least this many with K >= kGemmLongK
-constexpr int64_t kGemmLongK = 4096;
+constexpr int kCUs = 256;               // one ring tile per CU at a time (LDS-limited)
 
 // one LDS array per ring slot (A then B) and per scale buffer (A then B): the
 // compiler tells in-flight LDS loads apart by the array they write, and only
@@ -120,21 +120,21 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 template <int N> __device__ __forceinline__ uint8_t* slot_a() {
   return N == 0 ? s_slot0 : N == 1 ? s_slot1 : N == 2 ? s_slot2 : s_slot3;
 }
-template <int N> __device__ __forceinline__ uint8_t* slot_b() { return slot_a<N>() + kOpBytes; }
 
 // LDS placement of a 64-byte row: its 16-byte chunk c sits at chunk
 // c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the 16-byte fragment
 // reads of 32 consecutive rows hit distinct banks in 8- and 16-lane phases
 __device__ __forceinline__ int row_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// rows r0 .. r0+255, k0 .. k0+63 of one operand into a ring slot: wave w's
+// rows r0 .. r0+ROWS-1, k0 .. k0+63 of one operand into a ring slot: wave w's
 // load u covers the 16 rows of group g = 4u + w, lane L the physical chunk
 // L % 4 of row 16 g + L / 4 (1 KiB per load, written lane after lane)
+template <int ROWS>
 __device__ __forceinline__ void load_stage(const uint8_t* base, int64_t rows, int64_t r0, int64_t K,
                                            int64_t k0, uint8_t* lds, int wave, int lane) {
   const int lr = lane >> 2;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < ROWS / 64; ++u) {
     const int g = 4 * u + wave;
     const int c = (lane & 3) ^ row_swizzle(16 * g + lr);
     int64_t row = r0 + 16 * g + lr;
@@ -169,42 +169,52 @@ template <int N> __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-struct Tile256 {
+// A ring tile of BM x BN outputs (BM, BN in {128, 256}): four waves in a
+// 2 x 2 layout, each (BM/2) x (BN/2) = MI x NJ MFMA tiles of 32 x 32.  A ring
+// slot holds A's BM rows then B's BN rows of one 64-deep stage.
+template <int BM, int BN>
+struct TileRing {
+  static constexpr int MI = BM / 64, NJ = BN / 64;
+  static constexpr int kLoads = BM / 64 + BN / 64;   // LDS loads of one stage per wave
   const GemmParams& p;
   int wave, lane, fr, h;
   int64_t m0, n0, K, stages;
   int64_t kstart;               // first stage of this tile (K order rotated per tile)
   int swz;                      // row_swizzle of this lane's fragment rows
   int arow, brow;               // LDS byte offset of this lane's row in tile 0
-  v16f acc[4][4];
-  v8i fa[2][4], fb[2][4];       // fragments, double-buffered by stage parity
-  u32x4 sca[2][4], scb[2][4];   // scale groups, double-buffered by group parity
+  v16f acc[MI][NJ];
+  v8i fa[2][MI], fb[2][NJ];     // fragments, double-buffered by stage parity
+  u32x4 sca[2][MI], scb[2][NJ]; // scale groups, double-buffered by group parity
 
-  __device__ Tile256(const GemmParams& pp, int64_t mm0, int64_t nn0, int w, int l, int64_t ks)
+  __device__ TileRing(const GemmParams& pp, int64_t mm0, int64_t nn0, int w, int l, int64_t ks)
       : p(pp), wave(w), lane(l), m0(mm0), n0(nn0), kstart(ks) {
     fr = lane & 31;
     h = lane >> 5;
     K = p.K;
     stages = K / kBK;
     swz = row_swizzle(fr);
-    arow = ((wave >> 1) * 128 + fr) * kBK;
-    brow = ((wave & 1) * 128 + fr) * kBK;
+    arow = ((wave >> 1) * (BM / 2) + fr) * kBK;
+    brow = ((wave & 1) * (BN / 2) + fr) * kBK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+      for (int j = 0; j < NJ; ++j) acc[i][j] = v16f{};
   }
+
+  template <int SLOT> __device__ __forceinline__ uint8_t* sa_slot() { return slot_a<SLOT>(); }
+  template <int SLOT> __device__ __forceinline__ uint8_t* sb_slot() { return slot_a<SLOT>() + BM * kBK; }
 
   // loads of stage t into ring slot t % 4 (stages past the end reload the
   // last one, into a slot nobody reads again); a stage that opens a scale
-  // group also brings that group's scales
+  // group also brings that group's scales (each wave 64 rows of A and of B:
+  // rows past the tile are loaded and never read)
   template <int SLOT, bool GROUP_START>
   __device__ __forceinline__ void issue(int64_t t) {
     int64_t tt = t < stages ? t : stages - 1;
     tt += kstart;
     if (tt >= stages) tt -= stages;
-    load_stage(p.qa, p.M, m0, K, tt * kBK, slot_a<SLOT>(), wave, lane);
-    load_stage(p.qb, p.N, n0, K, tt * kBK, slot_b<SLOT>(), wave, lane);
+    load_stage<BM>(p.qa, p.M, m0, K, tt * kBK, sa_slot<SLOT>(), wave, lane);
+    load_stage<BN>(p.qb, p.N, n0, K, tt * kBK, sb_slot<SLOT>(), wave, lane);
     if (GROUP_START) {
       const int64_t kb0 = (tt / kGroup) * 16;
       const int gpar = (int)((t / kGroup) & 1);
@@ -217,15 +227,18 @@ struct Tile256 {
   // fragment reads of ring slot SLOT into fragment buffer FB
   template <int SLOT, int FB>
   __device__ __forceinline__ void read_frags() {
-    const uint8_t* la = slot_a<SLOT>();
-    const uint8_t* lb = slot_b<SLOT>();
+    const uint8_t* la = sa_slot<SLOT>();
+    const uint8_t* lb = sb_slot<SLOT>();
     const int o0 = 16 * (h ^ swz), o1 = 16 * ((h + 2) ^ swz);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       const uint8_t* pa = la + arow + 32 * kBK * i;
-      const uint8_t* pb = lb + brow + 32 * kBK * i;
       fa[FB][i] = frag(*reinterpret_cast<const u32x4*>(pa + o0), *reinterpret_cast<const u32x4*>(pa + o1));
-      fb[FB][i] = frag(*reinterpret_cast<const u32x4*>(pb + o0), *reinterpret_cast<const u32x4*>(pb + o1));
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint8_t* pb = lb + brow + 32 * kBK * j;
+      fb[FB][j] = frag(*reinterpret_cast<const u32x4*>(pb + o0), *reinterpret_cast<const u32x4*>(pb + o1));
     }
   }
 
@@ -234,20 +247,21 @@ struct Tile256 {
     const uint8_t* la = GP ? s_scale1 : s_scale0;
     const uint8_t* lb = la + kScBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sca[GP][i] = *reinterpret_cast<const u32x4*>(la + 16 * ((wave >> 1) * 128 + 32 * i + fr));
-      scb[GP][i] = *reinterpret_cast<const u32x4*>(lb + 16 * ((wave & 1) * 128 + 32 * i + fr));
-    }
+    for (int i = 0; i < MI; ++i)
+      sca[GP][i] = *reinterpret_cast<const u32x4*>(la + 16 * ((wave >> 1) * (BM / 2) + 32 * i + fr));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      scb[GP][j] = *reinterpret_cast<const u32x4*>(lb + 16 * ((wave & 1) * (BN / 2) + 32 * j + fr));
   }
 
-  // the 16 MFMAs of a stage at position POS of its scale group
+  // the MI x NJ MFMAs of a stage at position POS of its scale group
   template <int FB, int GP, int POS>
   __device__ __forceinline__ void mma() {
     const int sh = 16 * (POS & 1) + 8 * h;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = mfma(fa[FB][i], fb[FB][j], acc[i][j], sca[GP][i][POS >> 1] >> sh,
                          scb[GP][j][POS >> 1] >> sh);
   }
@@ -256,23 +270,25 @@ struct Tile256 {
   // barrier, loads of stage s + 4, reads of stage s + 1, MFMAs of stage s
   template <int POS, int GP>
   __device__ __forceinline__ void step(int64_t s) {
-    // loads issued after those of stage s + 1: stages s + 2 and s + 3, eight
-    // DMA loads each plus two for a stage that opens a scale group
-    constexpr int kAfter = 16 + (((POS + 2) % kGroup) == 0 ? 2 : 0) + (((POS + 3) % kGroup) == 0 ? 2 : 0);
+    // loads issued after those of stage s + 1: stages s + 2 and s + 3, kLoads
+    // LDS loads each plus two for a stage that opens a scale group
+    constexpr int kAfter = 2 * kLoads + (((POS + 2) % kGroup) == 0 ? 2 : 0) + (((POS + 3) % kGroup) == 0 ? 2 : 0);
     ring_barrier<kAfter>();     // stage s+1 is in LDS; every read of stage s has returned
     issue<(POS + 4) % kStages, ((POS + 4) % kGroup) == 0>(s + 4);
     read_frags<(POS + 1) % kStages, (POS + 1) & 1>();
     if (POS == kGroup - 1) read_scales<GP ^ 1>();
     mma<POS & 1, GP, POS>();
     // order: reads first, then the MFMAs with the loads between them
+    constexpr int kReads = 2 * (MI + NJ), kMfma = MI * NJ;
+    constexpr int kPairs = kMfma < kLoads ? kMfma : kLoads;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int n = 0; n < kReads; ++n) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < kPairs; ++n) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if constexpr (kMfma > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPairs, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -293,7 +309,7 @@ struct Tile256 {
     issue<1, false>(1);
     issue<2, false>(2);
     issue<3, false>(3);
-    ring_barrier<24>();         // stage 0 and scale group 0 have landed
+    ring_barrier<3 * kLoads>(); // stage 0 and scale group 0 have landed
     read_frags<0, 0>();
     read_scales<0>();
     // stages come in groups of 8 (K % 512 == 0); two groups per trip so that
@@ -308,7 +324,8 @@ struct Tile256 {
   }
 };
 
-__global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile256_kernel(const GemmParams p) {
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -323,26 +340,27 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile256_kernel(const Gemm
   const uint32_t grp = v / gsize, first_m = grp * kGroupM;
   const uint32_t gm = min((uint32_t)p.tiles_m - first_m, (uint32_t)kGroupM);
   const uint32_t idx = v - grp * gsize;
-  const int64_t m0 = (int64_t)(first_m + idx % gm) * kBT;
-  const int64_t n0 = (int64_t)(idx / gm) * kBT;
+  const int64_t m0 = (int64_t)(first_m + idx % gm) * BM;
+  const int64_t n0 = (int64_t)(idx / gm) * BN;
 
   // XCD pairs start K at different quarters (whole scale groups) so that
   // concurrent tiles on different XCDs do not stream the same K columns,
   // whose rows sit a power-of-two stride apart, at the same time
   const int64_t ngroups = p.K / (kBK * kGroup);
   const int64_t ks = ((int64_t)((xcd / 2) % 4) * ngroups / 4) * kGroup;
-  Tile256 t(p, m0, n0, wave, lane, ks);
+  TileRing<BM, BN> t(p, m0, n0, wave, lane, ks);
   t.run();
 
+  constexpr int MI = BM / 64, NJ = BN / 64;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, fr = lane & 31;
-  const int64_t r0 = m0 + wm * 128, c0 = n0 + wn * 128 + fr;
-  if (m0 + kBT <= p.M && n0 + kBT <= p.N) {
+  const int64_t r0 = m0 + wm * (BM / 2), c0 = n0 + wn * (BN / 2) + fr;
+  if (m0 + BM <= p.M && n0 + BN <= p.N) {
     // a full tile: no bounds to check
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t at = (r0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4)) * p.N + c0 + 32 * j;
@@ -353,9 +371,9 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile256_kernel(const Gemm
         }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) store_tile(p, t.acc[i][j], r0 + 32 * i, c0 + 32 * j, h);
+      for (int j = 0; j < NJ; ++j) store_tile(p, t.acc[i][j], r0 + 32 * i, c0 + 32 * j, h);
   }
 }
 
@@ -478,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
       store_tile(p, acc[i][j], m0 + wm * 64 + 32 * i, n0 + wn * 64 + 32 * j + fr, h);
 }
 
-// ---- skinny (M <= 64) ---------------------------------------------------------
+// ---- skinny (M <= 128) ---------------------------------------------------------
 //
 // A few activation rows against a large weight (decode): the product is bound
 // by streaming B once from HBM.  A workgroup owns 32 output columns and its
@@ -671,23 +689,33 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.M = M; p.N = N; p.K = K;
   p.sa_ld = sa_pitch; p.sb_ld = sb_pitch;
   p.out_bf16 = out_bf16 ? 1 : 0;
-  const int64_t big = ((M + kBT - 1) / kBT) * ((N + kBT - 1) / kBT);
-  // the large tiling when it fills the chip, or when K is long enough that
-  // even a partly filled chip beats twice as many smaller tiles (measured)
-  const bool fills = big >= kGemmFillTiles || (big >= kGemmFewTiles && K >= kGemmLongK);
+  const int64_t skinny = (N + 31) / 32;
   if (M <= 32) {
-    const int64_t tiles = (N + 31) / 32;
-    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);
   } else if (M <= 64) {
-    const int64_t tiles = (N + 31) / 32;
-    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
+    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);
+  } else if (K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 && sb_pitch % 16 == 0) {
+    // the ring tile with the fewest rounds of tiles over the CUs, each round
+    // weighted by the time of one tile at full load (measured on 8192^3:
+    // 128 x 256 takes 0.625 and 128 x 128 0.375 of a 256 x 256 tile)
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128x256 = ((M + 127) / 128) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t c256 = 8 * ((t256 + kCUs - 1) / kCUs);
+    const int64_t c128x256 = 5 * ((t128x256 + kCUs - 1) / kCUs);
+    const int64_t c128 = 3 * ((t128 + kCUs - 1) / kCUs);
+    if (c256 <= c128x256 && c256 <= c128) {
+      p.tiles_m = (int32_t)((M + 255) / 256); p.tiles_n = (int32_t)((N + 255) / 256);
+      hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<256, 256>), dim3((uint32_t)t256), dim3(kThreads), 0, s, p);
+    } else if (c128x256 <= c128) {
+      p.tiles_m = (int32_t)((M + 127) / 128); p.tiles_n = (int32_t)((N + 255) / 256);
+      hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<128, 256>), dim3((uint32_t)t128x256), dim3(kThreads), 0, s, p);
+    } else {
+      p.tiles_m = (int32_t)((M + 127) / 128); p.tiles_n = (int32_t)((N + 127) / 128);
+      hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<128, 128>), dim3((uint32_t)t128), dim3(kThreads), 0, s, p);
+    }
   } else if (M <= 128) {
-    const int64_t tiles = (N + 31) / 32;
-    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<4>, dim3((uint32_t)tiles), dim3(kSkinnyWaves * 64), 0, s, p);
-  } else if (fills && K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 && sb_pitch % 16 == 0) {
-    p.tiles_m = (int32_t)((M + kBT - 1) / kBT);
-    p.tiles_n = (int32_t)((N + kBT - 1) / kBT);
-    hipLaunchKernelGGL(mxfp8_gemm_tile256_kernel, dim3((uint32_t)big), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<4>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);
   } else {
     p.tiles_m = (int32_t)((M + kGT - 1) / kGT);
     p.tiles_n = (int32_t)((N + kGT - 1) / kGT);

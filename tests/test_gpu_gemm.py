@@ -112,14 +112,16 @@ def test_gemm_nan_scale(orc):
 
 
 @pytest.mark.parametrize("mnk", [
-    # enough 256 x 256 tiles to fill the chip and K % 512 == 0: ragged M and N,
-    # one, two, three (odd: the trailing group) and four 512-deep scale groups,
-    # so that the XCD pairs start at different quarters of K
-    (4096 - 37, 4096 + 100, 512), (4096, 4096 + 256, 1024), (4352, 3840, 1536), (4096 + 1, 4096, 2048),
-    # many tiles but K % 512 != 0: the 128 x 128 tiling, odd 128-deep stage counts
-    (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (4352, 3840, 640),
-    # few 256 x 256 tiles but a long K: the large tiling on part of the chip, ragged M
-    (300, 2048, 4096), (65, 4096 + 64, 4096)])
+    # K % 512 == 0: the ring tiles, ragged M and N, one, two, three (odd: the
+    # trailing group) and four 512-deep scale groups, so that the XCD pairs
+    # start at different quarters of K.  256 x 256 tiles:
+    (4352, 3840, 1536), (2000, 7000, 1024),
+    # 128 x 256 tiles (fewer rounds over the CUs than 256 x 256):
+    (4096 - 37, 4096 + 100, 512), (4096, 4096 + 256, 1024), (4096 + 1, 4096, 2048), (1000, 7100, 1024),
+    # 128 x 128 tiles (few tiles in all):
+    (300, 2048, 4096), (129, 1000, 512), (200, 300, 1024),
+    # K % 512 != 0: the register-staged 128 x 128 tiling, odd 128-deep stage counts
+    (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (4352, 3840, 640)])
 def test_gemm_large_tiles_ragged_sampled(orc, mnk):
     """Large problems: sampled outputs, every column of the last row and every
     row of the last column."""
@@ -140,9 +142,12 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
 
 @pytest.mark.parametrize("mnk", [(16, 7168, 7168), (1, 4096, 4096), (32, 1000, 384), (5, 96, 128),
                                  (31, 33, 640), (17, 2048, 1152),
-                                 # two and four 32-row A tiles per workgroup
+                                 # two 32-row A tiles per workgroup
                                  (64, 7168, 7168), (48, 2048, 1024), (33, 100, 384), (64, 4096, 128),
-                                 (128, 7168, 7168), (97, 1000, 640), (65, 2048, 256)])
+                                 # four (64 < M <= 128 with K % 512 != 0)
+                                 (128, 7168, 7040), (97, 1000, 640), (65, 2048, 256),
+                                 # 64 < M <= 128 with K % 512 == 0: one row of 128 x 128 ring tiles
+                                 (128, 7168, 7168), (97, 3000, 2048), (65, 200, 512)])
 def test_gemm_skinny_decode(orc, mnk):
     """A few activation rows (decode): the K-split skinny path, including K
     with fewer 128-deep units than waves and N not a multiple of 32."""
