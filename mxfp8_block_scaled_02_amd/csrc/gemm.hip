@@ -20,8 +20,8 @@
 // Three kinds of tiling share that fragment layout:
 //
 // * ring tiles (K % 512 == 0, scale pitches multiples of 16): a workgroup of
-//   four waves (2 x 2) computes a 256 x 256, 128 x 256 or 128 x 128 tile, one
-//   workgroup per CU.  K advances in stages of 64 bytes through a ring of four
+//   four waves (2 x 2) computes a 256 x 256, 128 x 256, 128 x 128 or 64 x 128
+//   tile, one workgroup per CU.  K advances in stages of 64 bytes through a ring of four
 //   LDS slots that the loads fill directly (global_load_lds_dwordx4, no
 //   register staging): the loads of stage s + 4 go out while stage s
 //   computes, and the fragments of stage s + 1 are read into a second
@@ -94,7 +94,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v16f& acc,
   }
 }
 
-// ---- ring tiles (256 x 256, 128 x 256, 128 x 128) -------------------------
+// ---- ring tiles (256 x 256, 128 x 256, 128 x 128, 64 x 128) ---------------
 
 constexpr int kBT = 256;                // largest workgroup tile side
 constexpr int kBK = 64;                 // K bytes per stage (one MFMA step)
@@ -169,9 +169,10 @@ template <int N> __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// A ring tile of BM x BN outputs (BM, BN in {128, 256}): four waves in a
-// 2 x 2 layout, each (BM/2) x (BN/2) = MI x NJ MFMA tiles of 32 x 32.  A ring
-// slot holds A's BM rows then B's BN rows of one 64-deep stage.
+// A ring tile of BM x BN outputs (BM in {64, 128, 256}, BN in {128, 256}):
+// four waves in a 2 x 2 layout, each (BM/2) x (BN/2) = MI x NJ MFMA tiles of
+// 32 x 32.  A ring slot holds A's BM rows then B's BN rows of one 64-deep
+// stage.
 template <int BM, int BN>
 struct TileRing {
   static constexpr int MI = BM / 64, NJ = BN / 64;
@@ -695,24 +696,26 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   } else if (M <= 64) {
     hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);
   } else if (K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 && sb_pitch % 16 == 0) {
-    // the ring tile with the fewest rounds of tiles over the CUs, each round
-    // weighted by the time of one tile at full load (measured on 8192^3:
-    // 128 x 256 takes 0.625 and 128 x 128 0.375 of a 256 x 256 tile)
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    const int64_t t128x256 = ((M + 127) / 128) * ((N + 255) / 256);
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t c256 = 8 * ((t256 + kCUs - 1) / kCUs);
-    const int64_t c128x256 = 5 * ((t128x256 + kCUs - 1) / kCUs);
-    const int64_t c128 = 3 * ((t128 + kCUs - 1) / kCUs);
-    if (c256 <= c128x256 && c256 <= c128) {
-      p.tiles_m = (int32_t)((M + 255) / 256); p.tiles_n = (int32_t)((N + 255) / 256);
-      hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<256, 256>), dim3((uint32_t)t256), dim3(kThreads), 0, s, p);
-    } else if (c128x256 <= c128) {
-      p.tiles_m = (int32_t)((M + 127) / 128); p.tiles_n = (int32_t)((N + 255) / 256);
-      hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<128, 256>), dim3((uint32_t)t128x256), dim3(kThreads), 0, s, p);
-    } else {
-      p.tiles_m = (int32_t)((M + 127) / 128); p.tiles_n = (int32_t)((N + 127) / 128);
-      hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<128, 128>), dim3((uint32_t)t128), dim3(kThreads), 0, s, p);
+    // the ring tile with the least rounds of tiles over the CUs times the
+    // time of one tile at full load, in eighths of a 256 x 256 tile's
+    // (measured on 8192^3: 128 x 256 takes 5, 128 x 128 3 and 64 x 128 2)
+    struct Choice { int bm, bn; int64_t weight; };
+    constexpr Choice kChoices[4] = {{256, 256, 8}, {128, 256, 5}, {128, 128, 3}, {64, 128, 2}};
+    int best = 0;
+    int64_t best_cost = 0;
+    for (int c = 0; c < 4; ++c) {
+      const int64_t tiles = ((M + kChoices[c].bm - 1) / kChoices[c].bm) * ((N + kChoices[c].bn - 1) / kChoices[c].bn);
+      const int64_t cost = kChoices[c].weight * ((tiles + kCUs - 1) / kCUs);
+      if (c == 0 || cost < best_cost) { best = c; best_cost = cost; }
+    }
+    p.tiles_m = (int32_t)((M + kChoices[best].bm - 1) / kChoices[best].bm);
+    p.tiles_n = (int32_t)((N + kChoices[best].bn - 1) / kChoices[best].bn);
+    const dim3 grid((uint32_t)((int64_t)p.tiles_m * p.tiles_n));
+    switch (best) {
+      case 0: hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<256, 256>), grid, dim3(kThreads), 0, s, p); break;
+      case 1: hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<128, 256>), grid, dim3(kThreads), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<128, 128>), grid, dim3(kThreads), 0, s, p); break;
+      default: hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<64, 128>), grid, dim3(kThreads), 0, s, p); break;
     }
   } else if (M <= 128) {
     hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<4>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);

@@ -118,7 +118,9 @@ def test_gemm_nan_scale(orc):
     (4352, 3840, 1536), (2000, 7000, 1024),
     # 128 x 256 tiles (fewer rounds over the CUs than 256 x 256):
     (4096 - 37, 4096 + 100, 512), (4096, 4096 + 256, 1024), (4096 + 1, 4096, 2048), (1000, 7100, 1024),
-    # 128 x 128 tiles (few tiles in all):
+    # 128 x 128 tiles:
+    (500, 7000, 1024), (400, 6000, 512),
+    # 64 x 128 tiles (few tiles in all):
     (300, 2048, 4096), (129, 1000, 512), (200, 300, 1024),
     # K % 512 != 0: the register-staged 128 x 128 tiling, odd 128-deep stage counts
     (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (4352, 3840, 640)])
@@ -146,7 +148,7 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
                                  (64, 7168, 7168), (48, 2048, 1024), (33, 100, 384), (64, 4096, 128),
                                  # four (64 < M <= 128 with K % 512 != 0)
                                  (128, 7168, 7040), (97, 1000, 640), (65, 2048, 256),
-                                 # 64 < M <= 128 with K % 512 == 0: one row of 128 x 128 ring tiles
+                                 # 64 < M <= 128 with K % 512 == 0: two rows of 64 x 128 ring tiles
                                  (128, 7168, 7168), (97, 3000, 2048), (65, 200, 512)])
 def test_gemm_skinny_decode(orc, mnk):
     """A few activation rows (decode): the K-split skinny path, including K
