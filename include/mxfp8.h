@@ -71,7 +71,11 @@ typedef enum {
     MXFP8_OK = 0,
     MXFP8_ERR_NULL = 1,      /* a required pointer is NULL, or a plane's data /
                                 scale pointers are not both set or both NULL */
-    MXFP8_ERR_SHAPE = 2,     /* negative size, partial block, or size limit */
+    MXFP8_ERR_SHAPE = 2,     /* negative size, partial block, or size limit
+                                (a byte count above 2^61; a tensor needing
+                                more than the 2^30 tasks of one launch, which
+                                takes 2^40 elements or more; a product of
+                                more than 2^28 tiles of 64 x 32 outputs) */
     MXFP8_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
     MXFP8_ERR_NO_OUTPUT = 4, /* neither plane requested */
     MXFP8_ERR_ARG = 5,       /* bad enum value, n < 0, or a non-finite eps */

@@ -15,8 +15,10 @@ namespace {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-// Largest element count and task count one launch may carry.
+// Largest task count one launch (and so one tensor) may carry.
 constexpr int64_t kMaxTasksPerLaunch = (int64_t)1 << 30;
+// Largest count of 64 x 32 output tiles of a matrix product.
+constexpr int64_t kMaxGemmTiles = (int64_t)1 << 28;
 
 bool fits(int64_t rows, int64_t cols) {
   return rows >= 0 && cols >= 0 && (cols == 0 || rows <= INT64_MAX / 4 / cols);
@@ -137,11 +139,15 @@ mxfp8_status run_groups(const std::vector<It>& items, TaskFn tasks, LaunchFn lau
 }
 
 // Runs the items through the compact argument block, or through the pitched
-// one when any plane has a pitch of its own.
+// one when any plane has a pitch of its own; a tensor with more tasks than
+// one launch carries fails the call first.
 template <class Compact, class Pitched, class It, class TaskFn, class LaunchFn>
 mxfp8_status run_items(const std::vector<It>& items, TaskFn tasks, LaunchFn launch) {
   bool pitched = false;
-  for (const It& it : items) pitched |= it.pitched;
+  for (const It& it : items) {
+    if (tasks(it.d) > kMaxTasksPerLaunch) return MXFP8_ERR_SHAPE;  // before any launch
+    pitched |= it.pitched;
+  }
   if (pitched) {
     Pitched a;
     return run_groups(items, tasks, [&](const Pitched& args, int64_t t) { return launch(args, t); }, a);
@@ -348,7 +354,9 @@ mxfp8_status mxfp8_gemm(const void* qa, const void* sa, const void* qb, const vo
   if (!sb_pitch) sb_pitch = kb;
   if (sa_pitch < kb || sb_pitch < kb || !fits(M, sa_pitch) || !fits(N, sb_pitch)) return MXFP8_ERR_SHAPE;
   if (sa_pitch % 4 || sb_pitch % 4) return MXFP8_ERR_ALIGN;
-  if (((M + 127) / 128) * ((N + 127) / 128) > INT32_MAX) return MXFP8_ERR_SHAPE;
+  // 64 x 32 outputs bound the smallest workgroup tile of every route, so this
+  // keeps grid sizes and tile indices within 32 bits
+  if (((M + 63) / 64) * ((N + 31) / 32) > kMaxGemmTiles) return MXFP8_ERR_SHAPE;
   (void)hipGetLastError();
   return hip_status(mx::launch_gemm(static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa),
                                     static_cast<const uint8_t*>(qb), static_cast<const uint8_t*>(sb),

@@ -60,6 +60,8 @@ def test_quantize_argument_checks(L):
     assert q(MIS, 4, 32, B, C, None, None, None) == ERR_ALIGN
     assert q(A, 4, 32, B, C + 1, None, None, None) == ERR_ALIGN
     assert q(A, 1 << 40, 1 << 40, B, C, None, None, None) == ERR_SHAPE   # overflow
+    # more tasks than one launch carries (2^45 elements, about 2^31 tasks)
+    assert q(A, 1 << 23, 1 << 22, B, C, None, None, None) == ERR_SHAPE
     # empty tensors are a no-op, whatever the pointers
     assert q(None, 0, 32, None, None, None, None, None) == OK
     assert q(None, 5, 0, None, None, None, None, None) == OK
@@ -101,6 +103,9 @@ def test_gemm_argument_checks(L):
     assert g(A, B, C, D, 4, 4, 256, 0, 6, A, 0, None) == ERR_SHAPE
     assert g(A, B, C, D, 4, 4, 256, 10, 0, A, 0, None) == ERR_ALIGN
     assert g(A, B, C, D, 4, 4, 256, -8, 0, A, 0, None) == ERR_SHAPE
+    # more output tiles than 32-bit grid and tile indices hold
+    assert g(A, B, C, D, 1, 1 << 40, 128, 0, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 1 << 21, 1 << 21, 128, 0, 0, A, 0, None) == ERR_SHAPE
 
 
 def test_grouped_checks_every_descriptor_first(L):
