@@ -126,13 +126,27 @@ def as_fp8(planes: MXFP8Planes) -> MXFP8Planes:
                        v(planes.columnwise_scale, torch.float8_e8m0fnu))
 
 
-def _as2d(x: torch.Tensor, name: str, dtype=torch.bfloat16) -> torch.Tensor:
+# float8 views of the byte planes (as_fp8) are accepted where bytes are
+_BYTE_ALIASES = {torch.float8_e4m3fn: torch.uint8, torch.float8_e8m0fnu: torch.uint8}
+
+
+def _bytes(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype in _BYTE_ALIASES else t
+
+
+def _as2d(x: torch.Tensor, name: str, dtype=torch.bfloat16, device=None) -> torch.Tensor:
+    if dtype == torch.uint8:
+        x = _bytes(x)
     if x.dtype != dtype:
         raise ValueError("%s must be %s, got %s" % (name, dtype, x.dtype))
     if not x.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and x.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, x.device))
     if not x.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if x.dim() == 0:
+        raise ValueError("%s must have at least one dimension" % name)
     if x.dim() == 1:
         return x.view(1, -1)
     return x.reshape(-1, x.shape[-1]) if x.dim() > 2 else x
@@ -149,6 +163,8 @@ def _stream(device) -> int:
 def _out(t, shape, dtype, device, name):
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device)
+    if dtype == torch.uint8:
+        t = _bytes(t)
     if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
         raise ValueError("%s must be a contiguous %s tensor of shape %s on %s" % (name, dtype, tuple(shape), device))
     return t
@@ -162,9 +178,11 @@ def _scale_pitch(t, shape, device, name, allocate=True):
         if not allocate:
             raise ValueError("%s is required" % name)
         return torch.empty(shape, dtype=torch.uint8, device=device), 0
+    t = _bytes(t)
     if t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) or t.device != device:
         raise ValueError("%s must be a uint8 tensor of shape %s on %s" % (name, tuple(shape), device))
-    if t.dim() != 2 or (shape[0] > 1 and shape[1] > 0 and (t.stride(1) != 1 or t.stride(0) < shape[1])):
+    if t.dim() != 2 or (shape[1] > 1 and t.stride(1) != 1) or (
+            shape[0] > 1 and shape[1] > 0 and t.stride(0) < shape[1]):
         raise ValueError("%s must have unit column stride and a row stride >= its width" % name)
     pitch = t.stride(0) if shape[0] > 1 else shape[1]
     return t, (0 if pitch == shape[1] else pitch)
@@ -244,7 +262,7 @@ def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwis
 def _norm_desc(x, gamma, weight_offset, eps, out):
     x2 = _as2d(x, "x")
     rows, cols = x2.shape
-    g = _as2d(gamma, "gamma")
+    g = _as2d(gamma, "gamma", device=x.device)
     if g.numel() != cols:
         raise ValueError("gamma must have %d elements" % cols)
     dev = x.device
@@ -347,7 +365,8 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
     B = (qb [N, K], sb [N, K/32]) (quantization.utils page, mm_mxfp8: a
     quantized activation times a pre-quantized weight [out, in])."""
     code = _out_code(dtype)
-    qa2, qb2 = _as2d(qa, "qa", torch.uint8), _as2d(qb, "qb", torch.uint8)
+    qa2 = _as2d(qa, "qa", torch.uint8)
+    qb2 = _as2d(qb, "qb", torch.uint8, device=qa.device)
     M, K = qa2.shape
     N = qb2.shape[0]
     if qb2.shape[1] != K:

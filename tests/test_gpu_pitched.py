@@ -161,3 +161,41 @@ def test_gemm_padded_scales_other_tiling(orc):
                          host(pb.rowwise_scale), ms, ns)
     err = np.abs(host(got)[ms, ns].astype(np.float64) - C)
     assert (err <= 2.0 ** -10 * mag).all()
+
+
+def test_scale_view_strides_checked():
+    """A one-row scale view whose columns are not adjacent bytes is refused
+    (the library writes each scale row as consecutive bytes)."""
+    say("scale view strides")
+    buf = torch.zeros((32, 64), dtype=torch.uint8, device=DEV)
+    bad = buf[:1, ::2]                                    # [1, 32], column stride 2
+    assert bad.shape == (1, 32) and bad.stride(1) == 2
+    with pytest.raises(ValueError, match="unit column stride"):
+        # columnwise scales of a [32, 32] tensor are [1, 32]
+        mx.quantize(bf16_input(32, 32, seed=21), False, True, out=mx.MXFP8Planes(None, None, None, bad))
+    with pytest.raises(ValueError, match="unit column stride"):
+        # rowwise scales of a [1, 1024] tensor are [1, 32]
+        mx.quantize(bf16_input(1, 1024, seed=21), True, False, out=mx.MXFP8Planes(None, None, bad, None))
+    assert bool((buf == 0).all())
+
+
+def test_float8_views_accepted():
+    """Planes viewed with the float8 dtypes (as_fp8) are accepted wherever
+    byte planes are, and give the same results."""
+    say("float8 views")
+    x = bf16_input(256, 512, seed=22)
+    w = (bf16_input(384, 512, seed=23) * 0.05).to(torch.bfloat16)
+    pa, pb = mx.quantize(x, True, True), mx.quantize(w, True, False)
+    fa, fb = mx.as_fp8(pa), mx.as_fp8(pb)
+    ref = mx.gemm(pa.rowwise_data, pa.rowwise_scale, pb.rowwise_data, pb.rowwise_scale)
+    got = mx.gemm(fa.rowwise_data, fa.rowwise_scale, fb.rowwise_data, fb.rowwise_scale)
+    d_ref = mx.dequantize(pa.columnwise_data, pa.columnwise_scale, mx.COLUMNWISE)
+    d_got = mx.dequantize(fa.columnwise_data, fa.columnwise_scale, mx.COLUMNWISE)
+    outs = mx.as_fp8(mx.MXFP8Planes(*(torch.empty_like(t) for t in pa)))
+    again = mx.quantize(x, True, True, out=outs)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(d_got.view(torch.int32), d_ref.view(torch.int32))
+    for a, b in zip(again, pa):
+        assert torch.equal(a, b)
+    assert torch.equal(outs.rowwise_data.view(torch.uint8), pa.rowwise_data)
