@@ -345,6 +345,7 @@ def main():
     if len(sys.argv) > 3 and sys.argv[1] == "--traffic-summary":
         res = traffic_summary(sys.argv[2], sys.argv[3])
         res["source_hash"] = kernel_source_hash()
+        res["hashed_sources"] = list(QUANTIZE_SOURCES)
         print(json.dumps(res, indent=1))
         if "--write" in sys.argv:
             with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
