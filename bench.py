@@ -387,7 +387,7 @@ def main():
     ms = main_run["ms"]
     gbs = main_run["bytes"] / (ms * 1e-3) / 1e9
     # the row+column launch on the 4096 x 4096 weight: (4096/32) x (4096/512) tiles
-    traffic = measured_traffic("mx::mxfp8_quantize_kernel<mx::QuantArgs>/1024")
+    traffic = measured_traffic("mx::mxfp8_quantize_kernel<mx::QuantArgs, true>/1024")
     line = {
         "metric": "bf16\u2192MXFP8 quantize GB/s (frac of MI355X HBM peak) + Gelem/s, 1 GPU",
         "value": round(gbs, 1),

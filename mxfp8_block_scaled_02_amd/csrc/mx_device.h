@@ -289,6 +289,21 @@ __device__ __forceinline__ void store8(void* p, u32x2 v) {
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
+// One scale byte, streamed (nt) or written back through the L2.  A tile owns
+// only a few bytes of each rowwise scale line, so those lines are completed
+// by several workgroups.  Written back, the pieces can merge before they reach
+// HBM, but dirty lines still in the L2 when the kernel ends are written back
+// at its end.  The quantize kernel streams them only when its whole grid is
+// resident at once, when no later work would hide that write-back.
+// (A template parameter: a run-time choice between the two stores is merged
+// by the compiler into one plain store.)
+template <bool NT>
+__device__ __forceinline__ void store_scale(void* p, uint32_t v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store((uint8_t)v, reinterpret_cast<uint8_t*>(p));
+  else
+    *reinterpret_cast<uint8_t*>(p) = (uint8_t)v;
+}
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

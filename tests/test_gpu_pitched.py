@@ -41,7 +41,10 @@ def bf16_input(rows, cols, seed):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("shape,columnwise", [((100, 1056), False), ((96, 1056), True),
-                                              ((1, 64), False), ((2048, 512), True)])
+                                              ((1, 64), False), ((2048, 512), True),
+                                              # more tiles than are resident at once (scale
+                                              # bytes written back rather than streamed)
+                                              ((4096, 8192), True)])
 def test_quantize_into_padded_scales(shape, columnwise, dtype):
     rows, cols = shape
     say("quantize padded", shape, "col" if columnwise else "row", dtype)
