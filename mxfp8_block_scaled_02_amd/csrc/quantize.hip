@@ -14,7 +14,8 @@
 // amax takes two DPP steps.
 //   flat  (rowwise only): the tensor is a flat array whose 32-element blocks
 //         are contiguous and whose scale array is in block order; a workgroup
-//         walks 256 x kFlatUnroll consecutive 8-element pieces.
+//         walks 256 x U consecutive 8-element pieces (U = flat_unroll: 1 for
+//         small tensors, kFlatUnroll otherwise).
 //   tile  (any columnwise request): a workgroup owns a 32 x 512 tile, each
 //         wave 8 of its rows, each lane 8 rows x 8 columns in registers.  A
 //         columnwise block is one lane column across the 4 waves: each wave
@@ -48,20 +49,20 @@ __device__ __forceinline__ RowScale lane_row_scale(const u32x4* v) {
     return row_scale_key(pair_max(chunk16_key(v[0], v[1])));
 }
 
-template <bool NT>
-__device__ void quant_flat_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid) {
-  const int64_t npieces = d.rows * d.cols / kLaneCols;   // whole blocks: cols % 32 == 0
-  const int64_t base = task * (int64_t)(kThreads * kFlatUnroll) + tid;
-  u32x4 v[kFlatUnroll][kCh];
+template <bool NT, int U>
+__device__ void quant_flat_pieces(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid,
+                                  int64_t npieces) {
+  const int64_t base = task * (int64_t)(kThreads * U) + tid;
+  u32x4 v[U][kCh];
 #pragma unroll
-  for (int u = 0; u < kFlatUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int64_t p = base + u * kThreads;
 #pragma unroll
     for (int h = 0; h < kCh; ++h)
       v[u][h] = p < npieces ? load16(d.x + p * kLaneCols + h * kChunk) : kZero4;
   }
 #pragma unroll
-  for (int u = 0; u < kFlatUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const int64_t p = base + u * kThreads;
     const RowScale rs = lane_row_scale(v[u]);
     if (p < npieces) {
@@ -72,6 +73,15 @@ __device__ void quant_flat_task(const QuantDesc& d, const QuantPitch& pitch, int
         store_scale<NT>(d.s_row + pitched_block(p * kLaneCols / kBlock, d.cols >> 5, pitch.s_row), rs.sbyte);
     }
   }
+}
+
+template <bool NT>
+__device__ void quant_flat_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid) {
+  const int64_t npieces = d.rows * d.cols / kLaneCols;   // whole blocks: cols % 32 == 0
+  if (flat_unroll(npieces) == 1)
+    quant_flat_pieces<NT, 1>(d, pitch, task, tid, npieces);
+  else
+    quant_flat_pieces<NT, kFlatUnroll>(d, pitch, task, tid, npieces);
 }
 
 template <bool NT>
@@ -219,7 +229,7 @@ int64_t quant_tasks(const QuantDesc& d) {
   if (d.q_col)
     return (d.rows / kTileRows) * ((d.cols + kTileCols - 1) / kTileCols);
   const int64_t pieces = d.rows * d.cols / kLaneCols;
-  const int64_t per = (int64_t)kThreads * kFlatUnroll;
+  const int64_t per = (int64_t)kThreads * flat_unroll(pieces);
   return (pieces + per - 1) / per;
 }
 

@@ -89,6 +89,14 @@ def test_rowwise_only_ragged(orc, shape):
         check_quantize(orc, bits, True, False, "rowonly%d" % i)
 
 
+@pytest.mark.parametrize("shape", [(4095, 2048), (4096, 2048), (4097, 2080)])
+def test_rowwise_only_around_the_unroll_switch(orc, shape):
+    # just below 2^20 8-element pieces a lane takes one piece per task, from
+    # there on four (the last of these shapes also ends in a partial task)
+    for i, bits in enumerate(P.random_tensors(seed=11, rows=shape[0], cols=shape[1])[:2]):
+        check_quantize(orc, bits, True, False, "rowonly-switch%d" % i)
+
+
 @pytest.mark.parametrize("shape", [(32, 8), (64, 40), (32, 520), (96, 1000)])
 def test_columnwise_only_cols_multiple_of_8(orc, shape):
     for i, bits in enumerate(P.random_tensors(seed=9, rows=shape[0], cols=shape[1])):
