@@ -303,7 +303,7 @@ mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc* descs, int32_
       total_rows += descs[i].rows;
     }
   }
-  const int variant = mx::norm_variant(max_cols);
+  const int variant = mx::norm_variant(max_cols, total_rows);
   const int rpt = mx::norm_rows_per_task(total_rows, variant);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return run_items<mx::NormArgs, mx::NormArgsPitched>(

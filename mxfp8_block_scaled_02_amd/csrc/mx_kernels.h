@@ -108,10 +108,12 @@ struct NormArgsPitched {
   int64_t p[kMax];   // bytes between rows of the scale plane
   __device__ int64_t pitch(int i) const { return p[i]; }
 };
-// Kernel shape for the longest row of a launch: waves per row and chunks
-// per lane (see rmsnorm_quantize.hip).  A task is rows_per_task consecutive
-// rows of one tensor, chosen from the launch's total row count.
-int norm_variant(int64_t cols);
+// Kernel shape from the longest row of a launch and its total row count:
+// waves per row and chunks per lane (see rmsnorm_quantize.hip).  A task is
+// rows_per_task consecutive rows of one tensor, also chosen from the total
+// row count.  Launches of at most kWideNormRows rows use 16 waves per row.
+constexpr int64_t kWideNormRows = 256;
+int norm_variant(int64_t cols, int64_t total_rows);
 int norm_rows_per_task(int64_t total_rows, int variant);
 hipError_t launch_rmsnorm_quantize(const NormArgs& a, int64_t total_tasks, int variant,
                                    int rows_per_task, hipStream_t s);

@@ -10,7 +10,9 @@
 // rides the epilogue on the same bf16 that lands in outputs_normed).
 //
 // A row belongs to one wave (rows up to 1024 elements, four rows per
-// workgroup) or to all four waves of a workgroup (longer rows).  Its L lanes
+// workgroup) or to all four waves of a workgroup (longer rows); a launch of
+// few rows (decode) gives each row a workgroup of 16 waves instead, so each
+// lane's serial work is a quarter as long.  Its L lanes
 // hold NCH 16-byte chunks each in registers: chunk j of lane t is chunk
 // t + L j of the row, so every load instruction reads L * 16 contiguous
 // bytes.  The sum of squares is a per-lane float32 chain, a fixed butterfly
@@ -168,14 +170,15 @@ __device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row,
   }
 }
 
-// WPR waves per row (1 or 4), NCH chunks per lane (0: two passes).  A task
-// is rows_per_task consecutive rows of one tensor: with WPR == 4 the whole
-// workgroup walks them in order; with WPR == 1 wave w takes rows w, w + 4, ...
-template <class Args, int WPR, int NCH>
-__global__ __launch_bounds__(kThreads) void mxfp8_rmsnorm_quantize_kernel(const Args a,
-                                                                         int rows_per_task) {
-  __shared__ float part[2 * kWavesPerGroup];
-  constexpr int kSlots = kWavesPerGroup / WPR;          // row slots per workgroup
+// WAVES waves per workgroup, WPR waves per row (1, 4 or 16), NCH chunks per
+// lane (0: two passes).  A task is rows_per_task consecutive rows of one
+// tensor: with WPR == WAVES the whole workgroup walks them in order; with
+// WPR == 1 wave w takes rows w, w + 4, ...
+template <class Args, int WPR, int NCH, int WAVES = kWavesPerGroup>
+__global__ __launch_bounds__(64 * WAVES) void mxfp8_rmsnorm_quantize_kernel(const Args a,
+                                                                           int rows_per_task) {
+  __shared__ float part[2 * WAVES];
+  constexpr int kSlots = WAVES / WPR;                   // row slots per workgroup
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int32_t task = (int32_t)blockIdx.x;
@@ -211,8 +214,12 @@ __global__ __launch_bounds__(kThreads) void mxfp8_rmsnorm_quantize_kernel(const 
 
 }  // namespace
 
-int norm_variant(int64_t cols) {
+int norm_variant(int64_t cols, int64_t total_rows) {
   const int64_t chunks = cols / kChunk;
+  // few rows of at least 4 waves' width: 16 waves per row (measured on the
+  // 16 x 7168 decode workload: 4.0 us with 4 waves per row)
+  if (total_rows <= kWideNormRows && chunks > 2 * kWave && chunks <= 32 * kWave)
+    return chunks <= 16 * kWave ? 161 : 162;
   if (chunks <= kWave) return 1;           // one wave per row, 1 chunk per lane
   if (chunks <= 2 * kWave) return 2;       // one wave per row, 2 chunks per lane
   if (chunks <= 1 * kThreads) return 11;   // four waves per row, 1..8 chunks per lane
@@ -227,7 +234,7 @@ int norm_rows_per_task(int64_t total_rows, int variant) {
   // then loaded once per two rows while the grid still covers every CU many
   // times (measured on the 8192 x 8192 and 65536 x 7168 workloads: 1 and 2
   // rows per task beat 4 and 8).
-  const int64_t slots = variant < 10 ? kWavesPerGroup : 1;
+  const int64_t slots = variant < 10 ? kWavesPerGroup : 1;   // row slots per workgroup
   const int64_t g = total_rows >= slots * 8192 ? 2 : 1;
   return (int)(g * slots);
 }
@@ -236,10 +243,12 @@ template <class Args>
 hipError_t launch_norm(const Args& a, int64_t total_tasks, int variant, int rows_per_task,
                        hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
-  const dim3 block(kThreads);
+  const dim3 block(kThreads), wide(64 * 16);
   const dim3 grid((uint32_t)total_tasks);
   const int r = rows_per_task;
   switch (variant) {
+    case 161: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 16, 1, 16>), grid, wide, 0, s, a, r); break;
+    case 162: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 16, 2, 16>), grid, wide, 0, s, a, r); break;
     case 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 1>), grid, block, 0, s, a, r); break;
     case 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 2>), grid, block, 0, s, a, r); break;
     case 11: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 1>), grid, block, 0, s, a, r); break;

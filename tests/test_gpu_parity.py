@@ -336,6 +336,9 @@ def check_fused(orc, x, gamma, off, eps, rows_sel=None, what=""):
 
 @pytest.mark.parametrize("shape", [(1, 32), (5, 96), (16, 512), (3, 544), (64, 4096),
                                    (8, 16384), (4, 16416), (2, 40000),
+                                   # at most 256 rows: 16 waves per row (1 or 2 chunks a
+                                   # lane); 257 rows: four waves per row again
+                                   (3, 12288), (256, 2080), (257, 2080),
                                    # enough rows that a workgroup walks several, last group ragged
                                    (2051, 96), (4099, 2048), (16411, 4096), (20003, 7168)])
 def test_fused_shapes(orc, shape):
