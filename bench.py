@@ -292,13 +292,20 @@ def trace_summary(trace_csv: str) -> str:
                 continue
             key = (short_kernel_name(name), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
             agg[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines = ["%-60s %10s %6s %12s %12s %12s" % ("kernel", "workgroups", "calls", "mean_us",
-                                                "median_us", "min_us")]
+    lines = ["%-60s %10s %6s %10s %10s %10s %10s %10s" % ("kernel", "workgroups", "calls", "mean_us",
+                                                          "p10_us", "median_us", "p90_us", "min_us")]
     for (name, wgs), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         v.sort()
-        lines.append("%-60s %10d %6d %12.3f %12.3f %12.3f" % (
-            name[-60:], wgs, len(v), sum(v) / len(v) / 1e3, v[len(v) // 2] / 1e3, v[0] / 1e3))
+        lines.append("%-60s %10d %6d %10.3f %10.3f %10.3f %10.3f %10.3f" % (
+            name[-60:], wgs, len(v), sum(v) / len(v) / 1e3, percentile(v, 10) / 1e3, v[len(v) // 2] / 1e3,
+            percentile(v, 90) / 1e3, v[0] / 1e3))
     return "\n".join(lines)
+
+
+def percentile(sorted_values, q):
+    """The q-th percentile of a sorted list (nearest rank)."""
+    k = max(0, min(len(sorted_values) - 1, -(-q * len(sorted_values) // 100) - 1))
+    return sorted_values[k]
 
 
 def counter_bytes(counter_csv: str, counter: str):
