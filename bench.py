@@ -148,6 +148,17 @@ def bench_other_rows(torch, mx, synth, steps):
     ms, _ = T.run(lambda i: mx.quantize(xs[i % n], True, False, out=outs[i % n]), steps, 10)
     res["rowwise_256x1024"] = (ms, alg, r * c)
 
+    x = synth.workload("rowwise_8192x7168", device=dev)["x"]
+    r, c = x.shape
+    alg = r * c * 3 + r * c // 32
+    sets = rotation(alg)
+    xs = [x.clone() for _ in range(sets)]
+    del x
+    outs = [mx.quantize(xi, True, False) for xi in xs]
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % sets], True, False, out=outs[i % sets]), max(steps // 4, 10), 3)
+    res["rowwise_8192x7168"] = (ms, alg, r * c)
+    del xs, outs
+
     w = synth.workload("rmsnorm_8192x8192", device=dev)
     r, c = w["x"].shape
     alg = r * c * 2 + r * c * 2 + r * c + r * c // 32 + c * 2

@@ -25,6 +25,8 @@ Workloads (sizes are one GPU's share at its real shape):
    offset 0.0, eps 1e-5
 6. rowwise + columnwise quantize of a float32 master weight [4096, 4096]: the
    recipe of 2 kept in float32, with float32 subnormal tiles
+7. rowwise-only quantize of a prefill activation [8192, 7168] ~ N(0, 1): the
+   activation a linear layer quantizes before its MXFP8 product
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ SHAPES = {
     "rmsnorm_decode_16x7168": (16, 7168),
     "rmsnorm_prefill_65536x7168": (65536, 7168),
     "rowcol_f32_4096x4096": (4096, 4096),
+    "rowwise_8192x7168": (8192, 7168),
 }
 SEEDS = {
     "rowwise_256x1024": 1001,
@@ -49,6 +52,7 @@ SEEDS = {
     "rmsnorm_decode_16x7168": 1005,
     "rmsnorm_prefill_65536x7168": 1005,
     "rowcol_f32_4096x4096": 1006,
+    "rowwise_8192x7168": 1007,
 }
 
 
@@ -160,7 +164,7 @@ def expert_weights(n=64, rows=2048, cols=7168, seed=1004, device="cpu", std=0.01
 def workload(name: str, device="cpu", **overrides):
     """Inputs of a named workload as a dict of tensors and scalars."""
     seed = overrides.pop("seed", SEEDS[name])
-    if name == "rowwise_256x1024":
+    if name in ("rowwise_256x1024", "rowwise_8192x7168"):
         r, c = overrides.get("shape", SHAPES[name])
         return {"x": rowwise_input(r, c, seed, device)}
     if name == "rowcol_4096x4096":

@@ -129,6 +129,12 @@ def test_every_value_against_every_scale(orc):
     check_quantize(orc, np.ascontiguousarray(xt[:, :cols]), False, True, "pairs columnwise")
 
 
+def test_rowwise_activation_8192x7168_full(orc):
+    # the rowwise-only bench workload at full size, every byte against the oracle
+    x = synth.workload("rowwise_8192x7168")["x"]
+    check_quantize(orc, synth.bf16_bits(x), True, False, "activation 8192x7168")
+
+
 def test_weight_4096_full(orc):
     x = synth.workload("rowcol_4096x4096")["x"]
     check_quantize(orc, synth.bf16_bits(x), True, True, "rowcol_4096x4096")
