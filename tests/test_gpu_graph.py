@@ -47,3 +47,49 @@ def test_graph_replays_match_eager():
         assert np.array_equal(host(normed.view(torch.int16)), host(wn.view(torch.int16)))
         assert np.array_equal(host(q), host(wq)) and np.array_equal(host(s), host(ws))
         assert np.array_equal(host(deq.view(torch.int32)), host(wd.view(torch.int32)))
+
+
+def test_calls_run_on_the_current_stream():
+    """Every entry point launches on the caller's current stream: on a side
+    stream held up by a long sleep, then given a new input, each result must
+    reflect that new input (a launch on any other stream would read the old
+    one)."""
+    print("[case] side stream: quantize, quantize_f32, rmsnorm_quantize, dequantize, gemm", flush=True)
+    x = synth.weight_with_outliers(256, 1056, seed=41).to(DEV)
+    x_new = synth.weight_with_outliers(256, 1056, seed=42).to(DEV)
+    xf = x.float()
+    xf_new = x_new.float()
+    xn, gamma = synth.rmsnorm_inputs(64, 7168, seed=43, x_std=3.0, row_decades=2.0)
+    xn, gamma = xn.to(DEV), gamma.to(DEV)
+    xn_new = (xn.float() * 3.0).to(torch.bfloat16)
+    a = synth.weight_with_outliers(96, 512, seed=44).to(DEV)
+    a_new = synth.weight_with_outliers(96, 512, seed=45).to(DEV)
+    b = mx.quantize(synth.weight_with_outliers(160, 512, seed=46).to(DEV), True, False)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)     # default priority
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)        # hold the stream for several milliseconds
+        x.copy_(x_new)
+        xf.copy_(xf_new)
+        xn.copy_(xn_new)
+        a.copy_(a_new)
+        p = mx.quantize(x, True, True)
+        pf = mx.quantize(xf, True, True)
+        normed, q, s = mx.rmsnorm_quantize(xn, gamma, 0.5, 1e-5)
+        pa = mx.quantize(a, True, False)
+        d = mx.dequantize(p.columnwise_data, p.columnwise_scale, mx.COLUMNWISE)
+        out = mx.gemm(pa.rowwise_data, pa.rowwise_scale, b.rowwise_data, b.rowwise_scale)
+    torch.cuda.synchronize()
+    want = mx.quantize(x_new, True, True)
+    wantf = mx.quantize(xf_new, True, True)
+    wn, wq, ws = mx.rmsnorm_quantize(xn_new, gamma, 0.5, 1e-5)
+    wa = mx.quantize(a_new, True, False)
+    wd = mx.dequantize(want.columnwise_data, want.columnwise_scale, mx.COLUMNWISE)
+    wo = mx.gemm(wa.rowwise_data, wa.rowwise_scale, b.rowwise_data, b.rowwise_scale)
+    torch.cuda.synchronize()
+    for got, exp in zip(list(p) + list(pf), list(want) + list(wantf)):
+        assert np.array_equal(host(got), host(exp)), "quantize did not see the side stream's input"
+    assert np.array_equal(host(normed.view(torch.int16)), host(wn.view(torch.int16)))
+    assert np.array_equal(host(q), host(wq)) and np.array_equal(host(s), host(ws))
+    assert np.array_equal(host(d.view(torch.int32)), host(wd.view(torch.int32)))
+    assert np.array_equal(host(out.view(torch.int32)), host(wo.view(torch.int32)))
