@@ -162,11 +162,13 @@ def bench_other_rows(torch, mx, synth, steps):
     w = synth.workload("rmsnorm_8192x8192", device=dev)
     r, c = w["x"].shape
     alg = r * c * 2 + r * c * 2 + r * c + r * c // 32 + c * 2
-    o = mx.rmsnorm_quantize(w["x"], w["gamma"], w["weight_offset"], w["eps"])
-    ms, _ = T.run(lambda i: mx.rmsnorm_quantize(w["x"], w["gamma"], w["weight_offset"], w["eps"], out=o),
-                  max(steps // 4, 5), 3)
+    sets = rotation(alg)
+    xs = [w["x"].clone() for _ in range(sets)]
+    os_ = [mx.rmsnorm_quantize(xi, w["gamma"], w["weight_offset"], w["eps"]) for xi in xs]
+    ms, _ = T.run(lambda i: mx.rmsnorm_quantize(xs[i % sets], w["gamma"], w["weight_offset"], w["eps"],
+                                                out=os_[i % sets]), max(steps // 4, 5), 3)
     res["rmsnorm_8192x8192"] = (ms, alg, r * c)
-    del w, o
+    del w, xs, os_
 
     xs = synth.workload("grouped_64x2048x7168", device=dev)["xs"]
     r, c = xs[0].shape
@@ -226,9 +228,13 @@ def bench_other_rows(torch, mx, synth, steps):
     p = mx.quantize(x, True, True)
     for axis, q, s in ((0, p.rowwise_data, p.rowwise_scale), (1, p.columnwise_data, p.columnwise_scale)):
         alg = r * c + s.numel() + r * c * 4
-        out = mx.dequantize(q, s, axis)
-        ms, _ = T.run(lambda i: mx.dequantize(q, s, axis, out=out), steps, 5)
+        sets = rotation(alg)
+        qs = [(q.clone(), s.clone()) for _ in range(sets)]
+        outs = [mx.dequantize(qi, si, axis) for qi, si in qs]
+        ms, _ = T.run(lambda i: mx.dequantize(qs[i % sets][0], qs[i % sets][1], axis, out=outs[i % sets]),
+                      steps, 5)
         res["dequantize_f32_%s_4096x4096" % ("row" if axis == 0 else "col")] = (ms, alg, r * c)
+        del qs, outs
     out = {k: {"ms_per_launch": round(ms, 5), "GB_s": round(b / (ms * 1e-3) / 1e9, 1),
                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "Gelem_s": round(e / (ms * 1e-3) / 1e9, 2), "alg_bytes": b}
@@ -249,8 +255,13 @@ def bench_gemm(torch, mx, steps):
         b = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
         pa, pb = mx.quantize(a, True, False), mx.quantize(b, True, False)
         del a, b
+        # the weight rotates over copies that together exceed the Infinity
+        # Cache, so every launch reads B from HBM, as a layer's weight is
+        sets = rotation(N * K + N * K // 32)
+        bs = [(pb.rowwise_data.clone(), pb.rowwise_scale.clone()) for _ in range(sets)]
+        del pb
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        fn = lambda i: mx.gemm(pa.rowwise_data, pa.rowwise_scale, pb.rowwise_data, pb.rowwise_scale,
+        fn = lambda i: mx.gemm(pa.rowwise_data, pa.rowwise_scale, bs[i % sets][0], bs[i % sets][1],
                                torch.bfloat16, out=out)
         ms, _ = T.run(fn, max(steps // 4, 10), 3)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
@@ -263,6 +274,7 @@ def bench_gemm(torch, mx, steps):
             rec.update({"alg_bytes": int(alg), "GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         res["gemm_bf16out_%dx%dx%d" % (M, N, K)] = rec
+        del bs, pa, out
     return res
 
 

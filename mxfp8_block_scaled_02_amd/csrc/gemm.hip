@@ -501,115 +501,151 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
 //
 // A few activation rows against a large weight (decode): the product is bound
 // by streaming B once from HBM.  A workgroup owns 32 output columns and its
-// four waves split K into contiguous ranges of 128-deep units.  Each wave
-// streams its B rows into two private LDS buffers with coalesced direct loads
-// (one 1 KiB load covers 8 rows x 128 bytes), reads the MFMA fragments back
-// (16-byte chunk c of row r stored at chunk c ^ (r % 8) ^ ((r / 8) % 2)), and
-// multiplies them by MT 32-row tiles of A (M <= 32 MT), whose fragments it
-// loads straight from cache (only the M real rows; padding rows are zero).
-// The four partial tiles meet in LDS and are summed in wave order.
+// four waves split K into contiguous ranges of 128-deep units.  For each unit
+// a wave loads the 32 B rows and the A rows (MT 32-row tiles, M <= 32 MT)
+// into registers with coalesced loads, one unit ahead: every load covers
+// 8 rows x 128 bytes (1 KiB).  It writes them into its own LDS region (the
+// 16-byte chunk c of row r at chunk c ^ (r % 8) ^ ((r / 8) % 2)), reads the
+// MFMA fragments back, and multiplies.  A rows past M are zero.  The four
+// partial tiles meet in LDS and are summed in wave order.
+//
+// Measured on 16 x 7168 x 7168 with the weight read from HBM: loading B
+// straight into LDS (global_load_lds) and the A fragments one per lane and
+// row took 15.7 us; this register path takes about 10.5 us.  Reading B
+// alone in the same pattern takes 8.9 us.
 
 constexpr int kSkinnyWaves = 4;
-constexpr int kSkinnyUnits = 1;                       // 128-deep units per chunk
-constexpr int kSkinnyChunk = 32 * 128 * kSkinnyUnits;  // one wave's chunk of B in LDS
-
-// the two chunk buffers of every wave, as two arrays so that the compiler
-// can tell a chunk in flight from the one being read
-__shared__ __attribute__((aligned(1024))) uint8_t s_skinny0[kSkinnyWaves * kSkinnyChunk];
-__shared__ __attribute__((aligned(1024))) uint8_t s_skinny1[kSkinnyWaves * kSkinnyChunk];
+constexpr int kSkinnyRegion = 32 * 128;   // one operand tile of one unit in LDS (4 KiB)
 
 __device__ __forceinline__ int skinny_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// loads one chunk issues: per unit four LDS loads of B, a B scale word, and
-// per A tile four fragment loads and a scale word
-template <int MT> constexpr int skinny_loads() { return kSkinnyUnits * (5 + 5 * MT); }
+// s_waitcnt lgkmcnt(0), vmcnt and expcnt left alone
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __device__ __forceinline__ void skinny_pin() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+
+// one unit in registers: lane l holds row 8 g + l / 8 of each 32-row tile,
+// chunk l % 8.  Scale words are in fragment order (row l % 32).  With PAIRS
+// one load fetches the words of two units (ps and ps + 1) and `off` (0 or 1,
+// the same for the wave) says which of them is this unit's; without PAIRS
+// (a single 128-deep unit in K) only .x is loaded.
 template <int MT>
-struct SkinnyChunk {
-  u32x4 a[kSkinnyUnits][MT][4];
-  uint32_t sa[kSkinnyUnits][MT], sb[kSkinnyUnits];
+struct SkinnyUnit {
+  u32x4 b[4];
+  u32x4 a[MT][4];
+  u32x2 sa[MT], sb;
+  int64_t off;
 };
 
-template <int MT>
+template <int MT, bool PAIRS>
 struct Skinny {
   const GemmParams& p;
-  int wave, lane, fr, h;
-  int64_t n0, K, u1;
-  uint32_t amask[MT];           // ~0 for a real A row, 0 for a padding row
-  const uint8_t* pa[MT];
+  int lane, fr, h, lr, ch;
+  int64_t n0, K, units;
+  uint8_t* region;              // this wave's LDS: B tile, then the MT A tiles
   const uint8_t* psa[MT];
   const uint8_t* psb;
 
-  __device__ Skinny(const GemmParams& pp, int w, int l, int64_t nn0, int64_t uu1)
-      : p(pp), wave(w), lane(l), fr(l & 31), h(l >> 5), n0(nn0), K(pp.K), u1(uu1) {
+  __device__ Skinny(const GemmParams& pp, int w, int l, int64_t nn0, uint8_t* lds)
+      : p(pp), lane(l), fr(l & 31), h(l >> 5), lr(l >> 3), ch(l & 7), n0(nn0), K(pp.K),
+        units(pp.K / 128), region(lds + w * (1 + MT) * kSkinnyRegion) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int64_t row = 32 * t + fr;
-      const int64_t rr = min(row, p.M - 1);
-      amask[t] = row < p.M ? ~0u : 0u;
-      pa[t] = p.qa + rr * K + 16 * h;
-      psa[t] = p.sa + rr * p.sa_ld;
-    }
+    for (int t = 0; t < MT; ++t) psa[t] = p.sa + min((int64_t)(32 * t + fr), p.M - 1) * p.sa_ld;
     psb = p.sb + min(n0 + fr, p.N - 1) * p.sb_ld;
   }
 
-  // units u .. u + kSkinnyUnits - 1 (past u1: the last unit again) of B into
-  // this wave's part of buf, and the matching A fragments and scales
-  __device__ __forceinline__ void load(uint8_t* buf, int64_t u, SkinnyChunk<MT>& c) {
-    uint8_t* mine = buf + wave * kSkinnyChunk;
-    const int lr = lane >> 3;
+  // Unit u into c.  The scale words go out first: the register copies the
+  // loop makes of them wait for their loads, and loads complete in order,
+  // so a wait for an early load leaves the later ones in flight.  Each scale
+  // load touches one line per row; fetching two units' words at once halves
+  // them (measured on 16 x 7168 x 7168: about 3.8 us of 14.2 went to
+  // one-word scale loads).
+  __device__ __forceinline__ void load(int64_t u, SkinnyUnit<MT>& c, bool scales) const {
+    if (scales) {
+      if constexpr (PAIRS) {
+        const int64_t ps = min(u, units - 2);   // both words inside the row
 #pragma unroll
-    for (int v = 0; v < kSkinnyUnits; ++v) {
-      const int64_t uu = min(u + v, u1 - 1);
+        for (int t = 0; t < MT; ++t) c.sa[t] = *reinterpret_cast<const u32x2_a4*>(psa[t] + ps * 4);
+        c.sb = *reinterpret_cast<const u32x2_a4*>(psb + ps * 4);
+        c.off = u - ps;
+      } else {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) c.sa[t].x = *reinterpret_cast<const uint32_t*>(psa[t] + u * 4);
+        c.sb.x = *reinterpret_cast<const uint32_t*>(psb + u * 4);
+        c.off = 0;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t row = min(n0 + 8 * g + lr, p.N - 1);
+      c.b[g] = load16(p.qb + row * K + u * 128 + 16 * ch);
+    }
+    // rows past M read row M - 1 (a cache hit) and are zeroed in stage(); a
+    // select here would make the compiler wait for the load at once
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int r = 8 * g + lr;
-        const int chunk = (lane & 7) ^ skinny_swizzle(r);
-        const int64_t row = min(n0 + r, p.N - 1);
-        __builtin_amdgcn_global_load_lds(p.qb + row * K + uu * 128 + 16 * chunk,
-                                         (lds_ptr)(mine + 4096 * v + 1024 * g), 16, 0, 0);
+        const int64_t row = min((int64_t)(32 * t + 8 * g + lr), p.M - 1);
+        c.a[t][g] = load16_cached(p.qa + row * K + u * 128 + 16 * ch);
       }
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c.a[v][t][q] = load16_cached(pa[t] + uu * 128 + 32 * q) & amask[t];
-        c.sa[v][t] = *reinterpret_cast<const uint32_t*>(psa[t] + uu * 4);
-      }
-      c.sb[v] = *reinterpret_cast<const uint32_t*>(psb + uu * 4);
     }
   }
 
-  __device__ __forceinline__ void compute(const uint8_t* buf, int64_t u, const SkinnyChunk<MT>& c,
-                                          v16f (&acc)[MT]) {
-    const uint8_t* mine = buf + wave * kSkinnyChunk + fr * 128;
+  // the unit's tiles into this wave's LDS region, swizzled
+  __device__ __forceinline__ void stage(const SkinnyUnit<MT>& c) const {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r = 8 * g + lr;
+      const int at = r * 128 + 16 * (ch ^ skinny_swizzle(r));
+      *reinterpret_cast<u32x4*>(region + at) = c.b[g];
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        *reinterpret_cast<u32x4*>(region + (1 + t) * kSkinnyRegion + at) =
+            32 * t + r < p.M ? c.a[t][g] : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // the unit in c through LDS and the MFMAs with scale words sa, sb (its B
+  // fragments ANDed with keep); c is refilled with unit next
+  __device__ __forceinline__ void step(SkinnyUnit<MT>& c, const uint32_t (&sa)[MT], uint32_t sb,
+                                       int64_t next, bool scales, uint32_t keep, v16f (&acc)[MT]) const {
+    stage(c);
+    skinny_pin();
+    load(next, c, scales);
+    skinny_pin();
+    wait_lds();                                  // the unit's LDS writes are done
+    skinny_pin();
+    compute(sa, sb, keep, acc);
+  }
+
+  __device__ __forceinline__ void compute(const uint32_t (&sa)[MT], uint32_t sb, uint32_t keep,
+                                          v16f (&acc)[MT]) const {
+    const uint8_t* row = region + fr * 128;
     const int f = skinny_swizzle(fr);
 #pragma unroll
-    for (int v = 0; v < kSkinnyUnits; ++v) {
-      // a unit past the end repeats the last one: its B fragments become zero
-      const uint32_t keep = u + v < u1 ? ~0u : 0u;
+    for (int j = 0; j < 2; ++j) {
+      const int c0 = 16 * ((4 * j + h) ^ f), c1 = 16 * ((4 * j + h + 2) ^ f);
+      const v8i fb = frag(*reinterpret_cast<const u32x4*>(row + c0) & keep,
+                          *reinterpret_cast<const u32x4*>(row + c1) & keep);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4 b0 = *reinterpret_cast<const u32x4*>(mine + 4096 * v + 16 * ((4 * j + h) ^ f));
-        u32x4 b1 = *reinterpret_cast<const u32x4*>(mine + 4096 * v + 16 * ((4 * j + h + 2) ^ f));
-        b0 &= keep;
-        b1 &= keep;
-        const v8i fb = frag(b0, b1);
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-          acc[t] = mfma(frag(c.a[v][t][2 * j], c.a[v][t][2 * j + 1]), fb, acc[t], c.sa[v][t] >> (16 * j + 8 * h),
-                        c.sb[v] >> (16 * j + 8 * h));
+      for (int t = 0; t < MT; ++t) {
+        const uint8_t* ra = row + (1 + t) * kSkinnyRegion;
+        const v8i fa = frag(*reinterpret_cast<const u32x4*>(ra + c0), *reinterpret_cast<const u32x4*>(ra + c1));
+        acc[t] = mfma(fa, fb, acc[t], sa[t] >> (16 * j + 8 * h), sb >> (16 * j + 8 * h));
       }
     }
   }
 };
 
-template <int MT>
+template <int MT, bool PAIRS>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kSkinnyWaves * (1 + MT) * kSkinnyRegion];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -617,46 +653,44 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
   const int64_t n0 = (int64_t)blockIdx.x * 32;
   const int64_t units = p.K / 128;
   const int64_t u0 = units * wave / kSkinnyWaves, u1 = units * (wave + 1) / kSkinnyWaves;
-  constexpr int kLoads = skinny_loads<MT>();
 
-  Skinny<MT> sk(p, wave, lane, n0, u1);
-
-  // Chunk pipeline, explicit about waits: each block of loads and each block
-  // of MFMAs is pinned in place (compiler memory fence + scheduling barrier),
-  // a chunk is read once only the next chunk's kLoads loads remain in flight,
-  // and a buffer is refilled only after its LDS reads have returned.
+  const Skinny<MT, PAIRS> sk(p, wave, lane, n0, lds);
   v16f acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = v16f{};
   if (u0 < u1) {
-    SkinnyChunk<MT> c0, c1;
-    sk.load(s_skinny0, u0, c0);
-    for (int64_t u = u0; u < u1; u += 2 * kSkinnyUnits) {
+    // Two units in flight: while unit u goes through LDS and the MFMAs, the
+    // loads of units u + 1 and u + 2 are outstanding.  The two register sets
+    // alternate (c0 even units from u0, c1 odd); a load past the wave's range
+    // reads its last unit again (a cache hit), so every iteration issues the
+    // same loads and the compiler waits for exactly the set it is about to
+    // use.  With PAIRS, c0's scale load also brings c1's words.
+    SkinnyUnit<MT> c0, c1;
+    sk.load(u0, c0, true);
+    sk.load(min(u0 + 1, u1 - 1), c1, !PAIRS);
+    for (int64_t u = u0; u < u1; u += 2) {
       skinny_pin();
-      wait_loads<kLoads>();                        // vmcnt(n) lgkmcnt(0)
+      uint32_t sa[MT], sb, sa1[MT], sb1;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        sa[t] = c0.off ? c0.sa[t].y : c0.sa[t].x;
+        sa1[t] = PAIRS ? c0.sa[t].y : c1.sa[t].x;
+      }
+      sb = c0.off ? c0.sb.y : c0.sb.x;
+      sb1 = PAIRS ? c0.sb.y : c1.sb.x;
+      sk.step(c0, sa, sb, min(u + 2, u1 - 1), true, ~0u, acc);
+      // unconditional, so that the compiler's wait counts are the same on
+      // every path; past the range (an odd count) it adds zero products
       skinny_pin();
-      sk.load(s_skinny1, u + kSkinnyUnits, c1);
-      skinny_pin();
-      wait_loads<kLoads>();                        // chunk u has landed
-      skinny_pin();
-      sk.compute(s_skinny0, u, c0, acc);
-      skinny_pin();
-      wait_loads<kLoads>();                        // reads of chunk u returned
-      skinny_pin();
-      sk.load(s_skinny0, u + 2 * kSkinnyUnits, c0);
-      skinny_pin();
-      wait_loads<kLoads>();                        // chunk u + kSkinnyUnits has landed
-      skinny_pin();
-      sk.compute(s_skinny1, u + kSkinnyUnits, c1, acc);
+      sk.step(c1, sa1, sb1, min(u + 3, u1 - 1), !PAIRS, u + 1 < u1 ? ~0u : 0u, acc);
     }
     skinny_pin();
-    wait_loads<0>();                               // no load may land after the workgroup ends
   }
 
-  // the partial tiles reuse the first chunk buffer once every wave is done,
-  // one 32-row A tile at a time
-  float (*part)[32][32] = reinterpret_cast<float (*)[32][32]>(s_skinny0);
-  static_assert(sizeof(float) * kSkinnyWaves * 32 * 32 <= sizeof(s_skinny0), "partials fit");
+  // the partial tiles reuse the LDS regions once every wave is done, one
+  // 32-row A tile at a time
+  float (*part)[32][32] = reinterpret_cast<float (*)[32][32]>(lds);
+  static_assert(sizeof(float) * kSkinnyWaves * 32 * 32 <= sizeof(lds), "partials fit");
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     __syncthreads();
@@ -679,6 +713,15 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
   }
 }
 
+// paired scale loads need two units in K (K >= 256)
+template <int MT>
+void launch_skinny(const GemmParams& p, int64_t workgroups, hipStream_t s) {
+  if (p.K >= 256)
+    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, true>), dim3((uint32_t)workgroups), dim3(kSkinnyWaves * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, false>), dim3((uint32_t)workgroups), dim3(kSkinnyWaves * 64), 0, s, p);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
@@ -692,9 +735,9 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t skinny = (N + 31) / 32;
   if (M <= 32) {
-    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<1>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);
+    launch_skinny<1>(p, skinny, s);
   } else if (M <= 64) {
-    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<2>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);
+    launch_skinny<2>(p, skinny, s);
   } else if (K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 && sb_pitch % 16 == 0) {
     // the ring tile with the least rounds of tiles over the CUs times the
     // time of one tile at full load, in eighths of a 256 x 256 tile's
@@ -718,7 +761,7 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
       default: hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<64, 128>), grid, dim3(kThreads), 0, s, p); break;
     }
   } else if (M <= 128) {
-    hipLaunchKernelGGL(mxfp8_gemm_skinny_kernel<4>, dim3((uint32_t)skinny), dim3(kSkinnyWaves * 64), 0, s, p);
+    launch_skinny<4>(p, skinny, s);
   } else {
     p.tiles_m = (int32_t)((M + kGT - 1) / kGT);
     p.tiles_n = (int32_t)((N + kGT - 1) / kGT);
