@@ -80,7 +80,7 @@ def test_random_shapes_and_routes(orc, seed):
             assert bool((b[mask] == 0xA5).all()), "padding written"
 
 
-@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("seed", range(6))
 def test_random_gemm_shapes(orc, seed):
     g = np.random.default_rng(2000 + seed)
     for case in range(8):
