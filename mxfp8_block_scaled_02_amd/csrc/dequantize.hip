@@ -18,15 +18,6 @@ namespace mx {
 
 namespace {
 
-__device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t task) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= task) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Decode the 4 bytes of q with per-element scales sc[0..3] and store them at
 // element e (16 bytes of float32 or 8 bytes of bf16 per lane, so each store
 // instruction writes one contiguous span across the wave).

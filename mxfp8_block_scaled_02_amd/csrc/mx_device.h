@@ -37,6 +37,8 @@ typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+constexpr u32x4 kZero4 = {0, 0, 0, 0};
+
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
       __builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b)));

@@ -159,6 +159,17 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
                        int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
                        void* out, bool out_bf16, hipStream_t s);
 
+// The tensor of a launch's table that task belongs to: the last i with
+// start[i] <= task, by binary search over the prefix sum of task counts.
+__device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t task) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= task) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Scale index of flat block b of a plane with bpr blocks per row, stored
 // with rows pitch bytes apart (b < 2^32 whenever pitch != bpr).
 __device__ __forceinline__ int64_t pitched_block(int64_t b, int64_t bpr, int64_t pitch) {

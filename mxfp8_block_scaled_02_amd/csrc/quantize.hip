@@ -28,16 +28,6 @@ namespace mx {
 
 namespace {
 
-__device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t task) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= task) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-constexpr u32x4 kZero4 = {0, 0, 0, 0};
 constexpr int kCh = kLaneCols / kChunk;     // 16-byte chunks per lane per row (1 or 2)
 
 // Rowwise scale parameters of the block that holds this lane's kLaneCols

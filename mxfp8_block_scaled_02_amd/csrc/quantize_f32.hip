@@ -26,17 +26,6 @@ namespace {
 constexpr int kF32Lane = 4;                       // float32 per lane per row
 constexpr int kF32TileCols = kWave * kF32Lane;    // 256
 
-__device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t task) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= task) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-constexpr u32x4 kZero4 = {0, 0, 0, 0};
-
 __device__ __forceinline__ uint32_t f32_key4(const u32x4& v) {
   return max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
 }

@@ -26,15 +26,6 @@ namespace mx {
 
 namespace {
 
-__device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t task) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= task) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 __device__ __forceinline__ float sumsq_chunk(const u32x4& v, float acc) {
   acc = __builtin_fmaf(bf16_lo(v.x), bf16_lo(v.x), acc);
   acc = __builtin_fmaf(bf16_hi(v.x), bf16_hi(v.x), acc);
