@@ -503,16 +503,17 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
 // by streaming B once from HBM.  A workgroup owns 32 output columns and its
 // four waves split K into contiguous ranges of 128-deep units.  For each unit
 // a wave loads the 32 B rows and the A rows (MT 32-row tiles, M <= 32 MT)
-// into registers with coalesced loads, one unit ahead: every load covers
+// into registers with coalesced loads, two units ahead: every load covers
 // 8 rows x 128 bytes (1 KiB).  It writes them into its own LDS region (the
 // 16-byte chunk c of row r at chunk c ^ (r % 8) ^ ((r / 8) % 2)), reads the
 // MFMA fragments back, and multiplies.  A rows past M are zero.  The four
 // partial tiles meet in LDS and are summed in wave order.
 //
-// Measured on 16 x 7168 x 7168 with the weight read from HBM: loading B
-// straight into LDS (global_load_lds) and the A fragments one per lane and
-// row took 15.7 us; this register path takes about 10.5 us.  Reading B
-// alone in the same pattern takes 8.9 us.
+// Measured on 16 x 7168 x 7168 with the weight read from HBM (rotating
+// copies): loading B straight into LDS (global_load_lds) and the A fragments
+// one per lane and row, one unit in flight, took 15.7 us; this register path
+// takes 13.3 us.  Reading B alone in the same pattern takes 8.9 us; most of
+// the rest goes to the scale-word loads, which touch one line per row.
 
 constexpr int kSkinnyWaves = 4;
 constexpr int kSkinnyRegion = 32 * 128;   // one operand tile of one unit in LDS (4 KiB)
