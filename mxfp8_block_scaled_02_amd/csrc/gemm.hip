@@ -530,11 +530,25 @@ __device__ __forceinline__ void skinny_pin() {
 
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 
+// Scale words.  STAGED (a wave's K range of at most staged_units<MT>() units):
+// the wave copies the words of its whole range into LDS once,
+// with loads in which consecutive lanes read consecutive words of a row, and
+// reads one word per row and unit from there.  Otherwise (PAIRED, K >= 256)
+// every other unit one load per tile brings two units' words, one per row.
+// A load of one word per row touches one cache line per row, 32 per load;
+// on 16 x 7168 x 7168 one-word loads cost about 3.8 us of 14.2, paired loads
+// about 2 us of 13.3.
+// units a wave can stage (LDS: 32 for one or two A tiles, 16 for four), the
+// words between staged rows (odd: no bank conflicts), the words of one tile
+template <int MT> constexpr int staged_units() { return MT <= 2 ? 32 : 16; }
+template <int MT> constexpr int staged_stride() { return staged_units<MT>() + 1; }
+template <int MT> constexpr int staged_tile() { return 32 * staged_stride<MT>(); }
+enum { kSkinnyStaged = 0, kSkinnyPaired = 1 };
+
 // one unit in registers: lane l holds row 8 g + l / 8 of each 32-row tile,
-// chunk l % 8.  Scale words are in fragment order (row l % 32).  With PAIRS
-// one load fetches the words of two units (ps and ps + 1) and `off` (0 or 1,
-// the same for the wave) says which of them is this unit's; without PAIRS
-// (a single 128-deep unit in K) only .x is loaded.
+// chunk l % 8.  PAIRED: the scale words of units ps and ps + 1 in fragment
+// order (row l % 32), and `off` (0 or 1, the same for the wave) says which of
+// them is this unit's.
 template <int MT>
 struct SkinnyUnit {
   u32x4 b[4];
@@ -543,43 +557,76 @@ struct SkinnyUnit {
   int64_t off;
 };
 
-template <int MT, bool PAIRS>
+template <int MT, int SC>
 struct Skinny {
   const GemmParams& p;
   int lane, fr, h, lr, ch;
   int64_t n0, K, units;
   uint8_t* region;              // this wave's LDS: B tile, then the MT A tiles
+  uint32_t* sreg;               // STAGED: this wave's scale words, B tile then the A tiles
   const uint8_t* psa[MT];
   const uint8_t* psb;
 
-  __device__ Skinny(const GemmParams& pp, int w, int l, int64_t nn0, uint8_t* lds)
+  __device__ Skinny(const GemmParams& pp, int w, int l, int64_t nn0, uint8_t* lds, uint32_t* slds)
       : p(pp), lane(l), fr(l & 31), h(l >> 5), lr(l >> 3), ch(l & 7), n0(nn0), K(pp.K),
-        units(pp.K / 128), region(lds + w * (1 + MT) * kSkinnyRegion) {
+        units(pp.K / 128), region(lds + w * (1 + MT) * kSkinnyRegion),
+        sreg(slds + w * (1 + MT) * staged_tile<MT>()) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) psa[t] = p.sa + min((int64_t)(32 * t + fr), p.M - 1) * p.sa_ld;
     psb = p.sb + min(n0 + fr, p.N - 1) * p.sb_ld;
   }
 
-  // Unit u into c.  The scale words go out first: the register copies the
-  // loop makes of them wait for their loads, and loads complete in order,
-  // so a wait for an early load leaves the later ones in flight.  Each scale
-  // load touches one line per row; fetching two units' words at once halves
-  // them (measured on 16 x 7168 x 7168: about 3.8 us of 14.2 went to
-  // one-word scale loads).
-  __device__ __forceinline__ void load(int64_t u, SkinnyUnit<MT>& c, bool scales) const {
-    if (scales) {
-      if constexpr (PAIRS) {
-        const int64_t ps = min(u, units - 2);   // both words inside the row
+  // STAGED: the scale words of units u0 .. u0 + U - 1 (U <= staged_units) of
+  // the B tile and the A tiles into sreg, word k of row r at r * stride + k.
+  // Lane l of load i takes entry e = l + 64 i of the row-major 32 x U block,
+  // so a load reads whole runs of one row.  All loads go out before the first
+  // LDS write.
+  __device__ __forceinline__ void stage_scales(int64_t u0, int U) const {
+    constexpr int kLoads = staged_units<MT>() * 32 / 64;
+    const int n = 32 * U, iters = (n + 63) / 64;
+    // e / U as (e * m) >> 16 with m = ceil(2^16 / U): exact for e < 2^16 / U
+    const uint32_t m = (65536u + (uint32_t)U - 1u) / (uint32_t)U;
+    uint32_t v[1 + MT][kLoads];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) c.sa[t] = *reinterpret_cast<const u32x2_a4*>(psa[t] + ps * 4);
-        c.sb = *reinterpret_cast<const u32x2_a4*>(psb + ps * 4);
-        c.off = u - ps;
-      } else {
+    for (int i = 0; i < kLoads; ++i) {
+      if (i < iters) {                            // the same for the whole wave
+        const int e = min(lane + 64 * i, n - 1);
+        const int r = (int)(((uint32_t)e * m) >> 16), k = e - r * U;
+        v[0][i] = *reinterpret_cast<const uint32_t*>(p.sb + min(n0 + r, p.N - 1) * p.sb_ld + (u0 + k) * 4);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) c.sa[t].x = *reinterpret_cast<const uint32_t*>(psa[t] + u * 4);
-        c.sb.x = *reinterpret_cast<const uint32_t*>(psb + u * 4);
-        c.off = 0;
+        for (int t = 0; t < MT; ++t)
+          v[1 + t][i] = *reinterpret_cast<const uint32_t*>(
+              p.sa + min((int64_t)(32 * t + r), p.M - 1) * p.sa_ld + (u0 + k) * 4);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int e = lane + 64 * i;
+      if (i < iters && e < n) {
+        const int r = (int)(((uint32_t)e * m) >> 16), k = e - r * U;
+#pragma unroll
+        for (int t = 0; t <= MT; ++t) sreg[t * staged_tile<MT>() + r * staged_stride<MT>() + k] = v[t][i];
+      }
+    }
+  }
+
+  // STAGED: the scale words of unit u0 + k in fragment order
+  __device__ __forceinline__ void staged_words(int k, uint32_t (&sa)[MT], uint32_t& sb) const {
+    sb = sreg[fr * staged_stride<MT>() + k];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) sa[t] = sreg[(1 + t) * staged_tile<MT>() + fr * staged_stride<MT>() + k];
+  }
+
+  // Unit u into c.  PAIRED scale words go out first: the register copies the
+  // loop makes of them wait for their loads, and loads complete in order,
+  // so a wait for an early load leaves the later ones in flight.
+  __device__ __forceinline__ void load(int64_t u, SkinnyUnit<MT>& c, bool scales) const {
+    if (scales) {                                 // PAIRED only; K >= 256
+      const int64_t ps = min(u, units - 2);       // both words inside the row
+#pragma unroll
+      for (int t = 0; t < MT; ++t) c.sa[t] = *reinterpret_cast<const u32x2_a4*>(psa[t] + ps * 4);
+      c.sb = *reinterpret_cast<const u32x2_a4*>(psb + ps * 4);
+      c.off = u - ps;
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -644,9 +691,10 @@ struct Skinny {
   }
 };
 
-template <int MT, bool PAIRS>
+template <int MT, int SC>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSkinnyWaves * (1 + MT) * kSkinnyRegion];
+  __shared__ uint32_t slds[SC == kSkinnyStaged ? kSkinnyWaves * (1 + MT) * staged_tile<MT>() : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -654,8 +702,9 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
   const int64_t n0 = (int64_t)blockIdx.x * 32;
   const int64_t units = p.K / 128;
   const int64_t u0 = units * wave / kSkinnyWaves, u1 = units * (wave + 1) / kSkinnyWaves;
+  constexpr bool kPaired = SC == kSkinnyPaired;
 
-  const Skinny<MT, PAIRS> sk(p, wave, lane, n0, lds);
+  const Skinny<MT, SC> sk(p, wave, lane, n0, lds, slds);
   v16f acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = v16f{};
@@ -665,25 +714,35 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
     // alternate (c0 even units from u0, c1 odd); a load past the wave's range
     // reads its last unit again (a cache hit), so every iteration issues the
     // same loads and the compiler waits for exactly the set it is about to
-    // use.  With PAIRS, c0's scale load also brings c1's words.
+    // use.  PAIRED: c0's scale load also brings c1's words.  STAGED: the
+    // scale words are copied into LDS behind the first two units' loads.
     SkinnyUnit<MT> c0, c1;
-    sk.load(u0, c0, true);
-    sk.load(min(u0 + 1, u1 - 1), c1, !PAIRS);
+    sk.load(u0, c0, kPaired);
+    sk.load(min(u0 + 1, u1 - 1), c1, false);
+    if constexpr (!kPaired) sk.stage_scales(u0, (int)(u1 - u0));
     for (int64_t u = u0; u < u1; u += 2) {
       skinny_pin();
       uint32_t sa[MT], sb, sa1[MT], sb1;
+      if constexpr (kPaired) {
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        sa[t] = c0.off ? c0.sa[t].y : c0.sa[t].x;
-        sa1[t] = PAIRS ? c0.sa[t].y : c1.sa[t].x;
+        for (int t = 0; t < MT; ++t) {
+          sa[t] = c0.off ? c0.sa[t].y : c0.sa[t].x;
+          sa1[t] = c0.sa[t].y;
+        }
+        sb = c0.off ? c0.sb.y : c0.sb.x;
+        sb1 = c0.sb.y;
+      } else {
+        sk.staged_words((int)(u - u0), sa, sb);
+        sk.staged_words((int)(min(u + 1, u1 - 1) - u0), sa1, sb1);
       }
-      sb = c0.off ? c0.sb.y : c0.sb.x;
-      sb1 = PAIRS ? c0.sb.y : c1.sb.x;
-      sk.step(c0, sa, sb, min(u + 2, u1 - 1), true, ~0u, acc);
-      // unconditional, so that the compiler's wait counts are the same on
-      // every path; past the range (an odd count) it adds zero products
+      sk.step(c0, sa, sb, min(u + 2, u1 - 1), kPaired, ~0u, acc);
+      // Unconditional, so that the compiler's wait counts are the same on
+      // every path.  Past the range (an odd count) its B fragments are zero,
+      // and its A fragments and scale words come from inside the product
+      // (the wave's last unit, or the next unit's words), so it adds zeros,
+      // or a NaN that the exact result already holds.
       skinny_pin();
-      sk.step(c1, sa1, sb1, min(u + 3, u1 - 1), !PAIRS, u + 1 < u1 ? ~0u : 0u, acc);
+      sk.step(c1, sa1, sb1, min(u + 3, u1 - 1), false, u + 1 < u1 ? ~0u : 0u, acc);
     }
     skinny_pin();
   }
@@ -714,13 +773,19 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
   }
 }
 
-// paired scale loads need two units in K (K >= 256)
+// staged scale words when every wave's range fits the staging area (K up to
+// 16384 for one or two A tiles, 8192 for four), otherwise paired loads (which
+// need K >= 256, true whenever staging does not fit)
 template <int MT>
 void launch_skinny(const GemmParams& p, int64_t workgroups, hipStream_t s) {
-  if (p.K >= 256)
-    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, true>), dim3((uint32_t)workgroups), dim3(kSkinnyWaves * 64), 0, s, p);
+  const int64_t units = p.K / 128, per_wave = (units + kSkinnyWaves - 1) / kSkinnyWaves;
+  const bool staged = per_wave <= staged_units<MT>();
+  if (staged)
+    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, kSkinnyStaged>), dim3((uint32_t)workgroups),
+                       dim3(kSkinnyWaves * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, false>), dim3((uint32_t)workgroups), dim3(kSkinnyWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, kSkinnyPaired>), dim3((uint32_t)workgroups),
+                       dim3(kSkinnyWaves * 64), 0, s, p);
 }
 
 }  // namespace

@@ -144,9 +144,11 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
 
 @pytest.mark.parametrize("mnk", [(16, 7168, 7168), (1, 4096, 4096), (32, 1000, 384), (5, 96, 128),
                                  (31, 33, 640), (17, 2048, 1152),
-                                 # K = 256: two units, the smallest K with paired scale words
-                                 # (a wave's only unit may be the second word of its pair)
+                                 # K = 256: two units; a wave's only unit may be the second of two
                                  (8, 64, 256), (20, 300, 256), (40, 130, 256),
+                                 # scale words loaded in pairs instead of staged in LDS: more than
+                                 # 32 units per wave (one or two A tiles), more than 16 (four)
+                                 (16, 96, 16896), (40, 130, 16512), (100, 64, 8320),
                                  # two 32-row A tiles per workgroup
                                  (64, 7168, 7168), (48, 2048, 1024), (33, 100, 384), (64, 4096, 128),
                                  # four (64 < M <= 128 with K % 512 != 0)
