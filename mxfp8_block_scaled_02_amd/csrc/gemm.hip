@@ -512,8 +512,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
 // Measured on 16 x 7168 x 7168 with the weight read from HBM (rotating
 // copies): loading B straight into LDS (global_load_lds) and the A fragments
 // one per lane and row, one unit in flight, took 15.7 us; this register path
-// takes 13.3 us.  Reading B alone in the same pattern takes 8.9 us; most of
-// the rest goes to the scale-word loads, which touch one line per row.
+// takes 12.7 us (13.3 us with paired scale-word loads instead of staged
+// ones).  Reading B alone in the same pattern takes 8.9 us.
 
 constexpr int kSkinnyWaves = 4;
 constexpr int kSkinnyRegion = 32 * 128;   // one operand tile of one unit in LDS (4 KiB)
