@@ -149,6 +149,9 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
                                  # scale words loaded in pairs instead of staged in LDS: more than
                                  # 32 units per wave (one or two A tiles), more than 16 (four)
                                  (16, 96, 16896), (40, 130, 16512), (100, 64, 8320),
+                                 # K = 128: one unit, one active wave, staged words of one unit
+                                 # with two and four A tiles
+                                 (33, 64, 128), (100, 200, 128),
                                  # two 32-row A tiles per workgroup
                                  (64, 7168, 7168), (48, 2048, 1024), (33, 100, 384), (64, 4096, 128),
                                  # four (64 < M <= 128 with K % 512 != 0)
