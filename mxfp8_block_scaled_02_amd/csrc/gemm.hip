@@ -37,9 +37,9 @@
 // * tile128: 128 x 128 tiles (four waves of 64 x 64) staged through registers
 //   into padded LDS rows; it takes the problems with M > 128 that the ring
 //   tiles do not (K not a multiple of 512, scale pitches not multiples of 16).
-// * skinny (decode: M <= 64, or M <= 128 where the ring tiles do not apply):
-//   32 output columns per workgroup, K split over its waves, B streamed once
-//   through LDS (see the section below).
+// * skinny (decode and small batches, M <= 128): 32 output columns per
+//   workgroup, K split over its waves, B streamed once through LDS (see the
+//   section below).
 //
 // Rows of A or B past M or N read a valid row (the last one) and their
 // outputs are not stored.  K must be a multiple of 128, and the scale planes'
@@ -804,6 +804,11 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
     launch_skinny<1>(p, skinny, s);
   } else if (M <= 64) {
     launch_skinny<2>(p, skinny, s);
+  } else if (M <= 128) {
+    // four A tiles; with the weight read from HBM this beats the ring tiles
+    // (128 x 7168 x 7168: 28 us against 43 us for 64 x 128 tiles; K = 4096:
+    // 19 against 26 us; K = 16384: 66 against 88 us)
+    launch_skinny<4>(p, skinny, s);
   } else if (K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 && sb_pitch % 16 == 0) {
     // the ring tile with the least rounds of tiles over the CUs times the
     // time of one tile at full load, in eighths of a 256 x 256 tile's
@@ -826,8 +831,6 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
       case 2: hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<128, 128>), grid, dim3(kThreads), 0, s, p); break;
       default: hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<64, 128>), grid, dim3(kThreads), 0, s, p); break;
     }
-  } else if (M <= 128) {
-    launch_skinny<4>(p, skinny, s);
   } else {
     p.tiles_m = (int32_t)((M + kGT - 1) / kGT);
     p.tiles_n = (int32_t)((N + kGT - 1) / kGT);

@@ -154,9 +154,9 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
                                  (33, 64, 128), (100, 200, 128),
                                  # two 32-row A tiles per workgroup
                                  (64, 7168, 7168), (48, 2048, 1024), (33, 100, 384), (64, 4096, 128),
-                                 # four (64 < M <= 128 with K % 512 != 0)
+                                 # four 32-row A tiles (64 < M <= 128)
                                  (128, 7168, 7040), (97, 1000, 640), (65, 2048, 256),
-                                 # 64 < M <= 128 with K % 512 == 0: two rows of 64 x 128 ring tiles
+                                 # 64 < M <= 128 with K % 512 == 0: also four A tiles
                                  (128, 7168, 7168), (97, 3000, 2048), (65, 200, 512)])
 def test_gemm_skinny_decode(orc, mnk):
     """A few activation rows (decode): the K-split skinny path, including K
