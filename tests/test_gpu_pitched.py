@@ -124,7 +124,9 @@ def test_dequantize_from_padded_scales(axis):
 
 
 @pytest.mark.parametrize("mnk,pitch_multiple", [((4096, 4096, 512), 32), ((16, 2048, 1024), 36),
-                                                ((300, 500, 384), 16)])
+                                                ((300, 500, 384), 16),
+                                                # four A tiles: staged scale words, then paired
+                                                ((100, 1000, 1024), 20), ((96, 300, 16896), 36)])
 def test_gemm_reads_padded_scales(mnk, pitch_multiple):
     """The same kernel runs for compact and padded planes here, so the outputs
     agree bit for bit; the planes come from quantizing into padded buffers."""
