@@ -253,7 +253,7 @@ def bench_gemm(torch, mx, steps):
     dev = torch.device("cuda:0")
     T = Timed(torch, EAGER)
     res = {}
-    for M, N, K in ((8192, 8192, 8192), (1024, 7168, 7168), (16, 7168, 7168)):
+    for M, N, K in ((8192, 8192, 8192), (1024, 7168, 7168), (128, 7168, 7168), (16, 7168, 7168)):
         g = torch.Generator(device=dev).manual_seed(M + N + K)
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         b = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
@@ -271,7 +271,7 @@ def bench_gemm(torch, mx, steps):
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         rec = {"ms_per_launch": round(ms, 5), "TFLOP_s": round(tf, 1),
                "frac_mfma_fp8": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)}
-        if M <= 32:
+        if M <= 128:
             # a few rows against a large weight: bound by streaming the planes
             # of B (and A) once and writing the output
             alg = (M + N) * K * (1 + 1 / 32) + M * N * 2
