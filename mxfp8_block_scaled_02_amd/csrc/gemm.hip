@@ -385,11 +385,20 @@ constexpr int kGK = 128;              // K bytes per LDS tile
 constexpr int kLdsStride = kGK + 16;  // padded LDS row
 constexpr int kLdsTile = kGT * kLdsStride;
 
-__device__ __forceinline__ u32x4 ld_global(const uint8_t* base, int64_t rows, int64_t row,
-                                           int64_t K, int64_t k) {
-  return row < rows ? load16_cached(base + row * K + k) : u32x4{0, 0, 0, 0};
-}
+// One 128-deep k tile of a workgroup in registers: thread t holds 16-byte
+// chunks t + 256 u (u < 4) of the 128 x 128-byte A and B tiles (row
+// (t >> 3) + 32 u, k offset 16 (t & 7)), and the scale word (4 bytes: the 4
+// blocks of the k tile) of this lane's fragment row in each of the wave's two
+// 32-row tiles of A and of B.
+struct Tile128Regs {
+  u32x4 a[4], b[4];
+  uint32_t sa[2], sb[2];
+};
 
+// Two k tiles in flight: while one is in LDS and feeding the MFMAs, the next
+// two are loading into the two register sets.  Rows past M or N read the last
+// row (their outputs are not stored), so no load sits behind a condition and
+// the compiler waits only for the register set it is about to store.
 __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kLdsTile];   // [buffer][A, B]
   const int tid = threadIdx.x;
@@ -399,43 +408,43 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
   const int64_t m0 = (int64_t)(blockIdx.x / p.tiles_n) * kGT;
   const int64_t n0 = (int64_t)(blockIdx.x % p.tiles_n) * kGT;
   const int64_t K = p.K;
-
-  // global -> LDS: thread t moves 16-byte chunks t + 256 u (u < 4) of each
-  // 128 x 128-byte tile: row (t >> 3) + 32 u, k offset 16 (t & 7)
   const int lrow = tid >> 3, lk = (tid & 7) * 16;
-  u32x4 ra[4], rb[4];
-  auto fetch = [&](int64_t k0) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = ld_global(p.qa, p.M, m0 + lrow + 32 * u, K, k0 + lk);
-      rb[u] = ld_global(p.qb, p.N, n0 + lrow + 32 * u, K, k0 + lk);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<u32x4*>(&lds[buf][0][(lrow + 32 * u) * kLdsStride + lk]) = ra[u];
-      *reinterpret_cast<u32x4*>(&lds[buf][1][(lrow + 32 * u) * kLdsStride + lk]) = rb[u];
-    }
-  };
-
-  // this lane's operand rows in each of the wave's two 32-row tiles
   const int h = lane >> 5;
   const int fr = lane & 31;
-  int64_t arow[2], brow[2];
+
+  const uint8_t* ga[4];
+  const uint8_t* gb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ga[u] = p.qa + min(m0 + lrow + 32 * u, p.M - 1) * K + lk;
+    gb[u] = p.qb + min(n0 + lrow + 32 * u, p.N - 1) * K + lk;
+  }
+  const uint8_t* gsa[2];
+  const uint8_t* gsb[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    arow[i] = m0 + wm * 64 + 32 * i + fr;
-    brow[i] = n0 + wn * 64 + 32 * i + fr;
+    gsa[i] = p.sa + min(m0 + wm * 64 + 32 * i + fr, p.M - 1) * p.sa_ld;
+    gsb[i] = p.sb + min(n0 + wn * 64 + 32 * i + fr, p.N - 1) * p.sb_ld;
   }
-  // scale bytes of this lane for k tile k0: index [tile i][64-k step s]
-  auto scales = [&](const uint8_t* s, int64_t ld, const int64_t* rows, int64_t nrows, int64_t k0,
-                    uint32_t (&out)[2][2]) {
+  // k tile kt into c: the scale words first (their loop copies wait for them)
+  auto fetch = [&](int64_t kt, Tile128Regs& c) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      c.sa[i] = *reinterpret_cast<const uint32_t*>(gsa[i] + kt * 4);
+      c.sb[i] = *reinterpret_cast<const uint32_t*>(gsb[i] + kt * 4);
+    }
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-        out[i][st] = rows[i] < nrows ? s[rows[i] * ld + k0 / kBlock + 2 * st + h] : 127u;
+    for (int u = 0; u < 4; ++u) {
+      c.a[u] = load16_cached(ga[u] + kt * kGK);
+      c.b[u] = load16_cached(gb[u] + kt * kGK);
+    }
+  };
+  auto stash = [&](int buf, const Tile128Regs& c) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      *reinterpret_cast<u32x4*>(&lds[buf][0][(lrow + 32 * u) * kLdsStride + lk]) = c.a[u];
+      *reinterpret_cast<u32x4*>(&lds[buf][1][(lrow + 32 * u) * kLdsStride + lk]) = c.b[u];
+    }
   };
 
   v16f acc[2][2];
@@ -443,23 +452,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
-
-  uint32_t sa_cur[2][2], sb_cur[2][2], sa_nxt[2][2], sb_nxt[2][2];
-  fetch(0);
-  scales(p.sa, p.sa_ld, arow, p.M, 0, sa_cur);
-  scales(p.sb, p.sb_ld, brow, p.N, 0, sb_cur);
-  stash(0);
-  __syncthreads();
-
-  const int64_t ktiles = K / kGK;
-  for (int64_t kt = 0; kt < ktiles; ++kt) {
-    const int buf = (int)(kt & 1);
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      fetch((kt + 1) * kGK);
-      scales(p.sa, p.sa_ld, arow, p.M, (kt + 1) * kGK, sa_nxt);
-      scales(p.sb, p.sb_ld, brow, p.N, (kt + 1) * kGK, sb_nxt);
-    }
+  auto compute = [&](int buf, const uint32_t (&sa)[2], const uint32_t (&sb)[2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       v8i fa[2], fb[2];
@@ -470,24 +463,38 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
         fa[i] = frag(*reinterpret_cast<const u32x4*>(la), *reinterpret_cast<const u32x4*>(la + 32));
         fb[i] = frag(*reinterpret_cast<const u32x4*>(lb), *reinterpret_cast<const u32x4*>(lb + 32));
       }
+      const int sh = 16 * st + 8 * h;    // the scale byte of this lane's 32-k block
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j], sa_cur[i][st], sb_cur[j][st]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j], sa[i] >> sh, sb[j] >> sh);
     }
-    if (more) {
-      // the other buffer was last read in the previous iteration, which every
-      // wave finished before that iteration's barrier
-      stash(buf ^ 1);
-      __syncthreads();          // the next tile is in LDS
+  };
+
+  const int64_t ktiles = K / kGK;
+  Tile128Regs c0, c1;
+  fetch(0, c0);
+  fetch(min((int64_t)1, ktiles - 1), c1);
+  stash(0, c0);
+  uint32_t sa0[2] = {c0.sa[0], c0.sa[1]}, sb0[2] = {c0.sb[0], c0.sb[1]};
+  __syncthreads();
+  for (int64_t kt = 0; kt < ktiles; kt += 2) {
+    // tile kt is in lds[0] (its scales in sa0/sb0), tile kt + 1 loading in c1
+    fetch(min(kt + 2, ktiles - 1), c0);
+    compute(0, sa0, sb0);
+    stash(1, c1);
+    const uint32_t sa1[2] = {c1.sa[0], c1.sa[1]}, sb1[2] = {c1.sb[0], c1.sb[1]};
+    __syncthreads();
+    // tile kt + 1 (past the end for an odd count: skipped) is in lds[1]
+    fetch(min(kt + 3, ktiles - 1), c1);
+    if (kt + 1 < ktiles) compute(1, sa1, sb1);
+    stash(0, c0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          sa_cur[i][st] = sa_nxt[i][st];
-          sb_cur[i][st] = sb_nxt[i][st];
-        }
+    for (int i = 0; i < 2; ++i) {
+      sa0[i] = c0.sa[i];
+      sb0[i] = c0.sb[i];
     }
+    __syncthreads();
   }
 
 #pragma unroll
