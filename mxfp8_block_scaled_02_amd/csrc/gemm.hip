@@ -19,7 +19,7 @@
 //
 // Three kinds of tiling share that fragment layout:
 //
-// * ring tiles (K % 512 == 0, scale pitches multiples of 16): a workgroup of
+// * ring tiles (M > 128, K >= 512): a workgroup of
 //   four waves (2 x 2) computes a 256 x 256, 128 x 256, 128 x 128 or 64 x 128
 //   tile, one workgroup per CU.  K advances in stages of 64 bytes through a ring of four
 //   LDS slots that the loads fill directly (global_load_lds_dwordx4, no
@@ -27,7 +27,9 @@
 //   computes, and the fragments of stage s + 1 are read into a second
 //   register set meanwhile, so a stage waits only for data requested three
 //   stages earlier.  Scales travel the same way, 16 bytes (512 k) per row and
-//   operand every eight stages.  Waits count the loads still allowed in
+//   operand every eight stages; with K % 512 != 0 the last eight stages start
+//   with repeats of the stage before, whose scale bytes are set to 0, so that
+//   the group is a whole one.  Waits count the loads still allowed in
 //   flight (s_waitcnt vmcnt(n)) instead of draining them all at each barrier.
 //   Workgroups are mapped to tiles so that each XCD works on a compact block
 //   of the output (its L2 holds the shared panels), and XCD pairs start K at
@@ -35,16 +37,15 @@
 //   the 256 CUs take least time: large tiles move fewer bytes per MFMA, small
 //   ones keep more CUs busy when M or N is small.
 // * tile128: 128 x 128 tiles (four waves of 64 x 64) staged through registers
-//   into padded LDS rows; it takes the problems with M > 128 that the ring
-//   tiles do not (K not a multiple of 512, scale pitches not multiples of 16).
+//   into padded LDS rows; it takes the problems with M > 128 and K < 512.
 // * skinny (decode and small batches, M <= 128): 32 output columns per
 //   workgroup, K split over its waves, B streamed once through LDS (see the
 //   section below).
 //
 // Rows of A or B past M or N read a valid row (the last one) and their
 // outputs are not stored.  K must be a multiple of 128, and the scale planes'
-// rows are a caller-given pitch apart (a multiple of 4; the ring tiles also
-// want a multiple of 16, as compact planes with K % 512 == 0 have).  The
+// rows are a caller-given pitch apart (a multiple of 4: the ring tiles' 16-byte
+// scale loads into LDS need only 4-byte aligned addresses).  The
 // order in which the 64-deep MFMA steps accumulate depends on the tiling and,
 // for the ring tiles, on the tile's starting quarter; every order stays
 // within the tolerance that the tests derive for the instruction.
@@ -181,6 +182,8 @@ struct TileRing {
   int wave, lane, fr, h;
   int64_t m0, n0, K, stages;
   int64_t kstart;               // first stage of this tile (K order rotated per tile)
+  int vstages;                  // stages run: K / 64 rounded up to whole groups of 8
+  int dead;                     // stages of the last group past K (0 if K % 512 == 0)
   int swz;                      // row_swizzle of this lane's fragment rows
   int arow, brow;               // LDS byte offset of this lane's row in tile 0
   v16f acc[MI][NJ];
@@ -193,6 +196,8 @@ struct TileRing {
     h = lane >> 5;
     K = p.K;
     stages = K / kBK;
+    vstages = (int)((stages + kGroup - 1) / kGroup * kGroup);
+    dead = vstages - (int)stages;
     swz = row_swizzle(fr);
     arow = ((wave >> 1) * (BM / 2) + fr) * kBK;
     brow = ((wave & 1) * (BN / 2) + fr) * kBK;
@@ -208,16 +213,21 @@ struct TileRing {
   // loads of stage t into ring slot t % 4 (stages past the end reload the
   // last one, into a slot nobody reads again); a stage that opens a scale
   // group also brings that group's scales (each wave 64 rows of A and of B:
-  // rows past the tile are loaded and never read)
+  // rows past the tile are loaded and never read).
+  // With K % 512 != 0 the last group is run whole: its first `dead` stages
+  // reload the last stage of the group before (and take scale bytes 0, see
+  // read_scales), its others take the remaining K, and its scales are the
+  // row's last 16 bytes, so that every stage keeps its position in a group.
   template <int SLOT, bool GROUP_START>
   __device__ __forceinline__ void issue(int64_t t) {
-    int64_t tt = t < stages ? t : stages - 1;
-    tt += kstart;
-    if (tt >= stages) tt -= stages;
-    load_stage<BM>(p.qa, p.M, m0, K, tt * kBK, sa_slot<SLOT>(), wave, lane);
-    load_stage<BN>(p.qb, p.N, n0, K, tt * kBK, sb_slot<SLOT>(), wave, lane);
+    int tt = (int)t < vstages ? (int)t : vstages - 1;
+    tt += (int)kstart;
+    if (tt >= vstages) tt -= vstages;
+    const int kt = max(tt - dead, min(tt, (dead ? vstages - kGroup : vstages) - 1));
+    load_stage<BM>(p.qa, p.M, m0, K, (int64_t)kt * kBK, sa_slot<SLOT>(), wave, lane);
+    load_stage<BN>(p.qb, p.N, n0, K, (int64_t)kt * kBK, sb_slot<SLOT>(), wave, lane);
     if (GROUP_START) {
-      const int64_t kb0 = (tt / kGroup) * 16;
+      const int64_t kb0 = min((tt / kGroup) * 16, (int)(K / kBlock) - 16);
       const int gpar = (int)((t / kGroup) & 1);
       uint8_t* sc = gpar ? s_scale1 : s_scale0;
       load_scales(p.sa, p.M, m0, p.sa_ld, kb0, sc, wave, lane);
@@ -243,8 +253,12 @@ struct TileRing {
     }
   }
 
+  // scale group GP into registers.  Words below zw (the dead stages of a
+  // short last group, two stages a word) become 0: those stages' products,
+  // scaled by 2^-254, round to zero, and a NaN among them is one that the
+  // stage they repeat has already added.
   template <int GP>
-  __device__ __forceinline__ void read_scales() {
+  __device__ __forceinline__ void read_scales(int zw) {
     const uint8_t* la = GP ? s_scale1 : s_scale0;
     const uint8_t* lb = la + kScBytes;
 #pragma unroll
@@ -253,6 +267,13 @@ struct TileRing {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       scb[GP][j] = *reinterpret_cast<const u32x4*>(lb + 16 * ((wave & 1) * (BN / 2) + 32 * j + fr));
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) sca[GP][i][k] = k < zw ? 0u : sca[GP][i][k];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) scb[GP][j][k] = k < zw ? 0u : scb[GP][j][k];
+    }
   }
 
   // the MI x NJ MFMAs of a stage at position POS of its scale group
@@ -277,7 +298,7 @@ struct TileRing {
     ring_barrier<kAfter>();     // stage s+1 is in LDS; every read of stage s has returned
     issue<(POS + 4) % kStages, ((POS + 4) % kGroup) == 0>(s + 4);
     read_frags<(POS + 1) % kStages, (POS + 1) & 1>();
-    if (POS == kGroup - 1) read_scales<GP ^ 1>();
+    if (POS == kGroup - 1) read_scales<GP ^ 1>((int)s + 1 == vstages - kGroup ? dead >> 1 : 0);
     mma<POS & 1, GP, POS>();
     // order: reads first, then the MFMAs with the loads between them
     constexpr int kReads = 2 * (MI + NJ), kMfma = MI * NJ;
@@ -312,15 +333,15 @@ struct TileRing {
     issue<3, false>(3);
     ring_barrier<3 * kLoads>(); // stage 0 and scale group 0 have landed
     read_frags<0, 0>();
-    read_scales<0>();
-    // stages come in groups of 8 (K % 512 == 0); two groups per trip so that
-    // the scale buffers are named statically
+    read_scales<0>(0);          // K >= 512: the first group is whole
+    // stages come in groups of 8, two groups per trip so that the scale
+    // buffers are named statically
     int64_t s = 0;
-    for (; s + 2 * kGroup <= stages; s += 2 * kGroup) {
+    for (; s + 2 * kGroup <= vstages; s += 2 * kGroup) {
       group<0>(s);
       group<1>(s + kGroup);
     }
-    if (s < stages) group<0>(s);
+    if (s < vstages) group<0>(s);
     wait_loads<0>();            // no load may land after the workgroup ends
   }
 };
@@ -348,7 +369,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const GemmPar
   // concurrent tiles on different XCDs do not stream the same K columns,
   // whose rows sit a power-of-two stride apart, at the same time
   const int64_t ngroups = p.K / (kBK * kGroup);
-  const int64_t ks = ((int64_t)((xcd / 2) % 4) * ngroups / 4) * kGroup;
+  // (not with K % 512 != 0: the short group has to come last)
+  const int64_t ks = p.K % (kBK * kGroup) ? 0 : ((int64_t)((xcd / 2) % 4) * ngroups / 4) * kGroup;
   TileRing<BM, BN> t(p, m0, n0, wave, lane, ks);
   t.run();
 
@@ -816,7 +838,7 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
     // (128 x 7168 x 7168: 28 us against 43 us for 64 x 128 tiles; K = 4096:
     // 19 against 26 us; K = 16384: 66 against 88 us)
     launch_skinny<4>(p, skinny, s);
-  } else if (K % (kBK * kGroup) == 0 && sa_pitch % 16 == 0 && sb_pitch % 16 == 0) {
+  } else if (K >= kBK * kGroup) {
     // the ring tile with the least rounds of tiles over the CUs times the
     // time of one tile at full load, in eighths of a 256 x 256 tile's
     // (measured on 8192^3: 128 x 256 takes 5, 128 x 128 3 and 64 x 128 2)

@@ -104,6 +104,20 @@ def test_gemm_nan_elements(orc):
     run(orc, qa, sa, qb, sb, "NaN elements")
 
 
+def test_gemm_nan_in_short_last_group(orc):
+    """K = 640 on the ring tiles: the last group's first six stages repeat
+    k 448..511 with scale bytes 0.  NaN data and NaN scales in the repeated
+    stage and in the live part of the short group give NaN exactly where the
+    oracle's product has it."""
+    qa, sa = quantized(256, 640, 1.0, seed=12)
+    qb, sb = quantized(320, 640, 0.05, seed=13)
+    qa[5, 460] = 0x7F                                     # NaN element in the repeated stage
+    qb[9, 600] = 0xFF                                     # NaN element past k 512
+    sa[4, 14] = 0xFF                                      # NaN scale of k 448..479
+    sb[7, 19] = 0xFF                                      # NaN scale of the last block
+    run(orc, qa, sa, qb, sb, "NaN in the short last group")
+
+
 def test_gemm_nan_scale(orc):
     qa, sa = quantized(128, 256, 1.0, seed=10)
     qb, sb = quantized(128, 256, 0.05, seed=11)
@@ -122,8 +136,12 @@ def test_gemm_nan_scale(orc):
     (500, 7000, 1024), (400, 6000, 512),
     # 64 x 128 tiles (few tiles in all):
     (300, 2048, 4096), (129, 1000, 512), (200, 300, 1024),
-    # K % 512 != 0: the register-staged 128 x 128 tiling, odd 128-deep stage counts
-    (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (4352, 3840, 640)])
+    # K % 512 != 0 with K >= 512: the ring tiles' short last group, whose first
+    # 2, 4 or 6 stages repeat the stage before with scales 0, on each tile size
+    (4352, 3840, 640), (4096, 4096 + 256, 896), (500, 7000, 768), (129, 1000, 1152),
+    (300, 2048, 11008), (2000, 1000, 4224),
+    # K < 512: the register-staged 128 x 128 tiling, odd 128-deep stage counts
+    (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (300, 500, 256)])
 def test_gemm_large_tiles_ragged_sampled(orc, mnk):
     """Large problems: sampled outputs, every column of the last row and every
     row of the last column."""

@@ -145,16 +145,19 @@ def test_gemm_reads_padded_scales(mnk, pitch_multiple):
     assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
 
 
-def test_gemm_padded_scales_other_tiling(orc):
-    """A pitch that is a multiple of 4 but not of 16 moves a large product to
-    the 128 x 128 tiling: checked against the oracle at sampled positions."""
-    M, N, K = 4096, 4096, 512
-    say("gemm padded pitch 20")
+@pytest.mark.parametrize("mnk,pitch", [((4096, 4096, 512), 20), ((4100, 1000, 640), 24),
+                                       ((300, 2000, 1152), 40)])
+def test_gemm_padded_scales_large(orc, mnk, pitch):
+    """A pitch that is a multiple of 4 but not of 16 puts the ring tiles' 16-byte
+    scale loads at 4-byte aligned addresses, also where K % 512 != 0 shifts the
+    last group's load back: checked against the oracle at sampled positions."""
+    M, N, K = mnk
+    say("gemm padded", mnk, "pitch", pitch)
     a = bf16_input(M, K, seed=11)
     b = (bf16_input(N, K, seed=12) * 0.05).to(torch.bfloat16)
     pa, pb = mx.quantize(a, True, False), mx.quantize(b, True, False)
-    _, sav = padded(M, K, mx.ROWWISE, 1, 20)
-    _, sbv = padded(N, K, mx.ROWWISE, 1, 20)
+    _, sav = padded(M, K, mx.ROWWISE, 1, pitch)
+    _, sbv = padded(N, K, mx.ROWWISE, 1, pitch)
     sav.copy_(pa.rowwise_scale)
     sbv.copy_(pb.rowwise_scale)
     got = mx.gemm(pa.rowwise_data, sav, pb.rowwise_data, sbv, torch.float32)
