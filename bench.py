@@ -253,7 +253,9 @@ def bench_gemm(torch, mx, steps):
     dev = torch.device("cuda:0")
     T = Timed(torch, EAGER)
     res = {}
-    for M, N, K in ((8192, 8192, 8192), (1024, 7168, 7168), (128, 7168, 7168), (16, 7168, 7168)):
+    # 4096 x 4096 x 11008: an MLP down projection, K not a multiple of 512
+    for M, N, K in ((8192, 8192, 8192), (1024, 7168, 7168), (4096, 4096, 11008), (128, 7168, 7168),
+                    (16, 7168, 7168)):
         g = torch.Generator(device=dev).manual_seed(M + N + K)
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         b = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
