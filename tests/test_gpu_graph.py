@@ -49,6 +49,58 @@ def test_graph_replays_match_eager():
         assert np.array_equal(host(deq.view(torch.int32)), host(wd.view(torch.int32)))
 
 
+def test_graph_replays_match_eager_f32_grouped_and_gemm():
+    """float32 input, a grouped call and the activation quantize followed by
+    the matrix product (skinny kernel, and ring tiles with a short last scale
+    group), captured together; both products are deterministic, so every
+    replay must equal the eager calls bit for bit."""
+    print("[case] graph: quantize f32 [128, 512], grouped [64, 256] [96, 1024] [32, 544], "
+          "quantize + gemm 40x300x1024 and 300x512x640", flush=True)
+    xf = synth.weight_with_outliers(128, 512, seed=51).to(DEV).float()
+    xs = [synth.weight_with_outliers(r, c, seed=52 + i).to(DEV)
+          for i, (r, c) in enumerate([(64, 256), (96, 1024), (32, 544)])]
+    a1 = synth.weight_with_outliers(40, 1024, seed=56).to(DEV)
+    a2 = synth.weight_with_outliers(300, 640, seed=57).to(DEV)
+    b1 = mx.quantize(synth.weight_with_outliers(300, 1024, seed=58).to(DEV), True, False)
+    b2 = mx.quantize(synth.weight_with_outliers(512, 640, seed=59).to(DEV), True, False)
+    pf = mx.quantize(xf, True, True)
+    pg = mx.quantize_grouped(xs, True, True)
+    pa1, pa2 = mx.quantize(a1, True, False), mx.quantize(a2, True, False)
+    c1 = mx.gemm(pa1.rowwise_data, pa1.rowwise_scale, b1.rowwise_data, b1.rowwise_scale, torch.float32)
+    c2 = mx.gemm(pa2.rowwise_data, pa2.rowwise_scale, b2.rowwise_data, b2.rowwise_scale, torch.bfloat16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mx.quantize(xf, True, True, out=pf)
+        mx.quantize_grouped(xs, True, True, outs=pg)
+        mx.quantize(a1, True, False, out=pa1)
+        mx.quantize(a2, True, False, out=pa2)
+        mx.gemm(pa1.rowwise_data, pa1.rowwise_scale, b1.rowwise_data, b1.rowwise_scale, torch.float32, out=c1)
+        mx.gemm(pa2.rowwise_data, pa2.rowwise_scale, b2.rowwise_data, b2.rowwise_scale, torch.bfloat16, out=c2)
+    for rep in range(4):
+        # eager work between replays: new inputs, written in place
+        xf.mul_(-1.25)
+        for x in xs:
+            x.copy_((x.float() * 1.5).to(torch.bfloat16))
+        a1.copy_(synth.weight_with_outliers(40, 1024, seed=200 + rep).to(DEV))
+        a2.copy_(synth.weight_with_outliers(300, 640, seed=300 + rep).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        wf = mx.quantize(xf.clone(), True, True)
+        wg = mx.quantize_grouped([x.clone() for x in xs], True, True)
+        w1, w2 = mx.quantize(a1.clone(), True, False), mx.quantize(a2.clone(), True, False)
+        d1 = mx.gemm(w1.rowwise_data, w1.rowwise_scale, b1.rowwise_data, b1.rowwise_scale, torch.float32)
+        d2 = mx.gemm(w2.rowwise_data, w2.rowwise_scale, b2.rowwise_data, b2.rowwise_scale, torch.bfloat16)
+        torch.cuda.synchronize()
+        for got, want in [(pf, wf)] + list(zip(pg, wg)) + [(pa1, w1), (pa2, w2)]:
+            for a, b in zip(got, want):
+                if a is not None or b is not None:
+                    assert np.array_equal(host(a), host(b)), "replay %d: planes differ" % rep
+        assert np.array_equal(host(c1.view(torch.int32)), host(d1.view(torch.int32))), "replay %d: skinny" % rep
+        assert np.array_equal(host(c2.view(torch.int16)), host(d2.view(torch.int16))), "replay %d: ring" % rep
+
+
 def test_calls_run_on_the_current_stream():
     """Every entry point launches on the caller's current stream: on a side
     stream held up by a long sleep, then given a new input, each result must
