@@ -378,7 +378,31 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const GemmPar
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, fr = lane & 31;
   const int64_t r0 = m0 + wm * (BM / 2), c0 = n0 + wn * (BN / 2) + fr;
-  if (m0 + BM <= p.M && n0 + BN <= p.N) {
+  if (m0 + BM <= p.M && n0 + BN <= p.N && p.out_bf16 && (p.N & 1) == 0) {
+    // a full tile with bf16 output, written as whole 128-byte row segments:
+    // lane fr packs its values of tiles j and j + 1 (columns fr and 32 + fr)
+    // into one dword, and lane d then takes columns 2d and 2d + 1 of that
+    // 64-column span from lanes 2d and 2d + 1 (mod 32, same half h), so 32
+    // lanes store one row's 128 bytes.  Storing each lane's own column
+    // instead leaves half lines, which cost several times the bytes' HBM time.
+    const int d = fr;
+    const int src0 = 4 * (((2 * d) & 31) + 32 * h), src1 = src0 + 4;
+    const uint32_t sel = d < 16 ? 0x05040100u : 0x07060302u;   // low or high halves
+    uint16_t* o = reinterpret_cast<uint16_t*>(p.out);
+    const int64_t cw = n0 + wn * (BN / 2) + 2 * d;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int jp = 0; jp < NJ / 2; ++jp)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ab = (int)pack_bf16x2(t.acc[i][2 * jp][r], t.acc[i][2 * jp + 1][r]);
+          const uint32_t x0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, ab);
+          const uint32_t x1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, ab);
+          const int64_t row = r0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
+          *reinterpret_cast<uint32_t*>(o + row * p.N + cw + 64 * jp) = __builtin_amdgcn_perm(x1, x0, sel);
+        }
+  } else if (m0 + BM <= p.M && n0 + BN <= p.N) {
     // a full tile: no bounds to check
 #pragma unroll
     for (int i = 0; i < MI; ++i)

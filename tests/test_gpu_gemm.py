@@ -160,6 +160,27 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
         check_close(got, C, mag, dtype == torch.bfloat16, "large tiles %s" % ((M, N, K),))
 
 
+@pytest.mark.parametrize("mnk", [(256, 256, 512), (4352, 3840, 640), (4096, 4096 + 256, 1024), (500, 7000, 768),
+                                 (129, 1000, 1152), (512, 1030, 512), (300, 2047, 640), (260, 130, 128),
+                                 (40, 300, 1024)])
+def test_gemm_bf16_output_is_rounded_f32_output(mnk):
+    """The bf16 output equals the float32 output of the same call rounded to
+    nearest even, element for element.  Full ring tiles with an even N store
+    bf16 through a lane exchange (whole 128-byte row segments); N not a
+    multiple of 64, odd N, partial tiles, tile128 and skinny take the other
+    stores."""
+    M, N, K = mnk
+    qa, sa = quantized(M, K, 1.0, seed=M + 17 * K)
+    qb, sb = quantized(N, K, 0.05, seed=N + 19 * K)
+    say("gemm bf16 vs rounded f32", (M, N, K))
+    f = mx.gemm(qa, sa, qb, sb, torch.float32)
+    b = mx.gemm(qa, sa, qb, sb, torch.bfloat16)
+    torch.cuda.synchronize()
+    want = f.to(torch.bfloat16)
+    bad = int((b.view(torch.int16) != want.view(torch.int16)).sum())
+    assert bad == 0, "%d of %d bf16 outputs differ from the rounded float32 output" % (bad, M * N)
+
+
 @pytest.mark.parametrize("mnk", [(16, 7168, 7168), (1, 4096, 4096), (32, 1000, 384), (5, 96, 128),
                                  (31, 33, 640), (17, 2048, 1152),
                                  # K = 256: two units; a wave's only unit may be the second of two
