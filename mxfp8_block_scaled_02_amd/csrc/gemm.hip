@@ -95,6 +95,30 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v16f& acc,
   }
 }
 
+// bf16 output of two 32 x 32 tiles side by side (columns col .. col + 63,
+// rows row0 + 8 (r / 4) + 4 h + r % 4; the tiles and their columns lie inside
+// the output and N is even), written as whole 128-byte row segments.  Lane fr
+// packs its values of the two tiles (columns fr and 32 + fr) into one dword;
+// lane d then takes columns 2d and 2d + 1 from lanes 2d and 2d + 1 (mod 32,
+// same half h), so 32 lanes store one row's 128 bytes.  Storing each lane's
+// own column instead leaves half lines, which cost several times the bytes'
+// HBM time; the nontemporal hint, as for float32 output, saves a little more.
+__device__ __forceinline__ void store_bf16_pair(const GemmParams& p, const v16f& lo, const v16f& hi,
+                                                int64_t row0, int64_t col, int fr, int h) {
+  const int src0 = 4 * (((2 * fr) & 31) + 32 * h), src1 = src0 + 4;
+  const uint32_t sel = fr < 16 ? 0x05040100u : 0x07060302u;   // low or high halves
+  uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + col + 2 * fr;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ab = (int)pack_bf16x2(lo[r], hi[r]);
+    const uint32_t x0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, ab);
+    const uint32_t x1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, ab);
+    const int64_t row = row0 + 8 * (r / 4) + 4 * h + (r % 4);
+    __builtin_nontemporal_store(__builtin_amdgcn_perm(x1, x0, sel),
+                                reinterpret_cast<uint32_t*>(o + row * p.N));
+  }
+}
+
 // ---- ring tiles (256 x 256, 128 x 256, 128 x 128, 64 x 128) ---------------
 
 constexpr int kBT = 256;                // largest workgroup tile side
@@ -379,29 +403,13 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const GemmPar
   const int h = lane >> 5, fr = lane & 31;
   const int64_t r0 = m0 + wm * (BM / 2), c0 = n0 + wn * (BN / 2) + fr;
   if (m0 + BM <= p.M && n0 + BN <= p.N && p.out_bf16 && (p.N & 1) == 0) {
-    // a full tile with bf16 output, written as whole 128-byte row segments:
-    // lane fr packs its values of tiles j and j + 1 (columns fr and 32 + fr)
-    // into one dword, and lane d then takes columns 2d and 2d + 1 of that
-    // 64-column span from lanes 2d and 2d + 1 (mod 32, same half h), so 32
-    // lanes store one row's 128 bytes.  Storing each lane's own column
-    // instead leaves half lines, which cost several times the bytes' HBM time.
-    const int d = fr;
-    const int src0 = 4 * (((2 * d) & 31) + 32 * h), src1 = src0 + 4;
-    const uint32_t sel = d < 16 ? 0x05040100u : 0x07060302u;   // low or high halves
-    uint16_t* o = reinterpret_cast<uint16_t*>(p.out);
-    const int64_t cw = n0 + wn * (BN / 2) + 2 * d;
+    // a full tile with bf16 output: whole row segments
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int jp = 0; jp < NJ / 2; ++jp)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ab = (int)pack_bf16x2(t.acc[i][2 * jp][r], t.acc[i][2 * jp + 1][r]);
-          const uint32_t x0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, ab);
-          const uint32_t x1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, ab);
-          const int64_t row = r0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4);
-          *reinterpret_cast<uint32_t*>(o + row * p.N + cw + 64 * jp) = __builtin_amdgcn_perm(x1, x0, sel);
-        }
+        store_bf16_pair(p, t.acc[i][2 * jp], t.acc[i][2 * jp + 1], r0 + 32 * i, n0 + wn * (BN / 2) + 64 * jp,
+                        fr, h);
   } else if (m0 + BM <= p.M && n0 + BN <= p.N) {
     // a full tile: no bounds to check
 #pragma unroll
@@ -543,6 +551,11 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
     __syncthreads();
   }
 
+  if (m0 + kGT <= p.M && n0 + kGT <= p.N && p.out_bf16 && (p.N & 1) == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) store_bf16_pair(p, acc[i][0], acc[i][1], m0 + wm * 64 + 32 * i, n0 + wn * 64, fr, h);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
