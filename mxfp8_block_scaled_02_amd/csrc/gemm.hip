@@ -96,13 +96,15 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v16f& acc,
 }
 
 // bf16 output of two 32 x 32 tiles side by side (columns col .. col + 63,
-// rows row0 + 8 (r / 4) + 4 h + r % 4; the tiles and their columns lie inside
-// the output and N is even), written as whole 128-byte row segments.  Lane fr
+// rows row0 + 8 (r / 4) + 4 h + r % 4; the columns lie inside the output and
+// N is even; ROWS_IN says every row lies inside too, else rows past M are
+// skipped), written as whole 128-byte row segments.  Lane fr
 // packs its values of the two tiles (columns fr and 32 + fr) into one dword;
 // lane d then takes columns 2d and 2d + 1 from lanes 2d and 2d + 1 (mod 32,
 // same half h), so 32 lanes store one row's 128 bytes.  Storing each lane's
 // own column instead leaves half lines, which cost several times the bytes'
 // HBM time; the nontemporal hint, as for float32 output, saves a little more.
+template <bool ROWS_IN = true>
 __device__ __forceinline__ void store_bf16_pair(const GemmParams& p, const v16f& lo, const v16f& hi,
                                                 int64_t row0, int64_t col, int fr, int h) {
   const int src0 = 4 * (((2 * fr) & 31) + 32 * h), src1 = src0 + 4;
@@ -114,8 +116,9 @@ __device__ __forceinline__ void store_bf16_pair(const GemmParams& p, const v16f&
     const uint32_t x0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, ab);
     const uint32_t x1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, ab);
     const int64_t row = row0 + 8 * (r / 4) + 4 * h + (r % 4);
-    __builtin_nontemporal_store(__builtin_amdgcn_perm(x1, x0, sel),
-                                reinterpret_cast<uint32_t*>(o + row * p.N));
+    if (ROWS_IN || row < p.M)
+      __builtin_nontemporal_store(__builtin_amdgcn_perm(x1, x0, sel),
+                                  reinterpret_cast<uint32_t*>(o + row * p.N));
   }
 }
 
@@ -554,6 +557,14 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
   if (m0 + kGT <= p.M && n0 + kGT <= p.N && p.out_bf16 && (p.N & 1) == 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) store_bf16_pair(p, acc[i][0], acc[i][1], m0 + wm * 64 + 32 * i, n0 + wn * 64, fr, h);
+    return;
+  }
+  if (p.out_bf16 && (p.N & 1) == 0 && n0 + wn * 64 + 64 <= p.N) {
+    // a partial tile whose wave columns lie inside N: rows past M skipped
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (m0 + wm * 64 + 32 * i < p.M)
+        store_bf16_pair<false>(p, acc[i][0], acc[i][1], m0 + wm * 64 + 32 * i, n0 + wn * 64, fr, h);
     return;
   }
 #pragma unroll

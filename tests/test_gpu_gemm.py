@@ -162,13 +162,14 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
 
 @pytest.mark.parametrize("mnk", [(256, 256, 512), (4352, 3840, 640), (4096, 4096 + 256, 1024), (500, 7000, 768),
                                  (129, 1000, 1152), (512, 1030, 512), (300, 2047, 640), (260, 130, 128),
-                                 (40, 300, 1024), (256, 384, 256), (384, 1152, 384), (4096, 4096, 128)])
+                                 (40, 300, 1024), (256, 384, 256), (384, 1152, 384), (4096, 4096, 128),
+                                 (1000, 4096, 384)])
 def test_gemm_bf16_output_is_rounded_f32_output(mnk):
     """The bf16 output equals the float32 output of the same call rounded to
     nearest even, element for element.  Full ring tiles with an even N store
     bf16 through a lane exchange (whole 128-byte row segments); N not a
-    multiple of 64 and full tile128 tiles take the same path; odd N, partial
-    tiles and skinny take the other stores."""
+    multiple of 64 and tile128 tiles (rows past M skipped) take the same path;
+    odd N, partial ring tiles and skinny take the other stores."""
     M, N, K = mnk
     qa, sa = quantized(M, K, 1.0, seed=M + 17 * K)
     qb, sb = quantized(N, K, 0.05, seed=N + 19 * K)
