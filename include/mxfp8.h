@@ -137,13 +137,32 @@ mxfp8_status mxfp8_quantize_f32(const void *x, int64_t rows, int64_t cols,
  *   normed[r, c] = bf16( x[r, c] / sqrt(mean_c(x[r, :]^2) + eps)
  *                        * (gamma[c] + weight_offset) )
  *
- * accumulated in float32 and rounded once to bf16; (q_row, s_row) is then
- * exactly mxfp8_quantize's rowwise plane of those normed bf16 values (the
- * page's execute: the quantize reads the same bf16 that lands in
- * outputs_normed, so it is byte-identical to a standalone quantize).
+ * rounded once to bf16 (nearest even); (q_row, s_row) is then exactly
+ * mxfp8_quantize's rowwise plane of those normed bf16 values (the page's
+ * execute: the quantize reads the same bf16 that lands in outputs_normed, so
+ * it is byte-identical to a standalone quantize).
  *
  *   x, normed  bf16 [rows, cols]     gamma  bf16 [cols]
  *   q_row      uint8 [rows, cols]    s_row  uint8 [rows, cols/32]
+ *
+ * Precision and range.  sum_c x[r, c]^2 is accumulated in float32 when that
+ * sum lies in [2^-60, 2^120], and otherwise again in float64, where the
+ * square of every bf16 value is exact and no row sum can overflow or
+ * underflow; rstd = 1 / sqrt(sum / cols + eps) is then within a few float32
+ * roundings of exact.  The product x * rstd * (gamma + weight_offset) is
+ * taken in float32 (gamma + weight_offset is one float32 addition).  Every finite bf16 row, from
+ * subnormals to the largest finite values, with any finite eps >= 0, gives
+ * normed values within one bf16 rounding (plus a few float32 roundings) of
+ * the exact formula.  Rows the formula leaves undefined follow IEEE
+ * arithmetic:
+ *   - a row of zeros with eps == 0 is 0 / 0: every normed value is NaN, so
+ *     every scale byte of the row is 0xFF and every element byte sign | 0x7F;
+ *     with eps > 0 a row of zeros gives zeros (with x's sign);
+ *   - a row holding +-Inf and no NaN has rstd = 0: its finite values give
+ *     +-0, its infinities NaN;
+ *   - a row holding a NaN is NaN everywhere.
+ * The sign bit of a NaN produced this way is not specified.  A result whose
+ * magnitude exceeds bf16's range (a huge gamma) is +-Inf.
  *
  * All pointers are required; cols % 32 == 0; eps must be finite and >= 0.
  */

@@ -294,7 +294,8 @@ def _norm_desc(x, gamma, weight_offset, eps, out):
 
 def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, weight_offset: float = 0.0,
                      eps: float = 1e-6, out=None):
-    """RMSNorm in float32 rounded once to bf16, then its rowwise MXFP8 plane.
+    """RMSNorm (sum of squares and rstd in float64, the products in float32)
+    rounded once to bf16, then its rowwise MXFP8 plane.
 
     Returns (normed bf16 [rows, cols], data uint8 [rows, cols], scales uint8
     [rows, cols/32]); the bytes equal ``quantize(normed)``."""

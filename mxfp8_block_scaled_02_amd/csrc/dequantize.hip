@@ -47,8 +47,8 @@ __device__ void deq_flat_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int6
   for (int u = 0; u < kDeqUnroll; ++u) {
     const int64_t p = base + u * kWave;
     const bool ok = p < nunits;
-    q[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(d.q) + p) : 0u;
-    s[u] = ok ? d.s[pitched_block(p >> 3, d.cols >> 5, s_pitch)] : 0u;   // 8 units per block
+    q[u] = ok ? load4(reinterpret_cast<const uint32_t*>(d.q) + p) : 0u;
+    s[u] = ok ? load1_cached(d.s + pitched_block(p >> 3, d.cols >> 5, s_pitch)) : 0u;   // 8 units per block
   }
 #pragma unroll
   for (int u = 0; u < kDeqUnroll; ++u) {
@@ -70,14 +70,14 @@ __device__ void deq_col_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int64
   const int64_t c = (task % col_tiles) * kDeqTileCols + (int64_t)lane * 4;
   if (c >= cols) return;                              // cols % 8 == 0: whole units only
   // rows r0 .. r0 + kDeqRows - 1 lie in one 32-row block (kDeqRows divides 32)
-  const uint32_t sb = *reinterpret_cast<const uint32_t*>(d.s + (r0 / kBlock) * s_pitch + c);
+  const uint32_t sb = load4_cached(d.s + (r0 / kBlock) * s_pitch + c);
   float sc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) sc[k] = e8m0_value((sb >> (8 * k)) & 0xFFu);
   uint32_t q[kDeqRows];
 #pragma unroll
   for (int r = 0; r < kDeqRows; ++r)
-    q[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(d.q + (r0 + r) * cols + c));
+    q[r] = load4(d.q + (r0 + r) * cols + c);
 #pragma unroll
   for (int r = 0; r < kDeqRows; ++r) put4(d.out, bf16, (r0 + r) * cols + c, q[r], sc);
 }

@@ -276,21 +276,45 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 // the caches for reuse that never comes.  Data that is reused (gamma) goes
 // through load16_cached.
 
+// Every tensor the kernels touch lives in global memory; the casts say so,
+// so that loads and stores are global_* instructions even where the
+// compiler cannot trace a pointer back to the kernel arguments (flat_*
+// instructions would otherwise be emitted).
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gload_ptr(const void* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gstore_ptr(void* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load(gload_ptr<u32x4>(p));
 }
 __device__ __forceinline__ u32x2 load8(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return __builtin_nontemporal_load(gload_ptr<u32x2>(p));
 }
 __device__ __forceinline__ u32x4 load16_cached(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+  return *gload_ptr<u32x4>(p);
 }
 __device__ __forceinline__ void store8(void* p, u32x2 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+  __builtin_nontemporal_store(v, gstore_ptr<u32x2>(p));
 }
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  __builtin_nontemporal_store(v, gstore_ptr<u32x4>(p));
 }
+__device__ __forceinline__ uint32_t load4(const void* p) {
+  return __builtin_nontemporal_load(gload_ptr<uint32_t>(p));
+}
+__device__ __forceinline__ void store4(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, gstore_ptr<uint32_t>(p));
+}
+// Small reads that neighbouring lanes or workgroups share (scale bytes and
+// words), and a scale word written back through the L2.
+__device__ __forceinline__ uint32_t load4_cached(const void* p) { return *gload_ptr<uint32_t>(p); }
+__device__ __forceinline__ uint32_t load1_cached(const void* p) { return *gload_ptr<uint8_t>(p); }
+__device__ __forceinline__ void store4_cached(void* p, uint32_t v) { *gstore_ptr<uint32_t>(p) = v; }
 // One scale byte, streamed (nt) or written back through the L2.  A tile owns
 // only a few bytes of each rowwise scale line, so those lines are completed
 // by several workgroups.  Written back, the pieces can merge before they reach
@@ -302,9 +326,9 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) {
 template <bool NT>
 __device__ __forceinline__ void store_scale(void* p, uint32_t v) {
   if constexpr (NT)
-    __builtin_nontemporal_store((uint8_t)v, reinterpret_cast<uint8_t*>(p));
+    __builtin_nontemporal_store((uint8_t)v, gstore_ptr<uint8_t>(p));
   else
-    *reinterpret_cast<uint8_t*>(p) = (uint8_t)v;
+    *gstore_ptr<uint8_t>(p) = (uint8_t)v;
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

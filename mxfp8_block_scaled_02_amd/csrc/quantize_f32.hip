@@ -88,8 +88,8 @@ __device__ void quant_f32_flat_task(const QuantDesc& d, const QuantPitch& pitch,
     const F32Scale sc = f32_scale_key(oct_max(f32_key4(v[u])));
     const uint32_t q = encode4_row(v[u], sc);
     if (p < npieces) {
-      __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(d.q_row) + p);
-      if ((tid & 7) == 0) d.s_row[pitched_block(p >> 3, d.cols >> 5, pitch.s_row)] = (uint8_t)sc.sbyte;
+      store4(reinterpret_cast<uint32_t*>(d.q_row) + p, q);
+      if ((tid & 7) == 0) store_scale<false>(d.s_row + pitched_block(p >> 3, d.cols >> 5, pitch.s_row), sc.sbyte);
     }
   }
 }
@@ -116,8 +116,8 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch,
       const F32Scale sc = f32_scale_key(oct_max(f32_key4(v[r])));
       const uint32_t q = encode4_row(v[r], sc);
       if (ok) {
-        __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(d.q_row + (r0 + r) * cols + c));
-        if ((lane & 7) == 0) d.s_row[(r0 + r) * sb_per_row + (c >> 5)] = (uint8_t)sc.sbyte;
+        store4(d.q_row + (r0 + r) * cols + c, q);
+        if ((lane & 7) == 0) store_scale<false>(d.s_row + (r0 + r) * sb_per_row + (c >> 5), sc.sbyte);
       }
     }
   }
@@ -141,7 +141,7 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch,
       sbytes |= sc[k].sbyte << (8 * k);
     }
     if (ok && wave == 0)
-      *reinterpret_cast<uint32_t*>(d.s_col + rb * pitch.s_col + c) = sbytes;
+      store4_cached(d.s_col + rb * pitch.s_col + c, sbytes);
     if (any_nan) {
       // a NaN/Inf column keeps only each element's sign bit
       u32x4 keep;
@@ -168,8 +168,8 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch,
       const uint32_t q1 = __builtin_amdgcn_perm(dd[1], dd[0], 0x07050301u) | nanq;
       if (ok) {
         uint8_t* qp = d.q_col + (r0 + r) * cols + c;
-        __builtin_nontemporal_store(q0, reinterpret_cast<uint32_t*>(qp));
-        __builtin_nontemporal_store(q1, reinterpret_cast<uint32_t*>(qp + cols));
+        store4(qp, q0);
+        store4(qp + cols, q1);
       }
     }
   }

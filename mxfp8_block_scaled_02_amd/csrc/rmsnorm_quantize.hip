@@ -4,10 +4,29 @@
 // (execute; "Args": gammas, float32 epsilons, weight_offsets, outputs_normed,
 // outputs_quant, outputs_scale [rows, cols/32]) on one GPU's rows:
 //   normed = bf16( x / sqrt(mean(x^2) + eps) * (gamma + weight_offset) )
-// computed in float32 and rounded once (v_cvt_pk_bf16_f32); the quantize then
-// reads the very bf16 words that are stored as normed, so its bytes equal a
-// standalone rowwise quantize of normed (the page's execute: the quantize
-// rides the epilogue on the same bf16 that lands in outputs_normed).
+// rounded once (v_cvt_pk_bf16_f32); the quantize then reads the very bf16
+// words that are stored as normed, so its bytes equal a standalone rowwise
+// quantize of normed (the page's execute: the quantize rides the epilogue on
+// the same bf16 that lands in outputs_normed).
+//
+// Range.  A row's sum of squares is first accumulated in float32.  When that
+// sum lies in [2^-60, 2^120], float32 is exact enough (nothing overflows, and
+// squares lost below float32's range are negligible), and rstd is its
+// reciprocal square root.  Otherwise (rows of huge or tiny values, Inf, NaN;
+// the branch is the same for every lane of the row) the squares are summed
+// again in float64: the square of a bf16 value has at most 16 significant
+// bits and lies between 2^-266 and 2^256, so every square is exact and no row
+// sum (fewer than 2^31 elements) can overflow or underflow.  The mean square
+// is formed in float64 and its reciprocal square root taken in float32 after
+// an exact power-of-two range reduction.  Either way rstd is applied in
+// float32 as (x * rstd) * w, the order the formula is written in;
+// |x * rstd| <= sqrt(cols), so that product cannot overflow.  rstd exceeds
+// float32's range only when the mean square is below about 2^-250, which
+// needs eps == 0 and a row whose values all lie below 2^-124 * sqrt(cols);
+// such a row is scaled by 2^64 first (exact) and rstd by 2^-64.  The IEEE
+// cases follow from the formula: a zero row with eps == 0 is 0 / 0 (NaN
+// everywhere); a row holding an infinity has rstd = 0 (its finite values give
+// +-0, its infinities NaN); a row holding a NaN is NaN.
 //
 // A row belongs to one wave (rows up to 1024 elements, four rows per
 // workgroup) or to all four waves of a workgroup (longer rows); a launch of
@@ -15,9 +34,9 @@
 // lane's serial work is a quarter as long.  Its L lanes
 // hold NCH 16-byte chunks each in registers: chunk j of lane t is chunk
 // t + L j of the row, so every load instruction reads L * 16 contiguous
-// bytes.  The sum of squares is a per-lane float32 chain, a fixed butterfly
-// over each wave, and a fixed-order sum of the wave totals through LDS, so
-// results do not depend on timing.  Rows too long for registers take two
+// bytes.  The sum of squares is a per-lane chain, a fixed DPP reduction over
+// each wave, and a fixed tree over the wave totals through LDS, so results do
+// not depend on timing.  Rows too long for registers take two
 // passes: the sum, then a second read that normalizes and quantizes.
 #include "mx_device.h"
 #include "mx_kernels.h"
@@ -26,52 +45,107 @@ namespace mx {
 
 namespace {
 
-__device__ __forceinline__ float sumsq_chunk(const u32x4& v, float acc) {
-  acc = __builtin_fmaf(bf16_lo(v.x), bf16_lo(v.x), acc);
-  acc = __builtin_fmaf(bf16_hi(v.x), bf16_hi(v.x), acc);
-  acc = __builtin_fmaf(bf16_lo(v.y), bf16_lo(v.y), acc);
-  acc = __builtin_fmaf(bf16_hi(v.y), bf16_hi(v.y), acc);
-  acc = __builtin_fmaf(bf16_lo(v.z), bf16_lo(v.z), acc);
-  acc = __builtin_fmaf(bf16_hi(v.z), bf16_hi(v.z), acc);
-  acc = __builtin_fmaf(bf16_lo(v.w), bf16_lo(v.w), acc);
-  acc = __builtin_fmaf(bf16_hi(v.w), bf16_hi(v.w), acc);
+// Adds the squares of a chunk's 8 values to a float32 or float64 sum (in
+// float64 each square is exact).
+template <class T>
+__device__ __forceinline__ T sumsq_chunk(const u32x4& v, T acc) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const T lo = bf16_lo(v[k]), hi = bf16_hi(v[k]);
+    acc = __builtin_fma(lo, lo, acc);
+    acc = __builtin_fma(hi, hi, acc);
+  }
   return acc;
 }
 
-// Butterfly sum over the 64 lanes; every lane ends with the same value.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// Sum over the 64 lanes.  Within each row of 16 lanes, four DPP steps pair
+// lane i with lane i ^ 1, i ^ 2 (quad permutes), then with its mirror in the
+// half row and in the row; each step adds the same two values in both
+// partners (IEEE addition is commutative), so all 16 lanes hold the same row
+// sum.  The four row sums are then read into scalars and added in one fixed
+// order, so every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+  const u32x2 h = __builtin_bit_cast(u32x2, v);
+  return __builtin_bit_cast(double, u32x2{(uint32_t)__builtin_amdgcn_mov_dpp((int)h.x, CTRL, 0xF, 0xF, true),
+                                          (uint32_t)__builtin_amdgcn_mov_dpp((int)h.y, CTRL, 0xF, 0xF, true)});
 }
 
-__device__ __forceinline__ uint32_t norm_pair(uint32_t xw, uint32_t gw, float rstd, float off) {
-  float lo = bf16_lo(xw) * rstd * (bf16_lo(gw) + off);
-  float hi = bf16_hi(xw) * rstd * (bf16_hi(gw) + off);
-  return pack_bf16x2(lo, hi);
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ double lane_value(double v, int lane) {
+  const u32x2 h = __builtin_bit_cast(u32x2, v);
+  return __builtin_bit_cast(double, u32x2{(uint32_t)__builtin_amdgcn_readlane((int)h.x, lane),
+                                          (uint32_t)__builtin_amdgcn_readlane((int)h.y, lane)});
+}
+
+template <class T>
+__device__ __forceinline__ T wave_sum(T v) {
+  v += dpp<0xB1>(v);    // quad [1, 0, 3, 2]
+  v += dpp<0x4E>(v);    // quad [2, 3, 0, 1]
+  v += dpp<0x141>(v);   // mirror within 8 lanes
+  v += dpp<0x140>(v);   // mirror within 16 lanes
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// How a row's rstd is applied in float32 (see the file comment): rstd itself,
+// or, for the rows whose rstd lies past float32's range, x * 2^64 times
+// rstd * 2^-64.  The flag is the same in every lane of the row.
+struct RowRstd {
+  float r;
+  bool pre;
+};
+
+// rstd = 1 / sqrt(ms), ms = ss / cols + eps formed in float64.  ms = m * 2^E
+// with m in [0.5, 2) and E even (frexp, one exponent step moved into m when
+// odd) is exact; rstd = rsq(m) * 2^(-E/2), with rsq(m) taken in float32
+// (v_rsq_f32, within 1 ulp, after rounding m to float32), so the float32
+// result is within a few 2^-24 of the exact one.  ms = 0 gives m = 0 and
+// rstd = inf; ms = inf or NaN gives m = ms and rstd = 0 or NaN.
+__device__ __forceinline__ RowRstd row_rstd(double ss, double inv_cols, float eps) {
+  const double ms = __builtin_fma(ss, inv_cols, (double)eps);
+  const double f = __builtin_amdgcn_frexp_mant(ms);   // [0.5, 1), or ms itself if 0 / inf / NaN
+  const int e = __builtin_amdgcn_frexp_exp(ms);
+  const int odd = e & 1;
+  const float m = (float)(odd ? f * 2.0 : f);
+  const float rm = __builtin_amdgcn_rsqf(m);
+  const int k = -((e - odd) >> 1);                     // rstd = rm * 2^k
+  const bool pre = k > 125;
+  return RowRstd{__builtin_ldexpf(rm, pre ? k - 64 : k), pre};
 }
 
 // Normalize one chunk with its float32 weights w (gamma + offset), store
-// normed, quantize the stored words.
+// normed, quantize the stored words.  y = ((x * pre) * rstd) * w, where pre
+// is 1 except for the rows whose rstd lies past float32's range (2^64 there).
 __device__ __forceinline__ void finish_chunk(const NormDesc& d, int64_t s_pitch, int64_t row,
                                              int64_t c, bool valid, const u32x4& v, const float* w,
-                                             float rstd, int t) {
+                                             float rstd, float pre, int t) {
   u32x4 y;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    y[k] = pack_bf16x2(bf16_lo(v[k]) * rstd * w[2 * k], bf16_hi(v[k]) * rstd * w[2 * k + 1]);
+    y[k] = pack_bf16x2(bf16_lo(v[k]) * pre * rstd * w[2 * k], bf16_hi(v[k]) * pre * rstd * w[2 * k + 1]);
   const RowScale rs = row_scale_key(quad_max(chunk_key(y)));
   const u32x2 q = encode_chunk_row(y, rs);
   if (valid) {
     const int64_t e = row * (int64_t)d.cols + c * kChunk;
     store16(d.normed + e, y);
     store8(d.q + e, q);
-    if ((t & 3) == 0) d.s[row * s_pitch + ((c * kChunk) >> 5)] = (uint8_t)rs.sbyte;
+    if ((t & 3) == 0) store_scale<false>(d.s + row * s_pitch + ((c * kChunk) >> 5), rs.sbyte);
   }
 }
 
-__device__ __forceinline__ void load_weights(const NormDesc& d, int64_t c, bool valid, float* w) {
-  const u32x4 g = valid ? load16_cached(d.gamma + c * kChunk) : u32x4{0, 0, 0, 0};
+// gamma's 8 values of chunk c (zeros past the row), and the weights
+// gamma + offset as float32.
+__device__ __forceinline__ u32x4 load_gamma(const NormDesc& d, int64_t c, bool valid) {
+  return valid ? load16_cached(d.gamma + c * kChunk) : u32x4{0, 0, 0, 0};
+}
+
+__device__ __forceinline__ void weights(const NormDesc& d, const u32x4& g, float* w) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     w[2 * k] = bf16_lo(g[k]) + d.weight_offset;
@@ -79,60 +153,123 @@ __device__ __forceinline__ void load_weights(const NormDesc& d, int64_t c, bool 
   }
 }
 
-// Sum of a row's partial sums: wave butterfly, then (WPR > 1) the WPR wave
-// totals in wave order through LDS.  part holds two slots, alternated by row,
-// so one barrier per row keeps writers of row k+1 off the values of row k.
-template <int WPR>
-__device__ __forceinline__ float row_sum(float acc, int sub, int lane, float* part, int slot) {
-  float w = wave_sum(acc);
+// Sum of a row's partial sums: wave reduction, then (WPR > 1) the WPR wave
+// totals through LDS in a fixed pairwise tree.  p holds the row's WPR slots;
+// the float32 sums alternate between two such regions by row, so one barrier
+// per row keeps writers of row k+1 off the values of row k.
+template <int WPR, class T>
+__device__ __forceinline__ T row_sum(T acc, int sub, int lane, T* p) {
+  T w = wave_sum(acc);
   if constexpr (WPR == 1) {
     return w;
   } else {
-    float* p = part + slot * WPR;
     if (lane == 0) p[sub] = w;
     __syncthreads();
-    float total = p[0];
+    T t[WPR];
 #pragma unroll
-    for (int k = 1; k < WPR; ++k) total += p[k];
-    return total;
+    for (int k = 0; k < WPR; ++k) t[k] = p[k];
+#pragma unroll
+    for (int n = WPR; n > 1; n >>= 1)
+#pragma unroll
+      for (int k = 0; k < n / 2; ++k) t[k] = t[2 * k] + t[2 * k + 1];
+    return t[0];
   }
+}
+
+// LDS of a workgroup: float32 row sums in two alternating regions, and one
+// region for the float64 sums of the rare rows that need them.  A wave can
+// write the float64 region for row k + 1 only after the float32 barrier of
+// row k + 1, which every wave reaches after reading row k's float64 sums.
+template <int WAVES>
+struct RowParts {
+  float f[2 * WAVES];
+  double d[WAVES];
+};
+
+// Whether a row's float32 sum of squares ss32 can be used (the same answer
+// in every lane of the row).  Inside [2^-60, 2^120] float32 is exact enough:
+// no square or partial sum can overflow, squares lost below float32's range
+// change the sum by less than 2^-35 of itself, and the sum's rounding error
+// stays below 2^-17.  Otherwise (huge or tiny rows, Inf, NaN) the row's
+// squares are summed again in float64.
+__device__ __forceinline__ bool sum32_ok(float ss32) {
+  return __builtin_amdgcn_readfirstlane((int)(ss32 >= 0x1p-60f && ss32 <= 0x1p120f));
+}
+
+__device__ __forceinline__ float rstd32(float ss32, float inv_cols32, float eps) {
+  return __builtin_amdgcn_rsqf(__builtin_fmaf(ss32, inv_cols32, eps));
+}
+
+// rstd and the prescale of a row from its float64 sum of squares ss.  The
+// empty asm keeps 1 / cols (a float64 division) inside the rare branch that
+// calls this; the compiler would otherwise compute it for every row.
+template <int WPR>
+__device__ __forceinline__ void rstd64(double acc, int32_t cols, float eps, int sub, int lane,
+                                       double* part64, float& r, float& pre) {
+  asm volatile("" : "+s"(cols));
+  const RowRstd rr = row_rstd(row_sum<WPR>(acc, sub, lane, part64), 1.0 / (double)cols, eps);
+  r = rr.r;
+  pre = rr.pre ? 0x1p64f : 1.0f;
 }
 
 // Rows first_row, first_row + step, ... (count of them) of one tensor; the
 // row's L = 64 * WPR lanes each hold NCH chunks (chunk j of lane t is chunk
 // t + L j).  The weights gamma + offset stay in registers across the rows.
-template <int WPR, int NCH>
+template <int WPR, int NCH, class Parts>
 __device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row, int step, int count,
-                          int sub, int lane, float* part) {
+                          int sub, int lane, Parts* part) {
   constexpr int L = kWave * WPR;           // lanes per row
   const int t = sub * kWave + lane;        // this lane's index within the row
   const int64_t nch = d.cols / kChunk;
-  const float inv_cols = 1.0f / (float)d.cols;
+  // 1 / cols within 1 ulp (v_rcp_f32): the mean square needs no more
+  const float inv_cols32 = __builtin_amdgcn_rcpf((float)d.cols);
   if constexpr (NCH > 0) {
-    float w[NCH][8];
+    // gamma's loads, then the first row's, are issued before any arithmetic
+    // waits on them
+    u32x4 g[NCH], v[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int64_t c = t + (int64_t)j * L;
-      load_weights(d, c, c < nch, w[j]);
+      g[j] = load_gamma(d, c, c < nch);
     }
-    for (int k = 0; k < count; ++k) {
-      const int64_t row = first_row + (int64_t)k * step;
+    auto load_row = [&](int64_t row) {
       const uint16_t* xr = d.x + row * (int64_t)d.cols;
-      u32x4 v[NCH];
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int64_t c = t + (int64_t)j * L;
         v[j] = c < nch ? load16(xr + c * kChunk) : u32x4{0, 0, 0, 0};
       }
+    };
+    if (count > 0) load_row(first_row);
+    float w[NCH][8];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) weights(d, g[j], w[j]);
+    for (int k = 0; k < count; ++k) {
+      const int64_t row = first_row + (int64_t)k * step;
+      if (k > 0) load_row(row);
       float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < NCH; ++j) acc = sumsq_chunk(v[j], acc);
-      const float ss = row_sum<WPR>(acc, sub, lane, part, k & 1);
-      const float rstd = 1.0f / __builtin_sqrtf(ss * inv_cols + d.eps);
+      const float ss32 = row_sum<WPR>(acc, sub, lane, part->f + (k & 1) * WPR);
+      float r, pre = 1.0f;
+      if (sum32_ok(ss32)) {
+        r = rstd32(ss32, inv_cols32, d.eps);
+      } else {
+        // the empty asm keeps this float64 work inside the branch (the
+        // compiler would otherwise compute it for every row, ahead of the test)
+        double a = 0.0;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+          u32x4 x = v[j];
+          asm volatile("" : "+v"(x));
+          a = sumsq_chunk(x, a);
+        }
+        rstd64<WPR>(a, d.cols, d.eps, sub, lane, part->d, r, pre);
+      }
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int64_t c = t + (int64_t)j * L;
-        finish_chunk(d, s_pitch, row, c, c < nch, v[j], w[j], rstd, t);
+        finish_chunk(d, s_pitch, row, c, c < nch, v[j], w[j], r, pre, t);
       }
     }
   } else {
@@ -147,15 +284,26 @@ __device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row,
         const u32x4 v = c < nch ? load16_cached(xr + c * kChunk) : u32x4{0, 0, 0, 0};
         acc = sumsq_chunk(v, acc);
       }
-      const float ss = row_sum<WPR>(acc, sub, lane, part, k & 1);
-      const float rstd = 1.0f / __builtin_sqrtf(ss * inv_cols + d.eps);
+      const float ss32 = row_sum<WPR>(acc, sub, lane, part->f + (k & 1) * WPR);
+      float r, pre = 1.0f;
+      if (sum32_ok(ss32)) {
+        r = rstd32(ss32, inv_cols32, d.eps);
+      } else {
+        double a = 0.0;
+        for (int64_t c0 = 0; c0 < nch; c0 += L) {
+          const int64_t c = c0 + t;
+          const u32x4 v = c < nch ? load16_cached(xr + c * kChunk) : u32x4{0, 0, 0, 0};
+          a = sumsq_chunk(v, a);
+        }
+        rstd64<WPR>(a, d.cols, d.eps, sub, lane, part->d, r, pre);
+      }
       for (int64_t c0 = 0; c0 < nch; c0 += L) {
         const int64_t c = c0 + t;
         const bool valid = c < nch;
         const u32x4 v = valid ? load16_cached(xr + c * kChunk) : u32x4{0, 0, 0, 0};
         float w[8];
-        load_weights(d, c, valid, w);
-        finish_chunk(d, s_pitch, row, c, valid, v, w, rstd, t);
+        weights(d, load_gamma(d, c, valid), w);
+        finish_chunk(d, s_pitch, row, c, valid, v, w, r, pre, t);
       }
     }
   }
@@ -168,7 +316,7 @@ __device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row,
 template <class Args, int WPR, int NCH, int WAVES = kWavesPerGroup>
 __global__ __launch_bounds__(64 * WAVES) void mxfp8_rmsnorm_quantize_kernel(const Args a,
                                                                            int rows_per_task) {
-  __shared__ float part[2 * WAVES];
+  __shared__ RowParts<WAVES> part;
   constexpr int kSlots = WAVES / WPR;                   // row slots per workgroup
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -185,22 +333,18 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_rmsnorm_quantize_kernel(cons
   asm volatile("" : "+s"(d0.x), "+s"(d0.gamma), "+s"(d0.normed), "+s"(d0.q), "+s"(d0.s),
                "+s"(d0.rows), "+s"(d0.cols), "+s"(d0.weight_offset), "+s"(d0.eps));
   if constexpr (!Args::kPitched) p0 = d0.cols >> 5;
-  if (a.n == 1) {
-    const int64_t row0 = (int64_t)task * rows_per_task;
-    const int64_t left = (int64_t)d0.rows - row0;
-    const int in_task = (int)(left < rows_per_task ? left : rows_per_task);
-    const int count = (in_task - slot + kSlots - 1) / kSlots;
-    norm_rows<WPR, NCH>(d0, p0, row0 + slot, kSlots, count, wave % WPR, lane, part);
-    return;
+  // a grouped launch replaces it with the task's own tensor
+  int64_t row0 = (int64_t)task * rows_per_task;
+  if (a.n != 1) {
+    const int i = find_desc(a.task_start, a.n, task);
+    d0 = a.d[i];
+    p0 = Args::kPitched ? a.pitch(i) : (int64_t)(d0.cols >> 5);
+    row0 = (int64_t)(task - a.task_start[i]) * rows_per_task;
   }
-  const int i = find_desc(a.task_start, a.n, task);
-  const NormDesc d = a.d[i];
-  const int64_t pi = Args::kPitched ? a.pitch(i) : (int64_t)(d.cols >> 5);
-  const int64_t row0 = (int64_t)(task - a.task_start[i]) * rows_per_task;
-  const int64_t left = (int64_t)d.rows - row0;
+  const int64_t left = (int64_t)d0.rows - row0;
   const int in_task = (int)(left < rows_per_task ? left : rows_per_task);
   const int count = (in_task - slot + kSlots - 1) / kSlots;   // rows slot, slot + kSlots, ...
-  norm_rows<WPR, NCH>(d, pi, row0 + slot, kSlots, count, wave % WPR, lane, part);
+  norm_rows<WPR, NCH>(d0, p0, row0 + slot, kSlots, count, wave % WPR, lane, &part);
 }
 
 }  // namespace

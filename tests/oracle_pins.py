@@ -400,6 +400,74 @@ def check_rmsnorm(orc, seed=11):
     assert np.allclose(y[0], want, rtol=1e-14)
 
 
+def check_rmsnorm_range(orc, seed=13):
+    """RMSNorm over bf16's whole range.  With eps = 0 the formula is invariant
+    under x -> 2^k x, and in binary floating point that holds bit for bit as
+    long as nothing overflows or underflows: squares, their sum, the mean and
+    the square root all scale by exact powers of two.  So rows at 2^-125 ..
+    2^126 must give the very same doubles as the row at 2^0, and a row of
+    bf16 subnormals m 2^-133 the same as m 2^-100.  The rows the formula
+    leaves undefined follow IEEE arithmetic: 0/0 is NaN, x * 0 is 0 for finite
+    x and NaN for an infinity."""
+    g = np.random.default_rng(seed)
+    cols = 224
+    gam = torch.from_numpy((1.0 + 0.1 * g.standard_normal(cols)).astype(np.float32))
+    gb = bf16_bits_of(gam.to(torch.bfloat16).double().numpy())
+    # |x| in [0.5, 2): every 2^k multiple for k in -125 .. 126 is a normal bf16
+    mag = g.uniform(0.5, 1.99, cols) * np.where(g.random(cols) < 0.5, -1.0, 1.0)
+    mag = torch.from_numpy(mag.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    base = bf16_bits_of(mag)[None, :]
+    want = orc.rmsnorm_f64(base, gb, 0.5, 0.0)
+    for k in (-125, -100, -60, 1, 60, 100, 126):
+        xk = bf16_bits_of(bf16_values(base) * 2.0 ** k)
+        assert (bf16_values(xk) == bf16_values(base) * 2.0 ** k).all()
+        got = orc.rmsnorm_f64(xk, gb, 0.5, 0.0)
+        assert (got == want).all(), "RMSNorm not scale invariant at 2^%d" % k
+        assert (orc.rmsnorm(xk, gb, 0.5, 0.0) == orc.round_bf16(want)).all()
+    # subnormal row m 2^-133 against its normal twin m 2^-100 (m = 1 .. 127)
+    m = g.integers(1, 128, cols) * np.where(g.random(cols) < 0.5, -1.0, 1.0)
+    sub = bf16_bits_of(m * 2.0 ** -133)[None, :]
+    assert ((sub & 0x7F80) == 0).all() and (bf16_values(sub) == m * 2.0 ** -133).all()
+    twin = bf16_bits_of(m * 2.0 ** -100)[None, :]
+    assert (orc.rmsnorm_f64(sub, gb, 0.0, 0.0) == orc.rmsnorm_f64(twin, gb, 0.0, 0.0)).all()
+    # a positive eps 2^29 times below the mean square (rows at 2^-60) moves
+    # rstd by about 2^-30; against rows at 2^-100 it dominates: then
+    # y = x / sqrt(mean(x^2) + eps) * w with eps the larger term
+    eps = float(np.float32(1e-45))                   # the smallest float32, 2^-149
+    assert eps == 2.0 ** -149
+    x60 = bf16_bits_of(bf16_values(base) * 2.0 ** -60)
+    assert np.allclose(orc.rmsnorm_f64(x60, gb, 0.5, eps), want, rtol=2.0 ** -28, atol=0)
+    assert not (orc.rmsnorm_f64(x60, gb, 0.5, eps) == want).all()
+    x100 = bf16_bits_of(bf16_values(base) * 2.0 ** -100)
+    w = bf16_values(gb) + 0.5
+    ms = np.mean(bf16_values(x100) ** 2)
+    ref = bf16_values(x100)[0] / math.sqrt(ms + eps) * w
+    assert np.allclose(orc.rmsnorm_f64(x100, gb, 0.5, eps)[0], ref, rtol=1e-14, atol=0)
+    # zero rows: NaN with eps = 0, signed zeros with eps > 0
+    z = np.zeros((1, cols), np.uint16)
+    z[0, ::3] = 0x8000
+    assert np.isnan(orc.rmsnorm_f64(z, gb, 0.5, 0.0)).all()
+    assert ((orc.rmsnorm(z, gb, 0.5, 0.0) & 0x7FFF) == 0x7FC0).all()
+    y0 = orc.rmsnorm_f64(z, gb, 0.5, 1e-5)
+    assert (y0 == 0).all() and (np.signbit(y0) == (z == 0x8000) ^ (w < 0)).all()
+    # infinities: rstd = 0, so finite values give signed zeros and the
+    # infinities 0 * inf = NaN; a NaN anywhere makes the whole row NaN
+    inf_row = base.copy()
+    inf_row[0, 7], inf_row[0, 100] = 0x7F80, 0xFF80
+    y = orc.rmsnorm_f64(inf_row, gb, 0.5, 1e-5)
+    assert np.isnan(y[0, [7, 100]]).all()
+    rest = np.ones(cols, bool)
+    rest[[7, 100]] = False
+    assert (y[0, rest] == 0).all()
+    assert (np.signbit(y[0, rest]) == (np.signbit(bf16_values(base)[0, rest]) ^ (w[rest] < 0))).all()
+    nan_row = base.copy()
+    nan_row[0, 50] = 0x7FC1
+    assert np.isnan(orc.rmsnorm_f64(nan_row, gb, 0.5, 1e-5)).all()
+    # the quantized plane of a NaN row: every block NaN
+    _, q, s = orc.rmsnorm_quantize(nan_row, gb, 0.5, 1e-5)
+    assert (s == 0xFF).all() and ((q & 0x7F) == 0x7F).all()
+
+
 def f32_blocks(seed=17, nblocks=4096):
     """float32 blocks: random values over a wide exponent range, plus blocks of
     exact e4m3 ties and ties +- 1 float32 ulp under an anchor that fixes the
@@ -490,6 +558,7 @@ QUICK_CHECKS = [
     ("dequant_tables", check_dequant_tables),
     ("round_bf16", check_round_bf16),
     ("rmsnorm", check_rmsnorm),
+    ("rmsnorm_range", check_rmsnorm_range),
     ("col_is_row_of_transpose", lambda o: check_col_is_row_of_transpose(o, random_tensors(rows=64, cols=64))),
     ("error_bound", lambda o: check_error_bound(o, random_tensors(rows=64, cols=64))),
     ("f32_input", check_f32_input),

@@ -3,8 +3,9 @@ oracle on the same seeded inputs.
 
 Quantized bytes and scales must match bit for bit; dequantized values must be
 equal (NaN where NaN); the fused op's normed bf16 must be within 2^-7 of the
-oracle's float64 RMSNorm (relative, zero exactly where the oracle's is zero),
-and its bytes must equal the oracle's quantize of the GPU's own normed output.
+oracle's float64 RMSNorm (relative; one 2^-133 step in bf16's subnormal range;
+zero exactly where the oracle's is zero, NaN exactly where it is NaN), and its
+bytes must equal the oracle's quantize of the GPU's own normed output.
 """
 import numpy as np
 import pytest
@@ -320,24 +321,138 @@ def test_grouped_64_experts_full_size(orc):
 
 # ----------------------------------------------------------------- RMSNorm --
 
+def check_normed(orc, nb, ref, what):
+    """GPU normed bf16 bits nb against the oracle's unrounded float64 RMSNorm.
+
+    Within 2^-7 of the exact value, relative (one bf16 rounding is at most
+    2^-9, the float32 products add a few 2^-24); in bf16's subnormal range,
+    where one step is 2^-133, within one step; zero exactly where the exact
+    value is zero; NaN exactly where it is NaN (the sign of a NaN is not
+    specified); an infinity only where the exact value rounds to it."""
+    got = P.bf16_values(nb)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), "%s: NaN pattern (%d vs %d NaN)" % (
+        what, int(np.isnan(got).sum()), int(nan.sum()))
+    g, r = got[~nan], ref[~nan]
+    want = P.bf16_values(orc.round_bf16(np.ascontiguousarray(r)))
+    err = np.abs(g - r)
+    with np.errstate(invalid="ignore"):
+        ok = (g == r) | (err <= 2.0 ** -7 * np.abs(r)) | ((np.abs(r) < 2.0 ** -126) & (err <= 2.0 ** -133))
+    ok |= np.isinf(g) & (g == want)
+    ok &= ~((r == 0) & (g != 0))
+    assert ok.all(), "%s: normed off at %d places, first got %s want %s" % (
+        what, int((~ok).sum()), g[~ok][:3].tolist(), r[~ok][:3].tolist())
+
+
+def check_fused_out(orc, xb, gb, off, eps, normed, q, s, what=""):
+    """One fused result (host arrays) against the oracle: normed within the
+    bound above, and q, s byte-identical to the oracle's rowwise quantize of
+    the GPU's own normed bf16."""
+    nb = np.ascontiguousarray(normed)
+    check_normed(orc, nb, orc.rmsnorm_f64(xb, gb, off, eps), what)
+    q2, s2 = orc.quantize_rowwise(nb)
+    assert_same(np.ascontiguousarray(q), q2, what + " q")
+    assert_same(np.ascontiguousarray(s), s2, what + " s")
+
+
 def check_fused(orc, x, gamma, off, eps, rows_sel=None, what=""):
     say("rmsnorm_quantize", what, tuple(x.shape))
     normed, q, s = mx.rmsnorm_quantize(x, gamma, off, eps)
     torch.cuda.synchronize()
-    xb = synth.bf16_bits(x if rows_sel is None else x[rows_sel])
-    gb = synth.bf16_bits(gamma)
-    nb = synth.bf16_bits(normed if rows_sel is None else normed[rows_sel])
-    qg = host(q if rows_sel is None else q[rows_sel])
-    sg = host(s if rows_sel is None else s[rows_sel])
-    ref = orc.rmsnorm_f64(xb, gb, off, eps)
-    got = P.bf16_values(nb)
-    assert ((got == 0) == (ref == 0)).all(), what + ": zero pattern"
-    rel_ok = np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref)
-    assert rel_ok.all(), "%s: normed off by more than 2^-7 at %d places" % (what, int((~rel_ok).sum()))
-    q2, s2 = orc.quantize_rowwise(nb)            # byte identity with a standalone quantize
-    assert_same(qg, q2, what + " q")
-    assert_same(sg, s2, what + " s")
+    sel = (lambda t: t) if rows_sel is None else (lambda t: t[rows_sel])
+    check_fused_out(orc, synth.bf16_bits(sel(x)), synth.bf16_bits(gamma), off, eps,
+                    synth.bf16_bits(sel(normed)), host(sel(q)), host(sel(s)), what)
     return normed, q, s
+
+
+def to_bf16_bits(v):
+    """bf16 bit patterns of float64 values, rounded to nearest even by torch."""
+    t = torch.from_numpy(np.asarray(v, np.float64).astype(np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def edge_rows(cols, seed):
+    """Rows over bf16's whole range and the IEEE special rows, one per line:
+    N(0,1)-shaped rows at 2^60, 2^100 and near the largest bf16 (2^127), at
+    2^-100 and 2^-126 (partly subnormal), at 2^-32 and 2^54 (whose float32
+    sums of squares fall on either side of the kernel's float32 range
+    depending on the width), a row of subnormals only, a row of tiny values
+    holding one value at 2^100, a constant row, a plain N(0, 1) row, a row of
+    zeros (+0 and -0), rows holding +Inf, +-Inf and a NaN."""
+    g = np.random.default_rng(seed)
+    base = lambda: np.clip(g.standard_normal(cols), -1.99, 1.99)
+    rows = [to_bf16_bits(base() * 2.0 ** k) for k in (60, 100, 127, -100, -126, -32, 54)]
+    sub = g.integers(1, 128, cols).astype(np.uint16) | np.where(g.random(cols) < 0.5, 0x8000, 0).astype(np.uint16)
+    rows.append(sub)
+    mixed = to_bf16_bits(base() * 2.0 ** -120)
+    mixed[g.integers(cols)] = to_bf16_bits([2.0 ** 100])[0]
+    rows.append(mixed)
+    rows.append(to_bf16_bits(np.full(cols, -3.0)))
+    rows.append(to_bf16_bits(base()))
+    z = np.zeros(cols, np.uint16)
+    z[::3] = 0x8000
+    rows.append(z)
+    inf1 = to_bf16_bits(base())
+    inf1[g.integers(cols)] = 0x7F80
+    rows.append(inf1)
+    inf2 = to_bf16_bits(base() * 2.0 ** 90)
+    inf2[0], inf2[cols - 1] = 0xFF80, 0x7F80
+    rows.append(inf2)
+    nan = to_bf16_bits(base())
+    nan[g.integers(cols)] = 0x7FC1
+    rows.append(nan)
+    return np.stack(rows)
+
+
+# Row widths and counts that reach every kernel shape: one wave per row with
+# 1 or 2 chunks a lane (96, 1024 columns), four waves per row with 1, 2, 4 or
+# 8 chunks a lane (2048 .. 16384, more than 256 rows), the two-pass rows
+# (20000), and 16 waves per row for launches of at most 256 rows (7168,
+# 16384 with one copy of the edge rows).  (copies of the edge rows, columns)
+EDGE_SHAPES = [(20, 96), (20, 1024), (20, 2048), (20, 4096), (20, 8192), (20, 16384), (20, 20000),
+               (1, 7168), (1, 16384)]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES)
+def test_fused_rows_over_the_whole_range(orc, shape):
+    reps, cols = shape
+    bits = np.tile(edge_rows(cols, seed=cols), (reps, 1))
+    rows = bits.shape[0]
+    gb = to_bf16_bits(1.0 + 0.1 * np.random.default_rng(cols + 1).standard_normal(cols))
+    x, gamma = dev_bits(bits), dev_bits(gb)
+    for off, eps in ((0.0, 0.0), (0.5, 1e-45), (1.0, 1e-6)):
+        what = "edge rows %s offset %g eps %g" % ((rows, cols), off, eps)
+        say("rmsnorm_quantize", what)
+        normed, q, s = mx.rmsnorm_quantize(x, gamma, off, eps)
+        torch.cuda.synchronize()
+        check_fused_out(orc, bits, gb, off, eps, synth.bf16_bits(normed), host(q), host(s), what)
+        nb = synth.bf16_bits(normed)
+        if eps == 0.0:
+            # the zero row is 0 / 0 and its quantized row all NaN blocks
+            zr = [i for i in range(rows) if ((bits[i] & 0x7FFF) == 0).all()]
+            assert zr and np.isnan(P.bf16_values(nb[zr])).all()
+            assert (host(s)[zr] == 0xFF).all() and ((host(q)[zr] & 0x7F) == 0x7F).all()
+
+
+def test_fused_scale_invariant_with_eps_zero():
+    """With eps = 0, RMSNorm(2^k x) = RMSNorm(x) exactly as long as 2^k x stays
+    a normal bf16: the GPU's float64 sum and rstd scale exactly, and x * rstd
+    is the same float32 product."""
+    g = np.random.default_rng(5)
+    cols = 7168
+    mag = to_bf16_bits(g.uniform(0.5, 1.99, (8, cols)) * np.where(g.random((8, cols)) < 0.5, -1, 1))
+    gb = to_bf16_bits(1.0 + 0.1 * g.standard_normal(cols))
+    ref = None
+    for k in (0, -120, -60, 60, 100, 126):
+        xk = to_bf16_bits(P.bf16_values(mag) * 2.0 ** k)
+        say("rmsnorm scale invariance 2^%d" % k)
+        normed, q, s = mx.rmsnorm_quantize(dev_bits(xk), dev_bits(gb), 0.25, 0.0)
+        torch.cuda.synchronize()
+        cur = (synth.bf16_bits(normed), host(q), host(s))
+        if ref is None:
+            ref = cur
+        for a, b in zip(ref, cur):
+            assert np.array_equal(a, b), "not invariant at 2^%d" % k
 
 
 @pytest.mark.parametrize("shape", [(1, 32), (5, 96), (16, 512), (3, 544), (64, 4096),
@@ -384,20 +499,75 @@ def test_fused_workload_prefill_sampled(orc):
 
 def test_fused_grouped(orc):
     shapes = [(16, 7168), (5, 96), (33, 8192)]
+    offs, epss = [0.0, 1.0, -0.25], [1e-5, 1e-6, 1e-3]
     xs, gs = [], []
     for i, s in enumerate(shapes):
         x, g = synth.rmsnorm_inputs(*s, seed=40 + i, x_std=1.0, row_decades=1.0)
         xs.append(x.to(DEV))
         gs.append(g.to(DEV))
-    res = mx.rmsnorm_quantize_grouped(xs, gs, [0.0, 1.0, -0.25], [1e-5, 1e-6, 1e-3])
+    say("rmsnorm_quantize_grouped", shapes)
+    res = mx.rmsnorm_quantize_grouped(xs, gs, offs, epss)
     torch.cuda.synchronize()
     for i, (x, g, (normed, q, s)) in enumerate(zip(xs, gs, res)):
-        n1, q1, s1 = mx.rmsnorm_quantize(x, g, [0.0, 1.0, -0.25][i], [1e-5, 1e-6, 1e-3][i])
+        # each descriptor's own offset and eps, against the oracle
+        check_fused_out(orc, synth.bf16_bits(x), synth.bf16_bits(g), offs[i], epss[i],
+                        synth.bf16_bits(normed), host(q), host(s), "grouped %d" % i)
+        n1, q1, s1 = mx.rmsnorm_quantize(x, g, offs[i], epss[i])
         torch.cuda.synchronize()
         assert np.array_equal(host(normed.view(torch.int16)), host(n1.view(torch.int16)))
         assert np.array_equal(host(q), host(q1)) and np.array_equal(host(s), host(s1))
-        q2, s2 = orc.quantize_rowwise(synth.bf16_bits(normed))
-        assert_same(host(q), q2, "grouped fused q")
+
+
+def test_fused_grouped_edge_rows_per_descriptor_eps(orc):
+    """The range edge rows in one grouped launch whose descriptors carry eps 0,
+    the smallest float32 and 1e-6."""
+    cols = 2048
+    bits = edge_rows(cols, seed=77)
+    gb = to_bf16_bits(1.0 + 0.1 * np.random.default_rng(78).standard_normal(cols))
+    x, g = dev_bits(bits), dev_bits(gb)
+    offs, epss = [0.0, 0.5, 1.0], [0.0, 1e-45, 1e-6]
+    say("rmsnorm_quantize_grouped edge rows")
+    res = mx.rmsnorm_quantize_grouped([x, x, x], [g, g, g], offs, epss)
+    torch.cuda.synchronize()
+    for i, (normed, q, s) in enumerate(res):
+        check_fused_out(orc, bits, gb, offs[i], epss[i], synth.bf16_bits(normed), host(q), host(s),
+                        "grouped edge rows eps %g" % epss[i])
+
+
+def guarded(n, dtype, pad=4096, fill=0xA5):
+    """A flat buffer of n elements of dtype between pad bytes of fill on each
+    side: (the whole byte buffer, the n-element view)."""
+    esz = torch.tensor([], dtype=dtype).element_size()
+    buf = torch.full((2 * pad + n * esz,), fill, dtype=torch.uint8, device=DEV)
+    return buf, buf[pad:pad + n * esz].view(dtype)
+
+
+def assert_guards(buf, pad=4096, fill=0xA5, what=""):
+    h = host(buf)
+    assert (h[:pad] == fill).all() and (h[-pad:] == fill).all(), what + ": write outside the buffer"
+
+
+@pytest.mark.parametrize("shape", [(3, 96), (40, 1056), (300, 4128), (5, 7168), (2, 20000)])
+def test_fused_guard_bands(orc, shape):
+    """normed, q and s inside 0xA5 guard bands; s also with padding between
+    its rows (a pitch 8 bytes wider than the plane)."""
+    rows, cols = shape
+    x, gamma = synth.rmsnorm_inputs(rows, cols, seed=rows + cols, x_std=2.0, row_decades=1.0)
+    nbuf, normed = guarded(rows * cols, torch.bfloat16)
+    qbuf, q = guarded(rows * cols, torch.uint8)
+    w = cols // 32
+    sbuf, sflat = guarded(rows * (w + 8), torch.uint8)
+    s = sflat.view(rows, w + 8)[:, :w]
+    say("rmsnorm_quantize guarded", shape)
+    mx.rmsnorm_quantize(x.to(DEV), gamma.to(DEV), 0.5, 1e-5,
+                        out=(normed.view(rows, cols), q.view(rows, cols), s))
+    torch.cuda.synchronize()
+    for b, name in ((nbuf, "normed"), (qbuf, "q"), (sbuf, "s")):
+        assert_guards(b, what=name)
+    assert (host(sflat.view(rows, w + 8)[:, w:]) == 0xA5).all(), "s: write between rows"
+    check_fused_out(orc, synth.bf16_bits(x), synth.bf16_bits(gamma), 0.5, 1e-5,
+                    synth.bf16_bits(normed.view(rows, cols)), host(q.view(rows, cols)), host(s),
+                    "guarded %s" % (shape,))
 
 
 # -------------------------------------------------------------- dequantize --
@@ -461,3 +631,27 @@ def test_dequantize_grouped(orc):
         ref = orc.dequantize(host(q), host(s), axis)
         got = host(o).astype(np.float64)
         assert ((got == ref) | (np.isnan(got) & np.isnan(ref))).all()
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (96, 1056), (64, 4128)])
+def test_dequantize_guard_bands(orc, shape):
+    """Dequantized output (float32 and bf16) inside 0xA5 guard bands, read from
+    scale planes that sit inside padded allocations."""
+    rows, cols = shape
+    bits = special_values(rows, cols, seed=rows + cols)
+    p = mx.quantize(dev_bits(bits), True, True)
+    _, sr = mx.padded_scale_plane(rows, cols, mx.ROWWISE, 1, 16, device=DEV, fill=0xFF)
+    _, sc = mx.padded_scale_plane(rows, cols, mx.COLUMNWISE, 1, 64, device=DEV, fill=0xFF)
+    sr.copy_(p.rowwise_scale)
+    sc.copy_(p.columnwise_scale)
+    for axis, q, s in ((mx.ROWWISE, p.rowwise_data, sr), (mx.COLUMNWISE, p.columnwise_data, sc)):
+        ref = orc.dequantize(host(q), host(s), axis)
+        for dtype in (torch.float32, torch.bfloat16):
+            say("dequantize guarded", shape, axis, dtype)
+            buf, out = guarded(rows * cols, dtype)
+            mx.dequantize(q, s, axis, dtype, out=out.view(rows, cols))
+            torch.cuda.synchronize()
+            assert_guards(buf, what="dequantize axis %d %s" % (axis, dtype))
+            got = host(out.view(rows, cols).float()).astype(np.float64)
+            want = ref if dtype == torch.float32 else P.bf16_values(orc.round_bf16(ref))
+            assert ((got == want) | (np.isnan(got) & np.isnan(want))).all()

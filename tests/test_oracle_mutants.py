@@ -37,6 +37,10 @@ MUTANTS = {
     "subnormal_code": ("r / ldexp(1.0, -9)", "r / ldexp(1.0, -10)"),
     "rms_eps_dropped": ("ss / (double)cols + (double)eps", "ss / (double)cols"),
     "rms_sum_not_mean": ("ss / (double)cols + (double)eps", "ss + (double)eps"),
+    # float32 accumulation of the squares: overflows for rows near 2^64 and
+    # flushes rows below 2^-75
+    "rms_sum_in_float32": ("double ss = 0.0;\n    for (int64_t c = 0; c < cols; ++c) {\n        double v = bf16_value(x_row[c]);\n        ss += v * v;\n    }",
+                           "float ss = 0.0f;\n    for (int64_t c = 0; c < cols; ++c) {\n        float v = (float)bf16_value(x_row[c]);\n        ss += v * v;\n    }"),
     "rms_offset_sign": ("(bf16_value(gamma[c]) + (double)weight_offset)",
                         "(bf16_value(gamma[c]) - (double)weight_offset)"),
     "dequant_exponent": ("ldexp(1.0 + m / 8.0, ef - 7)", "ldexp(1.0 + m / 8.0, ef - 8)"),

@@ -39,6 +39,10 @@ def test_rmsnorm_closed_forms(orc):
     P.check_rmsnorm(orc)
 
 
+def test_rmsnorm_over_the_whole_bf16_range(orc):
+    P.check_rmsnorm_range(orc)
+
+
 @pytest.fixture(scope="module")
 def xs():
     return P.random_tensors()
