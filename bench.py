@@ -1,20 +1,25 @@
 """Benchmark: bf16 -> MXFP8 quantize throughput on one MI355X.
 
 A step is one pass of the quantize path over one batch: the rowwise and
-columnwise planes of the bf16 weight [4096, 4096] (N(0, 0.02) with 0.1%
-outliers x1000, 1% zero and 1% subnormal 32x32 tiles) from a single read.
-Inputs are resident in HBM before timing starts.  The step rotates over
-enough copies of input and outputs that the working set exceeds the 256 MB
-Infinity Cache, so every step streams from HBM.
+columnwise planes of 64 MoE expert weights, each bf16 [2048, 7168] ~ N(0, 0.01),
+in one grouped launch (1.88 GB in, 3.82 GB of algorithmic bytes per step).
+That is the largest of the five workloads; the other four (a rowwise
+[256, 1024] activation, the row + column [4096, 4096] weight with outliers and
+zero / subnormal tiles, the fused RMSNorm + quantize at [8192, 8192], and the
+fused op at decode [16, 7168] and prefill [65536, 7168]) are measured the same
+way and reported under "configs".  Inputs are resident in HBM before timing
+starts.  Workloads smaller than three times the 256 MB Infinity Cache rotate
+over copies of their inputs and outputs, so every launch streams from HBM.
 
 The timed steps are captured into one HIP graph and replayed once between
-HIP events, so the figure is GPU time, not Python's per-call overhead.
+HIP events on the launch stream, so the figure is GPU time, not Python's
+per-call overhead.  Each workload times at least 50 launches (20 for the
+prefill), after at least 5 warm-up launches.
 
 Printed: one JSON line with GB/s of algorithmic bytes (input read once plus
-every output written once), its fraction of the 8 TB/s HBM peak, the other
-entry points measured the same way on their workloads, a plain device copy
-of the same byte count for context, and the CPU oracle timed on a bounded
-sample on this host.
+every output written once), its fraction of the 8 TB/s HBM peak, the five
+workloads, the other entry points, a plain device copy for context, and the
+CPU oracle timed on bounded samples of every workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -35,34 +40,44 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix-core peak
 MALL_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mxfp8_block_scaled_02_amd", "csrc")
+HEADLINE = "grouped_64x2048x7168"
+# the headline step's one launch: 64 x (2048 / 32) x (7168 / 512) tiles
+HEADLINE_KERNEL = "mx::mxfp8_quantize_kernel<mx::QuantArgs, false>/57344"
+
+# the sources each kernel family is built from: a stored traffic figure is
+# valid only while they are unchanged
+KERNEL_SOURCES = {
+    "mx::mxfp8_quantize_kernel": ("mx_device.h", "mx_kernels.h", "quantize.hip"),
+    "mx::mxfp8_quantize_f32_kernel": ("mx_device.h", "mx_kernels.h", "quantize_f32.hip"),
+    "mx::mxfp8_rmsnorm_quantize_kernel": ("mx_device.h", "mx_kernels.h", "rmsnorm_quantize.hip"),
+    "mx::mxfp8_dequantize_kernel": ("mx_device.h", "mx_kernels.h", "dequantize.hip"),
+    "mx::mxfp8_gemm": ("mx_device.h", "mx_kernels.h", "gemm.hip"),
+}
 
 
-# the sources the headline quantize kernel is built from
-QUANTIZE_SOURCES = ("mx_device.h", "mx_kernels.h", "quantize.hip")
+def sources_hash(kernel: str):
+    """Hash of the sources of the kernel family a trace key belongs to."""
+    for prefix, names in KERNEL_SOURCES.items():
+        if kernel.startswith(prefix):
+            h = hashlib.sha256()
+            for name in names:
+                with open(os.path.join(CSRC, name), "rb") as f:
+                    h.update(name.encode() + f.read())
+            return h.hexdigest()[:16]
+    return None
 
 
-def kernel_source_hash() -> str:
-    """Hash of the quantize kernel's sources: stored traffic figures are valid
-    only while it matches."""
-    h = hashlib.sha256()
-    for name in QUANTIZE_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter runs, if they were taken
-    on the current kernel sources (else None)."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of kernel from the committed counter runs, if they
+    were taken on its current sources (else None)."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        data = json.load(f)
-    if data.get("source_hash") != kernel_source_hash():
+        rec = json.load(f).get("kernels", {}).get(kernel)
+    if rec is None or rec.get("sources_hash") != sources_hash(kernel):
         return None
-    rec = data.get("kernels", {}).get(workload)
-    return None if rec is None else round(rec["bytes_per_launch"])
+    return round(rec["bytes_per_launch"])
 
 
 class Timed:
@@ -119,34 +134,96 @@ def rotation(per_set_bytes: int) -> int:
 EAGER = False
 
 
-def bench_rowcol(torch, mx, synth, steps, warmup):
-    dev = torch.device("cuda:0")
-    x = synth.workload("rowcol_4096x4096", device=dev)["x"]
-    rows, cols = x.shape
-    alg = rows * cols * 2 + 2 * rows * cols + rows * cols // 32 + (rows // 32) * cols
-    sets = rotation(alg)
-    xs = [x.clone() for _ in range(sets)]
-    outs = [mx.quantize(xi, True, True) for xi in xs]
-    fn = lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets])
-    ms, wall = Timed(torch, EAGER).run(fn, steps, warmup)
-    return {"ms": ms, "bytes": alg, "elems": rows * cols, "sets": sets, "wall_s": wall}
+def quant_bytes(r, c, rowwise, columnwise, in_bytes=2):
+    return r * c * in_bytes + (r * c + r * c // 32 if rowwise else 0) + (r * c + (r // 32) * c if columnwise else 0)
 
 
-def bench_other_rows(torch, mx, synth, steps):
-    """Each remaining entry point on its own workload (fewer steps)."""
+def fused_bytes(r, c):
+    return r * c * 2 + r * c * 2 + r * c + r * c // 32 + c * 2
+
+
+def rec(ms, alg, elems, launches, **extra):
+    gbs = alg / (ms * 1e-3) / 1e9
+    out = {"ms_per_launch": round(ms, 5), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+           "Gelem_s": round(elems / (ms * 1e-3) / 1e9, 2), "alg_bytes": alg, "launches_timed": launches}
+    out.update(extra)
+    return out
+
+
+def bench_headline(torch, mx, synth, steps, warmup):
+    """The grouped row + column quantize of 64 expert weights: one launch a step."""
     dev = torch.device("cuda:0")
-    res = {}
+    xs = synth.workload(HEADLINE, device=dev)["xs"]
+    r, c = xs[0].shape
+    alg = len(xs) * quant_bytes(r, c, True, True)
+    outs = mx.quantize_grouped(xs, True, True)
+    ms, wall = Timed(torch, EAGER).run(lambda i: mx.quantize_grouped(xs, True, True, outs=outs), steps, warmup)
+    del xs, outs
+    return {"ms": ms, "bytes": alg, "elems": 64 * r * c, "wall_s": wall, "shape": [r, c], "tensors": 64}
+
+
+def bench_configs(torch, mx, synth, steps):
+    """The other four workloads, each at least 50 launches (20 for the 65536-row
+    prefill) after 5 warm-up launches."""
+    dev = torch.device("cuda:0")
     T = Timed(torch, EAGER)
+    res = {}
+    k_small = max(50, steps // 2)
+    k_large = max(20, steps // 10)
 
     x = synth.workload("rowwise_256x1024", device=dev)["x"]
     r, c = x.shape
-    alg = r * c * 3 + r * c // 32
-    sets = rotation(alg) if alg * rotation(alg) < (1 << 31) else 1
-    xs = [x.clone() for _ in range(min(sets, 512))]
+    alg = quant_bytes(r, c, True, False)
+    n = min(rotation(alg), 512)
+    xs = [x.clone() for _ in range(n)]
     outs = [mx.quantize(xi, True, False) for xi in xs]
-    n = len(xs)
-    ms, _ = T.run(lambda i: mx.quantize(xs[i % n], True, False, out=outs[i % n]), steps, 10)
-    res["rowwise_256x1024"] = (ms, alg, r * c)
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % n], True, False, out=outs[i % n]), k_small, 10)
+    res["rowwise_256x1024"] = rec(ms, alg, r * c, k_small, rotating_sets=n, target_frac=0.70)
+    del xs, outs
+
+    x = synth.workload("rowcol_4096x4096", device=dev)["x"]
+    r, c = x.shape
+    alg = quant_bytes(r, c, True, True)
+    n = rotation(alg)
+    xs = [x.clone() for _ in range(n)]
+    outs = [mx.quantize(xi, True, True) for xi in xs]
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % n], True, True, out=outs[i % n]), k_small, 10)
+    res["rowcol_4096x4096"] = rec(ms, alg, r * c, k_small, rotating_sets=n, target_frac=0.70)
+    del xs, outs
+
+    w = synth.workload("rmsnorm_8192x8192", device=dev)
+    r, c = w["x"].shape
+    alg = fused_bytes(r, c)
+    n = rotation(alg)
+    xs = [w["x"]] + [w["x"].clone() for _ in range(n - 1)]
+    os_ = [mx.rmsnorm_quantize(xi, w["gamma"], w["weight_offset"], w["eps"]) for xi in xs]
+    ms, _ = T.run(lambda i: mx.rmsnorm_quantize(xs[i % n], w["gamma"], w["weight_offset"], w["eps"],
+                                                out=os_[i % n]), k_small, 5)
+    res["rmsnorm_8192x8192"] = rec(ms, alg, r * c, k_small, rotating_sets=n, target_frac=0.70)
+    del w, xs, os_
+
+    for name in ("rmsnorm_decode_16x7168", "rmsnorm_prefill_65536x7168"):
+        w = synth.workload(name, device=dev)
+        r, c = w["x"].shape
+        alg = fused_bytes(r, c)
+        # a small input rotates over copies; the prefill input alone is larger
+        # than the Infinity Cache
+        n = min(rotation(alg), 512) if alg < MALL_BYTES else 1
+        xs = [w["x"]] + [w["x"].clone() for _ in range(n - 1)]
+        os_ = [mx.rmsnorm_quantize(xi, w["gamma"], w["weight_offset"], w["eps"]) for xi in xs]
+        k = k_small if r < 1024 else k_large
+        ms, _ = T.run(lambda i: mx.rmsnorm_quantize(xs[i % n], w["gamma"], w["weight_offset"], w["eps"],
+                                                    out=os_[i % n]), k, 5)
+        res[name] = rec(ms, alg, r * c, k, rotating_sets=n)
+        del w, xs, os_
+    return res
+
+
+def bench_other_rows(torch, mx, synth, steps):
+    """The entry points outside the five workloads, each on its own input."""
+    dev = torch.device("cuda:0")
+    res = {}
+    T = Timed(torch, EAGER)
 
     x = synth.workload("rowwise_8192x7168", device=dev)["x"]
     r, c = x.shape
@@ -159,40 +236,6 @@ def bench_other_rows(torch, mx, synth, steps):
     res["rowwise_8192x7168"] = (ms, alg, r * c)
     del xs, outs
 
-    w = synth.workload("rmsnorm_8192x8192", device=dev)
-    r, c = w["x"].shape
-    alg = r * c * 2 + r * c * 2 + r * c + r * c // 32 + c * 2
-    sets = rotation(alg)
-    xs = [w["x"].clone() for _ in range(sets)]
-    os_ = [mx.rmsnorm_quantize(xi, w["gamma"], w["weight_offset"], w["eps"]) for xi in xs]
-    ms, _ = T.run(lambda i: mx.rmsnorm_quantize(xs[i % sets], w["gamma"], w["weight_offset"], w["eps"],
-                                                out=os_[i % sets]), max(steps // 4, 5), 3)
-    res["rmsnorm_8192x8192"] = (ms, alg, r * c)
-    del w, xs, os_
-
-    xs = synth.workload("grouped_64x2048x7168", device=dev)["xs"]
-    r, c = xs[0].shape
-    alg = len(xs) * (r * c * 2 + 2 * r * c + r * c // 32 + (r // 32) * c)
-    outs = mx.quantize_grouped(xs, True, True)
-    ms, _ = T.run(lambda i: mx.quantize_grouped(xs, True, True, outs=outs), max(steps // 10, 5), 2)
-    res["grouped_64x2048x7168"] = (ms, alg, len(xs) * r * c)
-    del xs, outs
-
-    for name in ("rmsnorm_decode_16x7168", "rmsnorm_prefill_65536x7168"):
-        w = synth.workload(name, device=dev)
-        r, c = w["x"].shape
-        alg = r * c * 2 + r * c * 2 + r * c + r * c // 32 + c * 2
-        # a small input rotates over copies like the small quantize line; the
-        # prefill input alone is larger than the Infinity Cache
-        n = min(rotation(alg), 512) if alg < MALL_BYTES else 1
-        xs = [w["x"]] + [w["x"].clone() for _ in range(n - 1)]
-        os_ = [mx.rmsnorm_quantize(xi, w["gamma"], w["weight_offset"], w["eps"]) for xi in xs]
-        k = steps if r < 1024 else max(steps // 10, 5)
-        ms, _ = T.run(lambda i: mx.rmsnorm_quantize(xs[i % n], w["gamma"], w["weight_offset"], w["eps"],
-                                                    out=os_[i % n]), k, 3)
-        res[name] = (ms, alg, r * c)
-        del w, xs, os_
-
     x = synth.workload("rowcol_f32_4096x4096", device=dev)["x"]
     r, c = x.shape
     alg = r * c * 4 + 2 * r * c + r * c // 32 + (r // 32) * c
@@ -203,7 +246,7 @@ def bench_other_rows(torch, mx, synth, steps):
     res["rowcol_f32_4096x4096"] = (ms, alg, r * c)
     del xs, outs
 
-    # context: a plain device copy moving the row+column step's input volume
+    # context: a plain device copy moving the 4096 x 4096 weight's volume
     sets = rotation(2 * (32 << 20))
     srcs = [torch.empty(32 << 20, dtype=torch.uint8, device=dev).fill_(1) for _ in range(sets)]
     dsts = [torch.empty_like(t) for t in srcs]
@@ -211,7 +254,7 @@ def bench_other_rows(torch, mx, synth, steps):
     res["context_device_copy_32MiB"] = (ms, 2 * (32 << 20), 0)
     del srcs, dsts
 
-    # the headline workload with both scale planes in padded allocations whose
+    # the 4096 x 4096 weight with both scale planes in padded allocations whose
     # rows are a pitch apart (136 and 4216 bytes instead of 128 and 4096):
     # same algorithmic bytes, written in place
     x = synth.workload("rowcol_4096x4096", device=dev)["x"]
@@ -295,39 +338,88 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(synth, target_s=12.0, single_s=6.0):
-    """The oracle on full passes of the headline weight: all host threads for
-    about target_s, then one thread for about single_s."""
+def cpu_baseline(torch, synth, min_s=0.75, dev="cuda:0"):
+    """The oracle on bounded samples of every workload, with all host threads
+    (OpenMP over rows, and over tensors for the experts) and with one thread.
+
+    Each sample is cut from the same seeded input the GPU quantizes (drawn on
+    the device, copied back).  Each leg repeats the sample until min_s seconds
+    have passed; rates are GB/s and Gelem/s of the same algorithmic bytes as
+    the GPU figures.  About 15 s of CPU work in all."""
     import oracle
-    x = synth.workload("rowcol_4096x4096")["x"]
-    bits = synth.bf16_bits(x)
-    rows, cols = bits.shape
-    alg = rows * cols * 2 + 2 * rows * cols + rows * cols // 32 + (rows // 32) * cols
-
-    def passes(limit_s):
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.quantize_rowwise(bits)
-            oracle.quantize_colwise(bits)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= limit_s or reps >= 1000:
-                return reps, el
-
+    dev = torch.device(dev)
     cores = oracle.max_threads()
-    reps, el = passes(target_s)
-    oracle.set_threads(1)
-    try:
-        reps1, el1 = passes(single_s)
-    finally:
-        oracle.set_threads(cores)
-    return {"value": round(alg * reps / el / 1e9, 3), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "%d passes of the full 4096x4096 weight, rowwise + columnwise planes, %.1f s"
-                      % (reps, el),
-            "value_1_thread": round(alg * reps1 / el1 / 1e9, 4),
-            "sample_1_thread": "%d passes, %.1f s" % (reps1, el1),
-            "cpu_model": cpu_model()}
+
+    def leg(fn, alg, elems, threads, what, limit=min_s):
+        oracle.set_threads(threads)
+        try:
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= limit or reps >= 10000:
+                    break
+        finally:
+            oracle.set_threads(cores)
+        return {"GB_s": round(alg * reps / el / 1e9, 4), "Gelem_s": round(elems * reps / el / 1e9, 5),
+                "threads": threads, "sample": "%s, %d passes in %.2f s" % (what, reps, el)}
+
+    def quant(bits, row, col):
+        def fn():
+            if row:
+                oracle.quantize_rowwise(bits)
+            if col:
+                oracle.quantize_colwise(bits)
+        return fn
+
+    def fused(w, bits):
+        gb = synth.bf16_bits(w["gamma"])
+        return lambda: oracle.rmsnorm_quantize(bits, gb, w["weight_offset"], w["eps"])
+
+    out = {}
+    x = synth.bf16_bits(synth.workload("rowwise_256x1024", device=dev)["x"])
+    r, c = x.shape
+    out["rowwise_256x1024"] = [leg(quant(x, True, False), quant_bytes(r, c, True, False), r * c, t,
+                                   "the whole [256, 1024] tensor") for t in (cores, 1)]
+
+    x = synth.bf16_bits(synth.workload("rowcol_4096x4096", device=dev)["x"])
+    legs = []
+    for t, rows in ((cores, 4096), (1, 1024)):
+        xs = x[:rows]
+        legs.append(leg(quant(xs, True, True), quant_bytes(rows, 4096, True, True), rows * 4096, t,
+                        "rows 0..%d of the [4096, 4096] weight, both planes" % rows))
+    out["rowcol_4096x4096"] = legs
+
+    xs = synth.workload(HEADLINE, device=dev)["xs"]
+    legs = []
+    for t, n_exp, rows in ((cores, 8, 2048), (1, 1, 1024)):
+        bits = [synth.bf16_bits(e[:rows]) for e in xs[:n_exp]]
+        fn = (lambda b=bits: [quant(e, True, True)() for e in b])
+        legs.append(leg(fn, n_exp * quant_bytes(rows, 7168, True, True), n_exp * rows * 7168, t,
+                        "%d of the 64 expert weights (rows 0..%d each), both planes" % (n_exp, rows)))
+    out[HEADLINE] = legs
+    del xs
+
+    for name, samples in (("rmsnorm_8192x8192", ((cores, 4096), (1, 512))),
+                          ("rmsnorm_decode_16x7168", ((cores, 16), (1, 16))),
+                          ("rmsnorm_prefill_65536x7168", ((cores, 8192), (1, 512)))):
+        w = synth.workload(name, device=dev)
+        R, C = w["x"].shape
+        legs = []
+        for t, rows in samples:
+            bits = synth.bf16_bits(w["x"][:rows])
+            legs.append(leg(fused(w, bits), fused_bytes(rows, C), rows * C, t,
+                            "rows 0..%d of [%d, %d], normed + rowwise plane" % (rows, R, C)))
+        out[name] = legs
+        del w
+
+    head = out[HEADLINE]
+    return {"value": head[0]["GB_s"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": head[0]["sample"] + " (the headline workload)",
+            "value_1_thread": head[1]["GB_s"], "sample_1_thread": head[1]["sample"],
+            "cpu_model": cpu_model(),
+            "per_config": {k: {"all_threads": v[0], "one_thread": v[1]} for k, v in out.items()}}
 
 
 def short_kernel_name(name: str) -> str:
@@ -396,7 +488,8 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int = 256 << 20)
             continue
         fb = sum(v) / len(v) * 1024.0 * f_scale
         wb = sum(write[key]) / len(write[key]) * 1024.0 * w_scale
-        res["%s/%d" % key] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+        res["%s/%d" % key] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                              "sources_hash": sources_hash(key[0])}
     return {"fetch_scale": f_scale, "write_scale": w_scale, "kernels": res}
 
 
@@ -406,11 +499,17 @@ def main():
         return
     if len(sys.argv) > 3 and sys.argv[1] == "--traffic-summary":
         res = traffic_summary(sys.argv[2], sys.argv[3])
-        res["source_hash"] = kernel_source_hash()
-        res["hashed_sources"] = list(QUANTIZE_SOURCES)
         print(json.dumps(res, indent=1))
         if "--write" in sys.argv:
-            with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+            path = os.path.join(PROFILES, "traffic.json")
+            old = {}
+            if os.path.exists(path):
+                with open(path) as f:
+                    old = json.load(f).get("kernels", {})
+            # keep the records of kernels this run did not launch
+            old.update(res["kernels"])
+            res["kernels"] = old
+            with open(path, "w") as f:
                 json.dump(res, f, indent=1)
         return
     ap = argparse.ArgumentParser()
@@ -445,11 +544,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    main_run = bench_rowcol(torch, mx, synth, args.steps, args.warmup)
+    main_run = bench_headline(torch, mx, synth, args.steps, args.warmup)
     ms = main_run["ms"]
     gbs = main_run["bytes"] / (ms * 1e-3) / 1e9
-    # the row+column launch on the 4096 x 4096 weight: (4096/32) x (4096/512) tiles
-    traffic = measured_traffic("mx::mxfp8_quantize_kernel<mx::QuantArgs, true>/1024")
     line = {
         "metric": "bf16\u2192MXFP8 quantize GB/s (frac of MI355X HBM peak) + Gelem/s, 1 GPU",
         "value": round(gbs, 1),
@@ -463,17 +560,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "rowcol_4096x4096", "shape": [4096, 4096],
+        "config": {"workload": HEADLINE, "tensors": main_run["tensors"], "shape": main_run["shape"],
                    "planes": ["rowwise", "columnwise"], "alg_bytes_per_step": main_run["bytes"],
-                   "rotating_sets": main_run["sets"]},
+                   "launches_per_step": 1},
         "Gelem_s": round(main_run["elems"] / (ms * 1e-3) / 1e9, 2),
+        # one launch per step, so the step time is the dominant kernel's
+        # average launch duration
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(HEADLINE_KERNEL), "kernel": HEADLINE_KERNEL},
     }
     if not args.no_other_rows:
+        line["configs"] = bench_configs(torch, mx, synth, args.steps)
         line["other_entry_points"] = bench_other_rows(torch, mx, synth, max(args.steps // 2, 20))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(synth)
+        line["cpu_baseline"] = cpu_baseline(torch, synth)
     print(json.dumps(line), flush=True)
 
 
