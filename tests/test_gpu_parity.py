@@ -233,6 +233,31 @@ def test_f32_columnwise_only(orc, shape):
     check_quantize_f32(orc, f32_specials(*shape, seed=12), False, True, "f32 colonly")
 
 
+@pytest.mark.parametrize("shape", [(32, 544), (64, 4128), (96, 1056), (32, 32)])
+def test_f32_guard_bands_partial_tiles(orc, shape):
+    """Both planes of float32 input whose last 256-column tile is partial:
+    lanes past the row's end recompute and rewrite the bytes of the row's
+    first 32 columns, so every write stays inside the planes and the bytes
+    equal the oracle's."""
+    rows, cols = shape
+    x = f32_specials(rows, cols, seed=rows * cols)
+    say("quantize_f32 guarded", shape)
+    bufs = [guarded(rows * cols, torch.uint8) for _ in range(2)]
+    sbufs = [guarded(rows * cols // 32, torch.uint8) for _ in range(2)]
+    out = mx.MXFP8Planes(bufs[0][1].view(rows, cols), bufs[1][1].view(rows, cols),
+                         sbufs[0][1].view(rows, cols // 32), sbufs[1][1].view(rows // 32, cols))
+    mx.quantize(dev_f32(x), True, True, out=out)
+    torch.cuda.synchronize()
+    for (b, _), name in zip(bufs + sbufs, ("q_row", "q_col", "s_row", "s_col")):
+        assert_guards(b, what="f32 " + name)
+    qr, sr = orc.quantize_rowwise(x)
+    qc, sc = orc.quantize_colwise(x)
+    assert_same(host(out.rowwise_data), qr, "q_row")
+    assert_same(host(out.rowwise_scale), sr, "s_row")
+    assert_same(host(out.columnwise_data), qc, "q_col")
+    assert_same(host(out.columnwise_scale), sc, "s_col")
+
+
 def test_f32_master_weight_4096(orc):
     x = synth.workload("rowcol_f32_4096x4096", device=DEV)["x"]
     check_quantize_f32(orc, x.cpu().numpy(), True, True, "rowcol_f32_4096x4096")
