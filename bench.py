@@ -42,7 +42,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mxfp8_block_scaled_02_amd", "csrc")
 HEADLINE = "grouped_64x2048x7168"
 # the headline step's one launch: 64 x (2048 / 32) x (7168 / 512) tiles
-HEADLINE_KERNEL = "mx::mxfp8_quantize_kernel<mx::QuantArgs, false>/57344"
+HEADLINE_KERNEL = "mx::mxfp8_quantize_kernel<mx::QuantArgs, false, true>/57344"
 
 # the sources each kernel family is built from: a stored traffic figure is
 # valid only while they are unchanged
@@ -506,7 +506,9 @@ def main():
             if os.path.exists(path):
                 with open(path) as f:
                     old = json.load(f).get("kernels", {})
-            # keep the records of kernels this run did not launch
+            # keep the records of kernels this run did not launch, unless their
+            # sources changed since (then no record of them is current)
+            old = {k: v for k, v in old.items() if v.get("sources_hash") == sources_hash(k.split("/")[0])}
             old.update(res["kernels"])
             res["kernels"] = old
             with open(path, "w") as f:

@@ -74,109 +74,137 @@ __device__ void quant_flat_task(const QuantDesc& d, const QuantPitch& pitch, int
     quant_flat_pieces<NT, kFlatUnroll>(d, pitch, task, tid, npieces);
 }
 
-template <bool NT>
+// Packed magnitude maxima of the lane's 8 columns over the wave's rows (word j
+// holds columns 2j, 2j + 1), also written to the lane's LDS slot.
+__device__ __forceinline__ u32x4 wave_col_max(const u32x4 (&v)[kRowsPerWave][kCh], u32x4* slot) {
+  u32x4 m = kZero4;
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = pk_max_u16(m[j], mag2(v[r][0][j]));
+  *slot = m;
+  return m;
+}
+
+// ROW: the rowwise plane is requested too (then cols % 32 == 0).
+template <bool NT, bool ROW>
 __device__ void quant_tile_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task,
                                 int wave, int lane, u32x4* colmax) {
   const int64_t cols = d.cols;
   const int64_t col_tiles = (cols + kTileCols - 1) / kTileCols;
+  if constexpr (ROW) {
+    // The column tiles of a row block share its rowwise scale lines.
+    // Workgroup ids are spread over the 8 XCDs in turn, so tiles whose ids
+    // are 8 apart run on one XCD and their pieces meet in its L2.  Tile
+    // (rb, ct) takes id 8 (col_tiles (rb / 8) + ct) + rb % 8, a permutation
+    // whenever the row blocks are a multiple of 8.  A resident grid whose
+    // column tiles are a multiple of 8 keeps the plain order, where each XCD
+    // holds whole column strips: measured faster there (4096 x 4096: 13.3
+    // against 13.6 us), slower everywhere else.
+    if ((d.rows / kTileRows) % 8 == 0 && !(NT && col_tiles % 8 == 0)) {
+      const int64_t j = task >> 3;
+      task = ((j / col_tiles) * 8 + (task & 7)) * col_tiles + j % col_tiles;
+    }
+  }
   const int64_t rb = task / col_tiles;                       // 32-row block index
   const int64_t r0 = rb * kTileRows + wave * kRowsPerWave;    // this wave's first row
   const int64_t c = (task % col_tiles) * kTileCols + (int64_t)lane * kLaneCols;
-  bool ok[kCh];                                              // chunk h: columns c + 8h ..
-#pragma unroll
-  for (int h = 0; h < kCh; ++h) ok[h] = c + h * kChunk < cols;
-  const uint16_t* xp = d.x + r0 * cols + c;
+  // Lanes past the row's end (only in a last, partial column tile) never load
+  // or store behind a branch: the compiler cannot know whether a store inside
+  // an `if` was issued (stores count in vmcnt), so it would wait for more
+  // loads, and finally for the wave's own earlier stores, before each row.
+  //   ROW (cols % 32 == 0): such a lane takes column (lane % 4) * 8 of the
+  //   same rows instead.  Its lane quad then covers columns 0..31 of the
+  //   tile's 32 rows exactly, so it computes the very bytes, row scales and
+  //   column scales that the lanes owning those columns compute, and its
+  //   stores rewrite identical bytes.
+  //   !ROW (columnwise only; cols % 8 == 0): such a lane reads columns 0..7
+  //   of its rows (always inside the tensor) and its stores are skipped;
+  //   what it computes reaches no output, since a column's maximum is its
+  //   own lane's.
+  static_assert(kCh == 1, "lane mirroring assumes one chunk per lane");
+  const bool ok = c < cols;
+  const int64_t ce = ok ? c : (ROW ? (int64_t)(lane & 3) * kLaneCols : 0);
+  const bool st = ROW || ok;
+  const uint16_t* xp = d.x + r0 * cols + ce;
 
   u32x4 v[kRowsPerWave][kCh];
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r)
-#pragma unroll
-    for (int h = 0; h < kCh; ++h)
-      v[r][h] = ok[h] ? load16(xp + r * cols + h * kChunk) : kZero4;
+  for (int r = 0; r < kRowsPerWave; ++r) v[r][0] = load16(xp + r * cols);
 
-  if (d.q_row) {
-    // cols % 32 == 0 here, so a block's lanes are either all present or absent
-    const int64_t sb_per_row = pitch.s_row;
+  // A resident grid (NT) runs one tile per workgroup: every wave there waits
+  // for all its loads before its first store (the column maxima need them
+  // all, and the empty asm keeps the stores behind them), so the chip reads
+  // first and then writes.  A streaming grid stores each row as its load
+  // lands, which overlaps other workgroups' loads.  Measured both ways:
+  // 4096 x 4096 13.3 against 13.6 us, 8192 x 7168 42.0 against 42.6 us.
+  u32x4 m = kZero4;
+  if constexpr (NT) {
+    m = wave_col_max(v, colmax + wave * kWave + lane);
+    asm volatile("" ::"v"(m[0]), "v"(m[1]), "v"(m[2]), "v"(m[3]));
+  }
+
+  // rowwise scale bytes of the wave's rows, stored after every data store of
+  // the tile, packed four to a dword: row r in byte r % 4 of word r / 4
+  uint32_t row_sb[kRowsPerWave / 4] = {};
+  if constexpr (ROW) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       const RowScale rs = lane_row_scale(v[r]);
-      if (ok[0]) {
-#pragma unroll
-        for (int h = 0; h < kCh; ++h)
-          store8(d.q_row + (r0 + r) * cols + c + h * kChunk, encode_chunk_row(v[r][h], rs));
-        if ((lane & (kBlock / kLaneCols - 1)) == 0)
-          store_scale<NT>(d.s_row + (r0 + r) * sb_per_row + (c >> 5), rs.sbyte);
-      }
+      row_sb[r / 4] |= rs.sbyte << (8 * (r % 4));
+      store8(d.q_row + (r0 + r) * cols + ce, encode_chunk_row(v[r][0], rs));
     }
   }
 
-  if (d.q_col) {
-    // packed column maxima: word j of chunk h holds columns c + 8h + 2j, + 1
-    u32x4 m[kCh];
+  if constexpr (!NT) m = wave_col_max(v, colmax + wave * kWave + lane);
+  __syncthreads();
 #pragma unroll
-    for (int h = 0; h < kCh; ++h) {
-      m[h] = kZero4;
+  for (int w = 0; w < kWavesPerGroup; ++w) {
+    if (w == wave) continue;
+    const u32x4 o = colmax[w * kWave + lane];
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r)
+    for (int j = 0; j < 4; ++j) m[j] = pk_max_u16(m[j], o[j]);
+  }
+  ColPair cp[4];
+  u32x2 sb, nanq;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m[h][j] = pk_max_u16(m[h][j], mag2(v[r][h][j]));
-      colmax[(wave * kWave + lane) * kCh + h] = m[h];
+  for (int j = 0; j < 4; ++j) cp[j] = col_pair(m[j]);
+  // scale bytes and NaN bytes of the chunk's 8 columns, in column order
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    sb[k] = __builtin_amdgcn_perm(cp[2 * k + 1].sbytes, cp[2 * k].sbytes, 0x06040200u);
+    nanq[k] = __builtin_amdgcn_perm(cp[2 * k + 1].nanff, cp[2 * k].nanff, 0x06040200u) & 0x7F7F7F7Fu;
+  }
+  if (st && wave == 0) store8(d.s_col + rb * pitch.s_col + ce, sb);
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; r += 2) {
+    uint8_t* qp = d.q_col + (r0 + r) * cols + ce;
+    u32x2 q0, q1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32x2 o = encode_col_quad(v[r][0][2 * k], v[r + 1][0][2 * k], v[r][0][2 * k + 1],
+                                      v[r + 1][0][2 * k + 1], cp[2 * k], cp[2 * k + 1]);
+      q0[k] = o.x | nanq[k];
+      q1[k] = o.y | nanq[k];
     }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w) {
-      if (w == wave) continue;
-#pragma unroll
-      for (int h = 0; h < kCh; ++h) {
-        const u32x4 o = colmax[(w * kWave + lane) * kCh + h];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m[h][j] = pk_max_u16(m[h][j], o[j]);
-      }
+    if (st) {
+      store8(qp, q0);
+      store8(qp + cols, q1);
     }
-    ColPair cp[kCh][4];
-    u32x2 sb[kCh], nanq[kCh];
+  }
+
+  if (ROW && (lane & (kBlock / kLaneCols - 1)) == 0) {
 #pragma unroll
-    for (int h = 0; h < kCh; ++h) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cp[h][j] = col_pair(m[h][j]);
-      // scale bytes and NaN bytes of the chunk's 8 columns, in column order
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        sb[h][k] = __builtin_amdgcn_perm(cp[h][2 * k + 1].sbytes, cp[h][2 * k].sbytes, 0x06040200u);
-        nanq[h][k] = __builtin_amdgcn_perm(cp[h][2 * k + 1].nanff, cp[h][2 * k].nanff,
-                                           0x06040200u) & 0x7F7F7F7Fu;
-      }
-    }
-    if (wave == 0) {
-#pragma unroll
-      for (int h = 0; h < kCh; ++h)
-        if (ok[h]) store8(d.s_col + rb * pitch.s_col + c + h * kChunk, sb[h]);
-    }
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; r += 2) {
-      uint8_t* qp = d.q_col + (r0 + r) * cols + c;
-#pragma unroll
-      for (int h = 0; h < kCh; ++h) {
-        u32x2 q0, q1;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const u32x2 o = encode_col_quad(v[r][h][2 * k], v[r + 1][h][2 * k],
-                                          v[r][h][2 * k + 1], v[r + 1][h][2 * k + 1],
-                                          cp[h][2 * k], cp[h][2 * k + 1]);
-          q0[k] = o.x | nanq[h][k];
-          q1[k] = o.y | nanq[h][k];
-        }
-        if (ok[h]) {
-          store8(qp + h * kChunk, q0);
-          store8(qp + cols + h * kChunk, q1);
-        }
-      }
-    }
+    for (int r = 0; r < kRowsPerWave; ++r)
+      store_scale<NT>(d.s_row + (r0 + r) * pitch.s_row + (ce >> 5), row_sb[r / 4] >> (8 * (r % 4)));
   }
 }
 
-// NT: stream the rowwise scale bytes (see store_scale and the launcher)
-template <class Args, bool NT>
+// NT: stream the rowwise scale bytes (see store_scale and the launcher).
+// ROWCOL: every tensor of the launch requests both planes (the launcher
+// checks), so only that tile path is compiled in; compiled together with the
+// other paths, it would share their code and registers.
+template <class Args, bool NT, bool ROWCOL>
 __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const Args a) {
   __shared__ u32x4 colmax[kThreads * kCh];
   const int tid = threadIdx.x;
@@ -195,21 +223,26 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const Args a) 
   asm volatile("" : "+s"(d0.x), "+s"(d0.q_row), "+s"(d0.s_row), "+s"(d0.q_col), "+s"(d0.s_col),
                "+s"(d0.rows), "+s"(d0.cols));
   if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, d0.cols};
-  if (a.n == 1) {
-    if (d0.q_col)
-      quant_tile_task<NT>(d0, p0, task, wave, lane, colmax);
-    else
-      quant_flat_task<NT>(d0, p0, task, tid);
-    return;
+  // a grouped launch replaces it with the task's own tensor
+  int64_t local = task;
+  if (a.n != 1) {
+    const int i = find_desc(a.task_start, a.n, task);
+    d0 = a.d[i];
+    p0 = Args::kPitched ? a.pitch(i) : QuantPitch{d0.cols >> 5, d0.cols};
+    local = task - a.task_start[i];
   }
-  const int i = find_desc(a.task_start, a.n, task);
-  const QuantDesc d = a.d[i];
-  const QuantPitch pi = Args::kPitched ? a.pitch(i) : QuantPitch{d.cols >> 5, d.cols};
-  const int64_t local = task - a.task_start[i];
-  if (d.q_col)
-    quant_tile_task<NT>(d, pi, local, wave, lane, colmax);
-  else
-    quant_flat_task<NT>(d, pi, local, tid);
+  if constexpr (ROWCOL) {
+    quant_tile_task<NT, true>(d0, p0, local, wave, lane, colmax);
+  } else {
+    if (d0.q_col) {
+      if (d0.q_row)
+        quant_tile_task<NT, true>(d0, p0, local, wave, lane, colmax);
+      else
+        quant_tile_task<NT, false>(d0, p0, local, wave, lane, colmax);
+    } else {
+      quant_flat_task<NT>(d0, p0, local, tid);
+    }
+  }
 }
 
 }  // namespace
@@ -224,19 +257,30 @@ int64_t quant_tasks(const QuantDesc& d) {
 }
 
 // A grid of at most this many workgroups is resident all at once (four per
-// CU): its scale bytes are streamed (see store_scale).  Measured: the
-// 4096 x 4096 row + column launch (1024 tiles) takes 13.3 us streamed and
-// 14.0 us written back; the 64 x 2048 x 7168 grouped launch (57344 tiles)
-// 0.73 ms streamed and 0.67 ms written back.
+// CU): its scale bytes are streamed (see store_scale) and its waves load
+// everything before they store.  Measured: the 4096 x 4096 row + column
+// launch (1024 tiles) takes 13.3 us so and 13.8 us as a streaming grid; the
+// 64 x 2048 x 7168 grouped launch (57344 tiles) 0.73 ms with streamed scale
+// bytes and 0.67 ms written back.
 constexpr int64_t kResidentTasks = 4 * 256;
 
 template <class Args>
 hipError_t launch_quantize_args(const Args& a, int64_t total_tasks, hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
-  if (total_tasks <= kResidentTasks)
-    hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, true>), dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, false>), dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
+  bool rowcol = true;
+  for (int i = 0; i < a.n; ++i) rowcol &= a.d[i].q_row != nullptr && a.d[i].q_col != nullptr;
+  const dim3 grid((uint32_t)total_tasks), block(kThreads);
+  if (total_tasks <= kResidentTasks) {
+    if (rowcol)
+      hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, true, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, true, false>), grid, block, 0, s, a);
+  } else {
+    if (rowcol)
+      hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
