@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 2
+#define MXFP8_ABI_VERSION 3
 #define MXFP8_BLOCK 32
 /* Descriptors handled by one kernel launch in the grouped calls; longer
  * lists are processed in consecutive launches of at most this many.  A list
@@ -66,6 +66,9 @@ extern "C" {
  * MXFP8_PITCHED_GROUP_PER_LAUNCH. */
 #define MXFP8_GROUP_PER_LAUNCH 64
 #define MXFP8_PITCHED_GROUP_PER_LAUNCH 32
+/* A rowwise scale pitch of this value selects the MFMA order (see "Scale
+ * pitches"). */
+#define MXFP8_SCALES_MFMA ((int64_t)-1)
 
 typedef enum {
     MXFP8_OK = 0,
@@ -208,6 +211,20 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
  *   matrix product     pitch >= K/32 and a multiple of 4.
  *
  * A pitch below the plane's width is MXFP8_ERR_SHAPE.
+ *
+ * The MFMA order (rowwise scale planes only; pitch MXFP8_SCALES_MFMA).  The
+ * Mojo page's Limitations name a preshuffled scale order that one AMD matrix
+ * kernel needs, without defining it; the library's reading is the order in
+ * which its own matrix product feeds the scale operand of the block-scaled
+ * MFMA.  A [rows, cols] tensor's scales are cut into groups of 512 columns (16
+ * blocks); group g holds, row after row, each row's 16 scale bytes of that
+ * group: block b of row r sits at byte (b / 16) * rows * 16 + r * 16 + b % 16.
+ * The plane has the compact plane's size, rows * cols/32 bytes.  Required:
+ * cols % 512 == 0 (for the matrix product, K % 512 == 0), else
+ * MXFP8_ERR_SHAPE; a columnwise plane with this pitch is MXFP8_ERR_SHAPE.
+ * Quantize, the fused RMSNorm and dequantize write or read it in their one
+ * pass; the matrix product loads each 512-deep group's scales of 64 rows as
+ * one contiguous 1 KiB run instead of 64 separate 16-byte pieces.
  */
 
 /*
@@ -232,10 +249,11 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
  * float32.  The float32 result is within
  *   sum_g sum_{k in g} min(|p_k|, 2^(E_g - 13)) + (11 n + 3) 2^-24 sum_k |p_k|
  * of the exact sum, p_k = A[m, k] B[n, k], 2^E_g the group's largest
- * exponent sum, n = K / 64 rounded up to a multiple of 8.  K must be a positive multiple of 128
- * (MXFP8_ERR_SHAPE otherwise); M == 0 or N == 0 is a no-op.  sa_pitch and
- * sb_pitch are the bytes between scale rows of A and of B (0: compact, K/32;
- * see "Scale pitches").
+ * exponent sum, n = K / 64 rounded up to a multiple of 8.  K must be a
+ * positive multiple of 128 (MXFP8_ERR_SHAPE otherwise); M == 0 or N == 0 is
+ * a no-op.  sa_pitch and sb_pitch are the bytes between scale rows of A and
+ * of B (0: compact, K/32), or MXFP8_SCALES_MFMA for a plane in the MFMA order
+ * (see "Scale pitches").
  */
 mxfp8_status mxfp8_gemm(const void *qa, const void *sa, const void *qb,
                         const void *sb, int64_t M, int64_t N, int64_t K,

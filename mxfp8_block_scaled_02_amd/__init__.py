@@ -26,13 +26,18 @@ import torch
 __all__ = [
     "MXFP8Planes", "quantize", "rmsnorm_quantize", "dequantize", "quantize_grouped",
     "rmsnorm_quantize_grouped", "dequantize_grouped", "gemm", "as_fp8", "library_path", "lib",
-    "BLOCK", "ROWWISE", "COLUMNWISE",
+    "BLOCK", "ROWWISE", "COLUMNWISE", "MFMA_GROUP", "mfma_scale_shape",
 ]
 
 BLOCK = 32
-ABI_VERSION = 2
+ABI_VERSION = 3
 ROWWISE, COLUMNWISE = 0, 1
 _OUT_F32, _OUT_BF16 = 0, 1
+# Rowwise scales in the MFMA order (see include/mxfp8.h, "Scale pitches"):
+# a [rows, cols] tensor's scales as a uint8 tensor [cols / 512, rows, 16],
+# passed to the library with the pitch MXFP8_SCALES_MFMA.
+MFMA_GROUP = 512
+_SCALES_MFMA = -1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
 _lib = None
@@ -187,15 +192,34 @@ def _out(t, shape, dtype, device, name):
     return t
 
 
-def _scale_pitch(t, shape, device, name, allocate=True):
+def mfma_scale_shape(rows: int, cols: int) -> tuple:
+    """Shape of the rowwise scales of a [rows, cols] tensor in the MFMA order:
+    (cols / 512, rows, 16); block b of row r is element [b // 16, r, b % 16]."""
+    if cols % MFMA_GROUP:
+        raise ValueError("the MFMA scale order needs cols %% %d == 0, got %d" % (MFMA_GROUP, cols))
+    return (cols // MFMA_GROUP, rows, MFMA_GROUP // BLOCK)
+
+
+def _scale_pitch(t, shape, device, name, allocate=True, mfma=False):
     """A scale plane [rows, width] as (tensor, pitch).  The tensor may be a view
     of a larger, padded allocation whose rows are stride(0) bytes apart: that
-    stride goes to the library as the plane's pitch (0 when compact)."""
+    stride goes to the library as the plane's pitch (0 when compact).  A
+    contiguous 3-D tensor [width / 16, rows, 16] (or mfma=True when the plane
+    is allocated here) is a rowwise plane in the MFMA order."""
     if t is None:
         if not allocate:
             raise ValueError("%s is required" % name)
+        if mfma:
+            return torch.empty(mfma_scale_shape(shape[0], shape[1] * BLOCK), dtype=torch.uint8,
+                               device=device), _SCALES_MFMA
         return torch.empty(shape, dtype=torch.uint8, device=device), 0
     t = _bytes(t)
+    if t.dim() == 3:
+        want = mfma_scale_shape(shape[0], shape[1] * BLOCK)
+        if t.dtype != torch.uint8 or tuple(t.shape) != want or t.device != device or not t.is_contiguous():
+            raise ValueError("%s in the MFMA order must be a contiguous uint8 tensor of shape %s on %s"
+                             % (name, want, device))
+        return t, _SCALES_MFMA
     if t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) or t.device != device:
         raise ValueError("%s must be a uint8 tensor of shape %s on %s" % (name, tuple(shape), device))
     if t.dim() != 2 or (shape[1] > 1 and t.stride(1) != 1) or (
@@ -203,6 +227,12 @@ def _scale_pitch(t, shape, device, name, allocate=True):
         raise ValueError("%s must have unit column stride and a row stride >= its width" % name)
     pitch = t.stride(0) if shape[0] > 1 else shape[1]
     return t, (0 if pitch == shape[1] else pitch)
+
+
+def _mfma(scale_order: str) -> bool:
+    if scale_order not in ("row", "mfma"):
+        raise ValueError("scale_order must be 'row' or 'mfma', got %r" % (scale_order,))
+    return scale_order == "mfma"
 
 
 def padded_scale_plane(rows: int, cols: int, axis: int = 0, row_multiple: int = 1,
@@ -221,7 +251,7 @@ def padded_scale_plane(rows: int, cols: int, axis: int = 0, row_multiple: int = 
     return buf, buf[:shape[0], :shape[1]]
 
 
-def _quant_desc(x, rowwise, columnwise, out):
+def _quant_desc(x, rowwise, columnwise, out, mfma=False):
     if x.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("x must be bfloat16 or float32, got %s" % x.dtype)
     x2 = _as2d(x, "x", x.dtype)
@@ -230,21 +260,26 @@ def _quant_desc(x, rowwise, columnwise, out):
     dev = x.device
     qr = _out(o.rowwise_data, (rows, cols), torch.uint8, dev, "rowwise_data") if rowwise else None
     qc = _out(o.columnwise_data, (rows, cols), torch.uint8, dev, "columnwise_data") if columnwise else None
-    sr, pr = _scale_pitch(o.rowwise_scale, (rows, cols // BLOCK), dev, "rowwise_scale") if rowwise else (None, 0)
+    sr, pr = (_scale_pitch(o.rowwise_scale, (rows, cols // BLOCK), dev, "rowwise_scale", mfma=mfma)
+              if rowwise else (None, 0))
     sc, pc = (_scale_pitch(o.columnwise_scale, (rows // BLOCK, cols), dev, "columnwise_scale")
               if columnwise else (None, 0))
+    if pc == _SCALES_MFMA:
+        raise ValueError("columnwise_scale: the MFMA order is for rowwise scales only")
     d = _QuantDesc(_ptr(x2), rows, cols, _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc), pr, pc)
     return d, MXFP8Planes(qr, qc, sr, sc)
 
 
 def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
-             out: Optional[MXFP8Planes] = None) -> MXFP8Planes:
+             out: Optional[MXFP8Planes] = None, scale_order: str = "row") -> MXFP8Planes:
     """Quantize x [rows, cols] (bf16, or a float32 master weight) into the
     requested planes in one launch.
 
     ``out`` supplies persistent plane buffers that are overwritten in place
-    (Megatron-Core quantization.utils page, quantize_params_to_mxfp8)."""
-    d, planes = _quant_desc(x, rowwise, columnwise, out)
+    (Megatron-Core quantization.utils page, quantize_params_to_mxfp8).
+    ``scale_order="mfma"`` writes the rowwise scales in the MFMA order
+    (cols % 512 == 0), which ``gemm`` and ``dequantize`` accept as they are."""
+    d, planes = _quant_desc(x, rowwise, columnwise, out, _mfma(scale_order))
     with _on(x.device):
         if d.s_row_pitch or d.s_col_pitch:
             # padded scale planes: a one-entry grouped call carries the pitches
@@ -257,8 +292,9 @@ def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
 
 
 def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwise: bool = False,
-                     outs: Optional[Sequence[MXFP8Planes]] = None) -> list:
+                     outs: Optional[Sequence[MXFP8Planes]] = None, scale_order: str = "row") -> list:
     """Quantize a list of tensors of any shapes (all bf16 or all float32) in one launch."""
+    mfma = _mfma(scale_order)
     if not xs:
         return []
     dev, dt = xs[0].device, xs[0].dtype
@@ -266,7 +302,7 @@ def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwis
     for i, x in enumerate(xs):
         if x.device != dev or x.dtype != dt:
             raise ValueError("all tensors must share one device and one dtype")
-        d, p = _quant_desc(x, rowwise, columnwise, outs[i] if outs else None)
+        d, p = _quant_desc(x, rowwise, columnwise, outs[i] if outs else None, mfma)
         descs.append(d)
         planes.append(p)
     arr = (_QuantDesc * len(descs))(*descs)
@@ -276,7 +312,7 @@ def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwis
     return planes
 
 
-def _norm_desc(x, gamma, weight_offset, eps, out):
+def _norm_desc(x, gamma, weight_offset, eps, out, mfma=False):
     x2 = _as2d(x, "x")
     rows, cols = x2.shape
     g = _as2d(gamma, "gamma", device=x.device)
@@ -286,20 +322,21 @@ def _norm_desc(x, gamma, weight_offset, eps, out):
     o = out or (None, None, None)
     normed = _out(o[0], (rows, cols), torch.bfloat16, dev, "normed")
     q = _out(o[1], (rows, cols), torch.uint8, dev, "q")
-    s, pitch = _scale_pitch(o[2], (rows, cols // BLOCK), dev, "s")
+    s, pitch = _scale_pitch(o[2], (rows, cols // BLOCK), dev, "s", mfma=mfma)
     d = _NormDesc(_ptr(x2), _ptr(g), float(weight_offset), float(eps), rows, cols,
                   _ptr(normed), _ptr(q), _ptr(s), pitch)
     return d, (normed, q, s)
 
 
 def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, weight_offset: float = 0.0,
-                     eps: float = 1e-6, out=None):
+                     eps: float = 1e-6, out=None, scale_order: str = "row"):
     """RMSNorm (sum of squares and rstd in float64, the products in float32)
     rounded once to bf16, then its rowwise MXFP8 plane.
 
     Returns (normed bf16 [rows, cols], data uint8 [rows, cols], scales uint8
-    [rows, cols/32]); the bytes equal ``quantize(normed)``."""
-    d, res = _norm_desc(x, gamma, weight_offset, eps, out)
+    [rows, cols/32], or [cols/512, rows, 16] with ``scale_order="mfma"``); the
+    bytes equal ``quantize(normed)``."""
+    d, res = _norm_desc(x, gamma, weight_offset, eps, out, _mfma(scale_order))
     with _on(x.device):
         if d.s_row_pitch:
             _check(lib().mxfp8_rmsnorm_quantize_grouped((_NormDesc * 1)(d), 1, _stream(x.device)))
@@ -310,8 +347,9 @@ def rmsnorm_quantize(x: torch.Tensor, gamma: torch.Tensor, weight_offset: float 
     return res
 
 
-def rmsnorm_quantize_grouped(xs, gammas, weight_offsets, epss, outs=None) -> list:
+def rmsnorm_quantize_grouped(xs, gammas, weight_offsets, epss, outs=None, scale_order: str = "row") -> list:
     """Fused RMSNorm + rowwise quantize over a list of tensors in one launch."""
+    mfma = _mfma(scale_order)
     if not xs:
         return []
     dev = xs[0].device
@@ -319,7 +357,7 @@ def rmsnorm_quantize_grouped(xs, gammas, weight_offsets, epss, outs=None) -> lis
     for i, x in enumerate(xs):
         if x.device != dev:
             raise ValueError("all tensors must be on one device")
-        d, r = _norm_desc(x, gammas[i], weight_offsets[i], epss[i], outs[i] if outs else None)
+        d, r = _norm_desc(x, gammas[i], weight_offsets[i], epss[i], outs[i] if outs else None, mfma)
         descs.append(d)
         res.append(r)
     arr = (_NormDesc * len(descs))(*descs)
@@ -335,6 +373,8 @@ def _deq_desc(q, s, axis, dtype, out):
     if not s.is_cuda:
         raise ValueError("s must be a GPU tensor")
     s2, pitch = _scale_pitch(s, want, q.device, "s", allocate=False)
+    if pitch == _SCALES_MFMA and axis != ROWWISE:
+        raise ValueError("s: the MFMA order is for rowwise scales only")
     o = _out(out, (rows, cols), dtype, q.device, "out")
     return _DeqDesc(_ptr(q2), _ptr(s2), rows, cols, int(axis), _ptr(o), pitch), o
 
@@ -381,7 +421,8 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
          dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[M, N] = A . B^T from rowwise planes A = (qa [M, K], sa [M, K/32]) and
     B = (qb [N, K], sb [N, K/32]) (quantization.utils page, mm_mxfp8: a
-    quantized activation times a pre-quantized weight [out, in])."""
+    quantized activation times a pre-quantized weight [out, in]).  Either
+    scale plane may be in the MFMA order ([K/512, rows, 16], K % 512 == 0)."""
     code = _out_code(dtype)
     qa2 = _as2d(qa, "qa", torch.uint8)
     qb2 = _as2d(qb, "qb", torch.uint8, device=qa.device)
@@ -389,7 +430,8 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
     N = qb2.shape[0]
     if qb2.shape[1] != K:
         raise ValueError("gemm: planes must be qa [M, K], sa [M, K/32], qb [N, K], sb [N, K/32]")
-    # scale planes may be views of padded allocations (rows a pitch apart)
+    # scale planes may be views of padded allocations (rows a pitch apart) or
+    # 3-D planes in the MFMA order
     sa2, pa = _scale_pitch(sa, (M, K // BLOCK), qa.device, "sa", allocate=False)
     sb2, pb = _scale_pitch(sb, (N, K // BLOCK), qa.device, "sb", allocate=False)
     o = _out(out, (M, N), dtype, qa.device, "out")

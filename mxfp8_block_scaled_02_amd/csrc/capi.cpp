@@ -28,9 +28,13 @@ bool fits(int64_t rows, int64_t cols) {
 // when its plane has a pitch of its own.
 bool flat_blocks_fit(int64_t rows, int64_t cols) { return rows * (cols / MXFP8_BLOCK) <= (int64_t)UINT32_MAX; }
 
+// A rowwise scale plane in the MFMA order needs whole 512-element groups.
+bool mfma_order_ok(int64_t pitch, int64_t cols) { return pitch != MXFP8_SCALES_MFMA || cols % 512 == 0; }
+
 mxfp8_status check_quant(const mxfp8_quant_desc& d) {
   if (d.rows < 0 || d.cols < 0 || !fits(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
-  if (d.s_row_pitch < 0 || d.s_col_pitch < 0) return MXFP8_ERR_SHAPE;
+  if ((d.s_row_pitch < 0 && d.s_row_pitch != MXFP8_SCALES_MFMA) || d.s_col_pitch < 0) return MXFP8_ERR_SHAPE;
+  if (!mfma_order_ok(d.s_row_pitch, d.cols)) return MXFP8_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   const bool row = d.q_row || d.s_row, col = d.q_col || d.s_col;
   if ((d.q_row == nullptr) != (d.s_row == nullptr)) return MXFP8_ERR_NULL;
@@ -42,7 +46,9 @@ mxfp8_status check_quant(const mxfp8_quant_desc& d) {
   if (misaligned(d.x) || misaligned(d.q_row) || misaligned(d.s_row) ||
       misaligned(d.q_col) || misaligned(d.s_col))
     return MXFP8_ERR_ALIGN;
-  if (row && d.s_row_pitch) {
+  if (row && d.s_row_pitch == MXFP8_SCALES_MFMA) {
+    if (!col && !flat_blocks_fit(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
+  } else if (row && d.s_row_pitch) {
     if (d.s_row_pitch < d.cols / MXFP8_BLOCK || !fits(d.rows, d.s_row_pitch)) return MXFP8_ERR_SHAPE;
     if (!col && d.s_row_pitch != d.cols / MXFP8_BLOCK && !flat_blocks_fit(d.rows, d.cols))
       return MXFP8_ERR_SHAPE;
@@ -58,14 +64,15 @@ mxfp8_status check_norm(const mxfp8_norm_desc& d) {
   if (d.rows < 0 || d.cols < 0 || d.rows > INT32_MAX || d.cols > INT32_MAX)
     return MXFP8_ERR_SHAPE;
   if (!isfinite(d.eps) || d.eps < 0.0f) return MXFP8_ERR_ARG;
-  if (d.s_row_pitch < 0) return MXFP8_ERR_SHAPE;
+  if (d.s_row_pitch < 0 && d.s_row_pitch != MXFP8_SCALES_MFMA) return MXFP8_ERR_SHAPE;
+  if (!mfma_order_ok(d.s_row_pitch, d.cols)) return MXFP8_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   if (!d.x || !d.gamma || !d.normed || !d.q_row || !d.s_row) return MXFP8_ERR_NULL;
   if (d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
   if (misaligned(d.x) || misaligned(d.gamma) || misaligned(d.normed) ||
       misaligned(d.q_row) || misaligned(d.s_row))
     return MXFP8_ERR_ALIGN;
-  if (d.s_row_pitch && (d.s_row_pitch < d.cols / MXFP8_BLOCK || !fits(d.rows, d.s_row_pitch)))
+  if (d.s_row_pitch > 0 && (d.s_row_pitch < d.cols / MXFP8_BLOCK || !fits(d.rows, d.s_row_pitch)))
     return MXFP8_ERR_SHAPE;
   return MXFP8_OK;
 }
@@ -73,14 +80,17 @@ mxfp8_status check_norm(const mxfp8_norm_desc& d) {
 mxfp8_status check_deq(const mxfp8_deq_desc& d) {
   if (d.axis != MXFP8_ROWWISE && d.axis != MXFP8_COLUMNWISE) return MXFP8_ERR_ARG;
   if (d.rows < 0 || d.cols < 0 || !fits(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
-  if (d.s_pitch < 0) return MXFP8_ERR_SHAPE;
+  if (d.s_pitch < 0 && (d.s_pitch != MXFP8_SCALES_MFMA || d.axis != MXFP8_ROWWISE)) return MXFP8_ERR_SHAPE;
+  if (!mfma_order_ok(d.s_pitch, d.cols)) return MXFP8_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   if (!d.q || !d.s || !d.out) return MXFP8_ERR_NULL;
   if (d.axis == MXFP8_ROWWISE && d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
   if (d.axis == MXFP8_COLUMNWISE && (d.rows % MXFP8_BLOCK || d.cols % 8))
     return MXFP8_ERR_SHAPE;
   if (misaligned(d.q) || misaligned(d.s) || misaligned(d.out)) return MXFP8_ERR_ALIGN;
-  if (d.s_pitch) {
+  if (d.s_pitch == MXFP8_SCALES_MFMA) {
+    if (!flat_blocks_fit(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
+  } else if (d.s_pitch) {
     const int64_t srows = d.axis == MXFP8_ROWWISE ? d.rows : d.rows / MXFP8_BLOCK;
     if (!fits(srows, d.s_pitch)) return MXFP8_ERR_SHAPE;
     if (d.axis == MXFP8_ROWWISE) {
@@ -194,16 +204,27 @@ mx::DeqDesc to_internal(const mxfp8_deq_desc& d) {
 }
 
 using QuantItem = Item<mx::QuantDesc, mx::QuantPitch>;
-using NormItem = Item<mx::NormDesc, int64_t>;
-using DeqItem = Item<mx::DeqDesc, int64_t>;
+using NormItem = Item<mx::NormDesc, mx::ScaleStride>;
+using DeqItem = Item<mx::DeqDesc, mx::ScaleStride>;
+
+// Strides of a rowwise scale plane of `rows` rows and width w from its pitch
+// argument (0 compact, MXFP8_SCALES_MFMA, or a row pitch).
+mx::ScaleStride row_scale_stride(int64_t pitch, int64_t rows, int64_t w) {
+  if (pitch == MXFP8_SCALES_MFMA) return {16, rows * 16};
+  return {pitch ? pitch : w, 16};
+}
+
+bool compact(mx::ScaleStride st, int64_t w) { return st.row == w && st.grp == 16; }
 
 QuantItem to_item(const mxfp8_quant_desc& d) {
   QuantItem it;
   it.d = to_internal(d);
   const int64_t wr = d.cols / MXFP8_BLOCK, wc = d.cols;
-  it.p.s_row = d.s_row_pitch ? d.s_row_pitch : wr;
+  const mx::ScaleStride sr = row_scale_stride(d.s_row_pitch, d.rows, wr);
+  it.p.s_row = sr.row;
+  it.p.s_grp = sr.grp;
   it.p.s_col = d.s_col_pitch ? d.s_col_pitch : wc;
-  it.pitched = (d.s_row && it.p.s_row != wr) || (d.s_col && it.p.s_col != wc);
+  it.pitched = (d.s_row && !compact(sr, wr)) || (d.s_col && it.p.s_col != wc);
   return it;
 }
 
@@ -211,17 +232,22 @@ NormItem to_item(const mxfp8_norm_desc& d) {
   NormItem it;
   it.d = to_internal(d);
   const int64_t w = d.cols / MXFP8_BLOCK;
-  it.p = d.s_row_pitch ? d.s_row_pitch : w;
-  it.pitched = it.p != w;
+  it.p = row_scale_stride(d.s_row_pitch, d.rows, w);
+  it.pitched = !compact(it.p, w);
   return it;
 }
 
 DeqItem to_item(const mxfp8_deq_desc& d) {
   DeqItem it;
   it.d = to_internal(d);
-  const int64_t w = d.axis == MXFP8_COLUMNWISE ? d.cols : d.cols / MXFP8_BLOCK;
-  it.p = d.s_pitch ? d.s_pitch : w;
-  it.pitched = it.p != w;
+  if (d.axis == MXFP8_COLUMNWISE) {
+    it.p = {d.s_pitch ? d.s_pitch : d.cols, 16};
+    it.pitched = it.p.row != d.cols;
+  } else {
+    const int64_t w = d.cols / MXFP8_BLOCK;
+    it.p = row_scale_stride(d.s_pitch, d.rows, w);
+    it.pitched = !compact(it.p, w);
+  }
   return it;
 }
 
@@ -343,24 +369,26 @@ mxfp8_status mxfp8_gemm(const void* qa, const void* sa, const void* qb, const vo
                         void* out, mxfp8_out_dtype out_dtype, void* stream) {
   if (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16) return MXFP8_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || !fits(M, K) || !fits(N, K) || !fits(M, N)) return MXFP8_ERR_SHAPE;
-  if (sa_pitch < 0 || sb_pitch < 0) return MXFP8_ERR_SHAPE;
+  if ((sa_pitch < 0 && sa_pitch != MXFP8_SCALES_MFMA) || (sb_pitch < 0 && sb_pitch != MXFP8_SCALES_MFMA))
+    return MXFP8_ERR_SHAPE;
+  if (!mfma_order_ok(sa_pitch, K) || !mfma_order_ok(sb_pitch, K)) return MXFP8_ERR_SHAPE;
   if (M == 0 || N == 0) return MXFP8_OK;
   if (K == 0 || K % 128) return MXFP8_ERR_SHAPE;
   if (!qa || !sa || !qb || !sb || !out) return MXFP8_ERR_NULL;
   if (misaligned(qa) || misaligned(sa) || misaligned(qb) || misaligned(sb) || misaligned(out))
     return MXFP8_ERR_ALIGN;
   const int64_t kb = K / MXFP8_BLOCK;
-  if (!sa_pitch) sa_pitch = kb;
-  if (!sb_pitch) sb_pitch = kb;
-  if (sa_pitch < kb || sb_pitch < kb || !fits(M, sa_pitch) || !fits(N, sb_pitch)) return MXFP8_ERR_SHAPE;
-  if (sa_pitch % 4 || sb_pitch % 4) return MXFP8_ERR_ALIGN;
+  if (sa_pitch > 0 && (sa_pitch < kb || !fits(M, sa_pitch))) return MXFP8_ERR_SHAPE;
+  if (sb_pitch > 0 && (sb_pitch < kb || !fits(N, sb_pitch))) return MXFP8_ERR_SHAPE;
+  if ((sa_pitch > 0 && sa_pitch % 4) || (sb_pitch > 0 && sb_pitch % 4)) return MXFP8_ERR_ALIGN;
+  const mx::ScaleStride sas = row_scale_stride(sa_pitch, M, kb), sbs = row_scale_stride(sb_pitch, N, kb);
   // 64 x 32 outputs bound the smallest workgroup tile of every route, so this
   // keeps grid sizes and tile indices within 32 bits
   if (((M + 63) / 64) * ((N + 31) / 32) > kMaxGemmTiles) return MXFP8_ERR_SHAPE;
   (void)hipGetLastError();
   return hip_status(mx::launch_gemm(static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa),
                                     static_cast<const uint8_t*>(qb), static_cast<const uint8_t*>(sb),
-                                    M, N, K, sa_pitch, sb_pitch, out, out_dtype == MXFP8_OUT_BF16,
+                                    M, N, K, sas, sbs, out, out_dtype == MXFP8_OUT_BF16,
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -39,7 +39,7 @@ __device__ __forceinline__ void put4(void* out, bool bf16, int64_t e, uint32_t q
 
 // Rowwise planes, walked flat in 4-element units: unit u of a wave task is
 // lane + 64 u, so every load and store instruction covers contiguous memory.
-__device__ void deq_flat_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int64_t task, int lane) {
+__device__ void deq_flat_task(const DeqDesc& d, ScaleStride ss, bool bf16, int64_t task, int lane) {
   const int64_t nunits = d.rows * d.cols / 4;
   const int64_t base = task * (int64_t)(kWave * kDeqUnroll) + lane;
   uint32_t q[kDeqUnroll], s[kDeqUnroll];
@@ -48,7 +48,7 @@ __device__ void deq_flat_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int6
     const int64_t p = base + u * kWave;
     const bool ok = p < nunits;
     q[u] = ok ? load4(reinterpret_cast<const uint32_t*>(d.q) + p) : 0u;
-    s[u] = ok ? load1_cached(d.s + pitched_block(p >> 3, d.cols >> 5, s_pitch)) : 0u;   // 8 units per block
+    s[u] = ok ? load1_cached(d.s + pitched_block(p >> 3, d.cols >> 5, ss)) : 0u;   // 8 units per block
   }
 #pragma unroll
   for (int u = 0; u < kDeqUnroll; ++u) {
@@ -63,14 +63,14 @@ __device__ void deq_flat_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int6
 
 // Columnwise planes: kDeqRows rows x 256 columns per wave task; lane l owns
 // columns 4l .. 4l+3 and reads their scale bytes once.
-__device__ void deq_col_task(const DeqDesc& d, int64_t s_pitch, bool bf16, int64_t task, int lane) {
+__device__ void deq_col_task(const DeqDesc& d, ScaleStride ss, bool bf16, int64_t task, int lane) {
   const int64_t cols = d.cols;
   const int64_t col_tiles = (cols + kDeqTileCols - 1) / kDeqTileCols;
   const int64_t r0 = (task / col_tiles) * kDeqRows;
   const int64_t c = (task % col_tiles) * kDeqTileCols + (int64_t)lane * 4;
   if (c >= cols) return;                              // cols % 8 == 0: whole units only
   // rows r0 .. r0 + kDeqRows - 1 lie in one 32-row block (kDeqRows divides 32)
-  const uint32_t sb = load4_cached(d.s + (r0 / kBlock) * s_pitch + c);
+  const uint32_t sb = load4_cached(d.s + (r0 / kBlock) * ss.row + c);
   float sc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) sc[k] = e8m0_value((sb >> (8 * k)) & 0xFFu);
@@ -91,14 +91,14 @@ __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const Args a
   // table size (the empty asm keeps those loads ahead of the branch)
   DeqDesc d0 = a.d[0];
   int32_t total0 = a.task_start[1];
-  int64_t p0 = 0;
+  ScaleStride p0 = {0, 0};
   if constexpr (Args::kPitched) {
     p0 = a.pitch(0);
-    asm volatile("" : "+s"(p0));
+    asm volatile("" : "+s"(p0.row), "+s"(p0.grp));
   }
   asm volatile("" : "+s"(d0.q), "+s"(d0.s), "+s"(d0.out), "+s"(d0.rows), "+s"(d0.cols), "+s"(d0.axis),
                "+s"(total0));
-  if constexpr (!Args::kPitched) p0 = d0.axis ? d0.cols : d0.cols >> 5;
+  if constexpr (!Args::kPitched) p0 = {d0.axis ? d0.cols : d0.cols >> 5, 16};
   if (a.n == 1) {
     if (task >= total0) return;
     if (d0.axis == 0)
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const Args a
   if (task >= a.task_start[a.n]) return;
   const int i = find_desc(a.task_start, a.n, task);
   const DeqDesc d = a.d[i];
-  const int64_t pi = Args::kPitched ? a.pitch(i) : (d.axis ? d.cols : d.cols >> 5);
+  const ScaleStride pi = Args::kPitched ? a.pitch(i) : ScaleStride{d.axis ? d.cols : d.cols >> 5, 16};
   const int64_t local = task - a.task_start[i];
   if (d.axis == 0)
     deq_flat_task(d, pi, a.out_bf16 != 0, local, lane);

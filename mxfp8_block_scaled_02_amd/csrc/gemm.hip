@@ -67,6 +67,8 @@ struct GemmParams {
   void* out;
   int64_t M, N, K;
   int64_t sa_ld, sb_ld;       // bytes between scale rows of A and of B
+  int64_t sa_gs, sb_gs;       // bytes between 16-block scale groups of a row
+                              // (16 compact or padded, rows * 16 in the MFMA order)
   int32_t out_bf16;
   int32_t tiles_m, tiles_n;
 };
@@ -171,14 +173,23 @@ __device__ __forceinline__ void load_stage(const uint8_t* base, int64_t rows, in
   }
 }
 
-// the 16 scale bytes of 512 k (k blocks kb0 .. kb0+15) of rows r0 .. r0+255
-// (rows ld bytes apart), one row per lane: wave w loads rows 64 w .. 64 w + 63
+// the 16 scale bytes of 512 k (k blocks kb0 .. kb0+15) of rows r0 .. r0+255,
+// one row per lane: wave w loads rows 64 w .. 64 w + 63.  Rows are ld bytes
+// apart and 16-block groups gs (in the MFMA order, 16 and rows * 16: the wave
+// reads 1 KiB in one run).
 __device__ __forceinline__ void load_scales(const uint8_t* s, int64_t rows, int64_t r0,
-                                            int64_t ld, int64_t kb0, uint8_t* lds, int wave,
-                                            int lane) {
+                                            int64_t ld, int64_t gs, int64_t kb0, uint8_t* lds,
+                                            int wave, int lane) {
   int64_t row = r0 + 64 * wave + lane;
   row = row < rows ? row : rows - 1;
-  __builtin_amdgcn_global_load_lds(s + row * ld + kb0, (lds_ptr)(lds + 1024 * wave), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(s + row * ld + kb0 + (kb0 >> 4) * (gs - 16), (lds_ptr)(lds + 1024 * wave),
+                                   16, 0, 0);
+}
+
+// Scale word w (the 4 blocks of 128 k) of a row starting at row_base, with
+// 16-block groups gs bytes apart: a word never straddles a group.
+__device__ __forceinline__ const uint8_t* scale_word(const uint8_t* row_base, int64_t w, int64_t gs) {
+  return row_base + w * 4 + (w >> 2) * (gs - 16);
 }
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) (expcnt left alone)
@@ -257,8 +268,8 @@ struct TileRing {
       const int64_t kb0 = min((tt / kGroup) * 16, (int)(K / kBlock) - 16);
       const int gpar = (int)((t / kGroup) & 1);
       uint8_t* sc = gpar ? s_scale1 : s_scale0;
-      load_scales(p.sa, p.M, m0, p.sa_ld, kb0, sc, wave, lane);
-      load_scales(p.sb, p.N, n0, p.sb_ld, kb0, sc + kScBytes, wave, lane);
+      load_scales(p.sa, p.M, m0, p.sa_ld, p.sa_gs, kb0, sc, wave, lane);
+      load_scales(p.sb, p.N, n0, p.sb_ld, p.sb_gs, kb0, sc + kScBytes, wave, lane);
     }
   }
 
@@ -487,8 +498,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
   auto fetch = [&](int64_t kt, Tile128Regs& c) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      c.sa[i] = *reinterpret_cast<const uint32_t*>(gsa[i] + kt * 4);
-      c.sb[i] = *reinterpret_cast<const uint32_t*>(gsb[i] + kt * 4);
+      c.sa[i] = *reinterpret_cast<const uint32_t*>(scale_word(gsa[i], kt, p.sa_gs));
+      c.sb[i] = *reinterpret_cast<const uint32_t*>(scale_word(gsb[i], kt, p.sb_gs));
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -669,11 +680,12 @@ struct Skinny {
       if (i < iters) {                            // the same for the whole wave
         const int e = min(lane + 64 * i, n - 1);
         const int r = (int)(((uint32_t)e * m) >> 16), k = e - r * U;
-        v[0][i] = *reinterpret_cast<const uint32_t*>(p.sb + min(n0 + r, p.N - 1) * p.sb_ld + (u0 + k) * 4);
+        v[0][i] = *reinterpret_cast<const uint32_t*>(
+            scale_word(p.sb + min(n0 + r, p.N - 1) * p.sb_ld, u0 + k, p.sb_gs));
 #pragma unroll
         for (int t = 0; t < MT; ++t)
           v[1 + t][i] = *reinterpret_cast<const uint32_t*>(
-              p.sa + min((int64_t)(32 * t + r), p.M - 1) * p.sa_ld + (u0 + k) * 4);
+              scale_word(p.sa + min((int64_t)(32 * t + r), p.M - 1) * p.sa_ld, u0 + k, p.sa_gs));
       }
     }
 #pragma unroll
@@ -683,6 +695,44 @@ struct Skinny {
         const int r = (int)(((uint32_t)e * m) >> 16), k = e - r * U;
 #pragma unroll
         for (int t = 0; t <= MT; ++t) sreg[t * staged_tile<MT>() + r * staged_stride<MT>() + k] = v[t][i];
+      }
+    }
+  }
+
+  // STAGED, both planes in the MFMA order (then K % 512 == 0): the 16-byte
+  // pieces (4 words) of the groups that hold units u0 .. u0 + U - 1, one
+  // piece a lane, consecutive lanes on consecutive rows of a group, so that a
+  // load reads two runs of 512 bytes.  Words of a piece outside the range are
+  // not written.  All loads go out before the first LDS write.
+  __device__ __forceinline__ void stage_scales_grouped(int64_t u0, int U) const {
+    constexpr int kIters = (staged_units<MT>() / 4 + 2 + 1) / 2;
+    const int64_t g0 = u0 >> 2;
+    const int ng = (int)(((u0 + U - 1) >> 2) - g0 + 1), iters = (ng + 1) / 2;
+    const int r = lane & 31;
+    u32x4 v[1 + MT][kIters];
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      if (i < iters) {                            // the same for the whole wave
+        const int64_t g = g0 + min(2 * i + (lane >> 5), ng - 1);
+        v[0][i] = *reinterpret_cast<const u32x4*>(p.sb + min(n0 + r, p.N - 1) * p.sb_ld + g * p.sb_gs);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          v[1 + t][i] = *reinterpret_cast<const u32x4*>(
+              p.sa + min((int64_t)(32 * t + r), p.M - 1) * p.sa_ld + g * p.sa_gs);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int gi = 2 * i + (lane >> 5);
+      if (i < iters && gi < ng) {
+        const int k0 = (int)((g0 + gi) * 4 - u0);   // unit of word 0, relative to u0
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (k0 + j >= 0 && k0 + j < U) {
+#pragma unroll
+            for (int t = 0; t <= MT; ++t) sreg[t * staged_tile<MT>() + r * staged_stride<MT>() + k0 + j] = v[t][i][j];
+          }
+        }
       }
     }
   }
@@ -699,10 +749,15 @@ struct Skinny {
   // so a wait for an early load leaves the later ones in flight.
   __device__ __forceinline__ void load(int64_t u, SkinnyUnit<MT>& c, bool scales) const {
     if (scales) {                                 // PAIRED only; K >= 256
-      const int64_t ps = min(u, units - 2);       // both words inside the row
+      // both words inside the row.  A pair that is used starts at an even
+      // unit (u, or units - 2 with units % 4 == 0 in the MFMA order), so it
+      // never straddles a 16-block group; a pair loaded past a wave's range
+      // may start at an odd unit, but never in the row's last group, so it
+      // stays inside the plane.
+      const int64_t ps = min(u, units - 2);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) c.sa[t] = *reinterpret_cast<const u32x2_a4*>(psa[t] + ps * 4);
-      c.sb = *reinterpret_cast<const u32x2_a4*>(psb + ps * 4);
+      for (int t = 0; t < MT; ++t) c.sa[t] = *reinterpret_cast<const u32x2_a4*>(scale_word(psa[t], ps, p.sa_gs));
+      c.sb = *reinterpret_cast<const u32x2_a4*>(scale_word(psb, ps, p.sb_gs));
       c.off = u - ps;
     }
 #pragma unroll
@@ -778,8 +833,14 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
   const int fr = lane & 31, h = lane >> 5;
   const int64_t n0 = (int64_t)blockIdx.x * 32;
   const int64_t units = p.K / 128;
-  const int64_t u0 = units * wave / kSkinnyWaves, u1 = units * (wave + 1) / kSkinnyWaves;
   constexpr bool kPaired = SC == kSkinnyPaired;
+  // PAIRED: every wave's range starts at an even unit, so each pair of scale
+  // words it uses (units u, u + 1 with u even) lies inside one 16-block group
+  const auto split = [&](int w) -> int64_t {
+    if (w == kSkinnyWaves) return units;
+    return kPaired ? 2 * ((units / 2) * w / kSkinnyWaves) : units * w / kSkinnyWaves;
+  };
+  const int64_t u0 = split(wave), u1 = split(wave + 1);
 
   const Skinny<MT, SC> sk(p, wave, lane, n0, lds, slds);
   v16f acc[MT];
@@ -796,7 +857,12 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
     SkinnyUnit<MT> c0, c1;
     sk.load(u0, c0, kPaired);
     sk.load(min(u0 + 1, u1 - 1), c1, false);
-    if constexpr (!kPaired) sk.stage_scales(u0, (int)(u1 - u0));
+    if constexpr (!kPaired) {
+      if (p.sa_gs != 16 && p.sb_gs != 16)
+        sk.stage_scales_grouped(u0, (int)(u1 - u0));
+      else
+        sk.stage_scales(u0, (int)(u1 - u0));
+    }
     for (int64_t u = u0; u < u1; u += 2) {
       skinny_pin();
       uint32_t sa[MT], sb, sa1[MT], sb1;
@@ -868,13 +934,14 @@ void launch_skinny(const GemmParams& p, int64_t workgroups, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
-                       int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
+                       int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
                        void* out, bool out_bf16, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmParams p;
   p.qa = qa; p.sa = sa; p.qb = qb; p.sb = sb; p.out = out;
   p.M = M; p.N = N; p.K = K;
-  p.sa_ld = sa_pitch; p.sb_ld = sb_pitch;
+  p.sa_ld = sa_stride.row; p.sb_ld = sb_stride.row;
+  p.sa_gs = sa_stride.grp; p.sb_gs = sb_stride.grp;
   p.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t skinny = (N + 31) / 32;
   if (M <= 32) {

@@ -44,10 +44,17 @@ struct QuantDesc {
   uint8_t* s_col;  // NULL: columnwise plane not requested
   int64_t rows, cols;
 };
-// Bytes from one row of a scale plane to the next.  Compact planes have the
-// plane's width; a padded allocation (a consumer's layout) has more.
+// Where a rowwise scale byte lives: block b of row r at
+// r * row + (b / 16) * grp + b % 16 (see scale_at).  Compact planes have
+// row = the plane's width and grp = 16; a padded allocation (a consumer's
+// layout) has a larger row; the MFMA order has row = 16 and grp = rows * 16.
+struct ScaleStride {
+  int64_t row, grp;
+};
+// Scale strides of a quantize call: rowwise (row, grp) and the columnwise
+// plane's row pitch (its rows are always contiguous).
 struct QuantPitch {
-  int64_t s_row, s_col;
+  int64_t s_row, s_col, s_grp;
 };
 // Compact planes: the pitch follows from the shape.
 struct QuantArgs {
@@ -56,7 +63,7 @@ struct QuantArgs {
   int32_t n;
   int32_t task_start[kMax + 1];
   QuantDesc d[kMax];
-  __device__ QuantPitch pitch(int i) const { return {d[i].cols >> 5, d[i].cols}; }
+  __device__ QuantPitch pitch(int i) const { return {d[i].cols >> 5, d[i].cols, 16}; }
 };
 // Planes with pitches of their own (fewer tensors per launch: the argument
 // block stays under 4 KiB).
@@ -97,7 +104,7 @@ struct NormArgs {
   int32_t n;
   int32_t task_start[kMax + 1];
   NormDesc d[kMax];
-  __device__ int64_t pitch(int i) const { return d[i].cols >> 5; }
+  __device__ ScaleStride pitch(int i) const { return {d[i].cols >> 5, 16}; }
 };
 struct NormArgsPitched {
   static constexpr int kMax = kPitchedGroupMax;
@@ -105,8 +112,8 @@ struct NormArgsPitched {
   int32_t n;
   int32_t task_start[kMax + 1];
   NormDesc d[kMax];
-  int64_t p[kMax];   // bytes between rows of the scale plane
-  __device__ int64_t pitch(int i) const { return p[i]; }
+  ScaleStride p[kMax];
+  __device__ ScaleStride pitch(int i) const { return p[i]; }
 };
 // Kernel shape from the longest row of a launch and its total row count:
 // waves per row and chunks per lane (see rmsnorm_quantize.hip).  A task is
@@ -135,7 +142,7 @@ struct DeqArgs {
   int32_t out_bf16;
   int32_t task_start[kMax + 1];
   DeqDesc d[kMax];
-  __device__ int64_t pitch(int i) const { return d[i].axis ? d[i].cols : d[i].cols >> 5; }
+  __device__ ScaleStride pitch(int i) const { return {d[i].axis ? d[i].cols : d[i].cols >> 5, 16}; }
 };
 struct DeqArgsPitched {
   static constexpr int kMax = kPitchedGroupMax;
@@ -144,8 +151,8 @@ struct DeqArgsPitched {
   int32_t out_bf16;
   int32_t task_start[kMax + 1];
   DeqDesc d[kMax];
-  int64_t p[kMax];   // bytes between rows of the scale plane
-  __device__ int64_t pitch(int i) const { return p[i]; }
+  ScaleStride p[kMax];   // columnwise planes: p.row is the row pitch
+  __device__ ScaleStride pitch(int i) const { return p[i]; }
 };
 int64_t deq_tasks(const DeqDesc& d);
 hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s);
@@ -154,9 +161,10 @@ hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipSt
 // ---- MXFP8 matrix product -------------------------------------------------
 // out[M, N] (float32, or bf16 if out_bf16) = A . B^T for rowwise planes
 // A = (qa [M, K], sa [M, K/32]), B = (qb [N, K], sb [N, K/32]); K % 128 == 0.
-// Scale rows are sa_pitch and sb_pitch bytes apart (multiples of 4).
+// The scale planes' strides are sa and sb (row strides multiples of 4; the
+// MFMA order only with K % 512 == 0).
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
-                       int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
+                       int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
                        void* out, bool out_bf16, hipStream_t s);
 
 // The tensor of a launch's table that task belongs to: the last i with
@@ -170,13 +178,20 @@ __device__ __forceinline__ int find_desc(const int32_t* start, int n, int32_t ta
   return lo;
 }
 
-// Scale index of flat block b of a plane with bpr blocks per row, stored
-// with rows pitch bytes apart (b < 2^32 whenever pitch != bpr).
-__device__ __forceinline__ int64_t pitched_block(int64_t b, int64_t bpr, int64_t pitch) {
-  if (pitch == bpr) return b;
+// Byte offset of the scale of block b of row r (see ScaleStride):
+// r * row + (b / 16) * grp + b % 16, written so that a grp known to be 16
+// leaves r * row + b.
+__device__ __forceinline__ int64_t scale_at(int64_t r, int64_t b, int64_t row, int64_t grp) {
+  return r * row + b + (b >> 4) * (grp - 16);
+}
+
+// Scale offset of flat block b of a plane with bpr blocks per row
+// (b < 2^32 whenever the plane is not compact).
+__device__ __forceinline__ int64_t pitched_block(int64_t b, int64_t bpr, ScaleStride st) {
+  if (st.row == bpr && st.grp == 16) return b;
   const uint32_t ub = (uint32_t)b, ubpr = (uint32_t)bpr;
   const uint32_t r = ub / ubpr;
-  return (int64_t)r * pitch + (ub - r * ubpr);
+  return scale_at(r, ub - r * ubpr, st.row, st.grp);
 }
 
 }  // namespace mx

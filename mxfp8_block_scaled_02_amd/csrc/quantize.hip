@@ -60,7 +60,7 @@ __device__ void quant_flat_pieces(const QuantDesc& d, const QuantPitch& pitch, i
       for (int h = 0; h < kCh; ++h)
         store8(d.q_row + p * kLaneCols + h * kChunk, encode_chunk_row(v[u][h], rs));
       if ((tid & (kBlock / kLaneCols - 1)) == 0)
-        store_scale<NT>(d.s_row + pitched_block(p * kLaneCols / kBlock, d.cols >> 5, pitch.s_row), rs.sbyte);
+        store_scale<NT>(d.s_row + pitched_block(p * kLaneCols / kBlock, d.cols >> 5, ScaleStride{pitch.s_row, pitch.s_grp}), rs.sbyte);
     }
   }
 }
@@ -196,7 +196,7 @@ __device__ void quant_tile_task(const QuantDesc& d, const QuantPitch& pitch, int
   if (ROW && (lane & (kBlock / kLaneCols - 1)) == 0) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r)
-      store_scale<NT>(d.s_row + (r0 + r) * pitch.s_row + (ce >> 5), row_sb[r / 4] >> (8 * (r % 4)));
+      store_scale<NT>(d.s_row + scale_at(r0 + r, ce >> 5, pitch.s_row, pitch.s_grp), row_sb[r / 4] >> (8 * (r % 4)));
   }
 }
 
@@ -215,20 +215,20 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const Args a) 
   // table size (the empty asm keeps those loads ahead of the branch), so the
   // first global load waits for one scalar round trip instead of two
   QuantDesc d0 = a.d[0];
-  QuantPitch p0 = {0, 0};
+  QuantPitch p0 = {0, 0, 0};
   if constexpr (Args::kPitched) {
     p0 = a.pitch(0);
-    asm volatile("" : "+s"(p0.s_row), "+s"(p0.s_col));
+    asm volatile("" : "+s"(p0.s_row), "+s"(p0.s_col), "+s"(p0.s_grp));
   }
   asm volatile("" : "+s"(d0.x), "+s"(d0.q_row), "+s"(d0.s_row), "+s"(d0.q_col), "+s"(d0.s_col),
                "+s"(d0.rows), "+s"(d0.cols));
-  if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, d0.cols};
+  if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, d0.cols, 16};
   // a grouped launch replaces it with the task's own tensor
   int64_t local = task;
   if (a.n != 1) {
     const int i = find_desc(a.task_start, a.n, task);
     d0 = a.d[i];
-    p0 = Args::kPitched ? a.pitch(i) : QuantPitch{d0.cols >> 5, d0.cols};
+    p0 = Args::kPitched ? a.pitch(i) : QuantPitch{d0.cols >> 5, d0.cols, 16};
     local = task - a.task_start[i];
   }
   if constexpr (ROWCOL) {

@@ -89,7 +89,7 @@ __device__ void quant_f32_flat_task(const QuantDesc& d, const QuantPitch& pitch,
     const uint32_t q = encode4_row(v[u], sc);
     if (p < npieces) {
       store4(reinterpret_cast<uint32_t*>(d.q_row) + p, q);
-      if ((tid & 7) == 0) store_scale<false>(d.s_row + pitched_block(p >> 3, d.cols >> 5, pitch.s_row), sc.sbyte);
+      if ((tid & 7) == 0) store_scale<false>(d.s_row + pitched_block(p >> 3, d.cols >> 5, ScaleStride{pitch.s_row, pitch.s_grp}), sc.sbyte);
     }
   }
 }
@@ -211,7 +211,7 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch,
   if (ROW && (lane & 7) == 0) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r)
-      store_scale<false>(d.s_row + (r0 + r) * pitch.s_row + (ce >> 5), row_sb[r / 4] >> (8 * (r % 4)));
+      store_scale<false>(d.s_row + scale_at(r0 + r, ce >> 5, pitch.s_row, pitch.s_grp), row_sb[r / 4] >> (8 * (r % 4)));
   }
 }
 
@@ -229,20 +229,20 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const Args
   // one tensor: its descriptor is read together with the table size (the
   // empty asm keeps those loads ahead of the branch)
   QuantDesc d0 = a.d[0];
-  QuantPitch p0 = {0, 0};
+  QuantPitch p0 = {0, 0, 0};
   if constexpr (Args::kPitched) {
     p0 = a.pitch(0);
-    asm volatile("" : "+s"(p0.s_row), "+s"(p0.s_col));
+    asm volatile("" : "+s"(p0.s_row), "+s"(p0.s_col), "+s"(p0.s_grp));
   }
   asm volatile("" : "+s"(d0.x), "+s"(d0.q_row), "+s"(d0.s_row), "+s"(d0.q_col), "+s"(d0.s_col),
                "+s"(d0.rows), "+s"(d0.cols));
-  if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, d0.cols};
+  if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, d0.cols, 16};
   // a grouped launch replaces it with the task's own tensor
   int64_t local = task;
   if (a.n != 1) {
     const int i = find_desc(a.task_start, a.n, task);
     d0 = a.d[i];
-    p0 = Args::kPitched ? a.pitch(i) : QuantPitch{d0.cols >> 5, d0.cols};
+    p0 = Args::kPitched ? a.pitch(i) : QuantPitch{d0.cols >> 5, d0.cols, 16};
     local = task - a.task_start[i];
   }
   if constexpr (ROWCOL) {

@@ -122,7 +122,7 @@ __device__ __forceinline__ RowRstd row_rstd(double ss, double inv_cols, float ep
 // Normalize one chunk with its float32 weights w (gamma + offset), store
 // normed, quantize the stored words.  y = ((x * pre) * rstd) * w, where pre
 // is 1 except for the rows whose rstd lies past float32's range (2^64 there).
-__device__ __forceinline__ void finish_chunk(const NormDesc& d, int64_t s_pitch, int64_t row,
+__device__ __forceinline__ void finish_chunk(const NormDesc& d, ScaleStride ss, int64_t row,
                                              int64_t c, bool valid, const u32x4& v, const float* w,
                                              float rstd, float pre, int t) {
   u32x4 y;
@@ -135,7 +135,7 @@ __device__ __forceinline__ void finish_chunk(const NormDesc& d, int64_t s_pitch,
     const int64_t e = row * (int64_t)d.cols + c * kChunk;
     store16(d.normed + e, y);
     store8(d.q + e, q);
-    if ((t & 3) == 0) store_scale<false>(d.s + row * s_pitch + ((c * kChunk) >> 5), rs.sbyte);
+    if ((t & 3) == 0) store_scale<false>(d.s + scale_at(row, (c * kChunk) >> 5, ss.row, ss.grp), rs.sbyte);
   }
 }
 
@@ -216,7 +216,7 @@ __device__ __forceinline__ void rstd64(double acc, int32_t cols, float eps, int 
 // row's L = 64 * WPR lanes each hold NCH chunks (chunk j of lane t is chunk
 // t + L j).  The weights gamma + offset stay in registers across the rows.
 template <int WPR, int NCH, class Parts>
-__device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row, int step, int count,
+__device__ void norm_rows(const NormDesc& d, ScaleStride ss, int64_t first_row, int step, int count,
                           int sub, int lane, Parts* part) {
   constexpr int L = kWave * WPR;           // lanes per row
   const int t = sub * kWave + lane;        // this lane's index within the row
@@ -269,7 +269,7 @@ __device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row,
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int64_t c = t + (int64_t)j * L;
-        finish_chunk(d, s_pitch, row, c, c < nch, v[j], w[j], r, pre, t);
+        finish_chunk(d, ss, row, c, c < nch, v[j], w[j], r, pre, t);
       }
     }
   } else {
@@ -303,7 +303,7 @@ __device__ void norm_rows(const NormDesc& d, int64_t s_pitch, int64_t first_row,
         const u32x4 v = valid ? load16_cached(xr + c * kChunk) : u32x4{0, 0, 0, 0};
         float w[8];
         weights(d, load_gamma(d, c, valid), w);
-        finish_chunk(d, s_pitch, row, c, valid, v, w, r, pre, t);
+        finish_chunk(d, ss, row, c, valid, v, w, r, pre, t);
       }
     }
   }
@@ -325,20 +325,20 @@ __global__ __launch_bounds__(64 * WAVES) void mxfp8_rmsnorm_quantize_kernel(cons
   // one tensor: its descriptor is read together with the table size (the
   // empty asm keeps those loads ahead of the branch)
   NormDesc d0 = a.d[0];
-  int64_t p0 = 0;
+  ScaleStride p0 = {0, 0};
   if constexpr (Args::kPitched) {
     p0 = a.pitch(0);
-    asm volatile("" : "+s"(p0));
+    asm volatile("" : "+s"(p0.row), "+s"(p0.grp));
   }
   asm volatile("" : "+s"(d0.x), "+s"(d0.gamma), "+s"(d0.normed), "+s"(d0.q), "+s"(d0.s),
                "+s"(d0.rows), "+s"(d0.cols), "+s"(d0.weight_offset), "+s"(d0.eps));
-  if constexpr (!Args::kPitched) p0 = d0.cols >> 5;
+  if constexpr (!Args::kPitched) p0 = {d0.cols >> 5, 16};
   // a grouped launch replaces it with the task's own tensor
   int64_t row0 = (int64_t)task * rows_per_task;
   if (a.n != 1) {
     const int i = find_desc(a.task_start, a.n, task);
     d0 = a.d[i];
-    p0 = Args::kPitched ? a.pitch(i) : (int64_t)(d0.cols >> 5);
+    p0 = Args::kPitched ? a.pitch(i) : ScaleStride{d0.cols >> 5, 16};
     row0 = (int64_t)(task - a.task_start[i]) * rows_per_task;
   }
   const int64_t left = (int64_t)d0.rows - row0;

@@ -41,7 +41,7 @@ def test_every_declared_function_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mxfp8_abi_version() == 2
+    assert L.mxfp8_abi_version() == 3
     for code in range(7):
         assert L.mxfp8_status_string(code)
     assert b"unknown" in L.mxfp8_status_string(99)
@@ -148,6 +148,47 @@ def test_scale_pitch_checks(L):
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 72 + 4)), 1, 0, None) == ERR_ALIGN
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 32)), 1, 0, None) == ERR_SHAPE
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 1 << 20, 64, 0, C, 1 << 60)), 1, 0, None) == ERR_SHAPE
+
+
+def test_mfma_scale_order_checks(L):
+    """Pitch MXFP8_SCALES_MFMA (-1): rowwise scales only, whole 512-column
+    groups; any other negative pitch stays an error.  Only rejected calls are
+    made here (no GPU)."""
+    Q, N, Dq, M = mx._QuantDesc, mx._NormDesc, mx._DeqDesc, -1
+    def quant(*d):
+        return L.mxfp8_quantize_grouped((Q * 1)(Q(*d)), 1, None)
+    assert quant(A, 4, 64, B, C, None, None, M, 0) == ERR_SHAPE          # cols % 512
+    assert quant(A, 4, 1536, B, C, None, None, -2, 0) == ERR_SHAPE       # no other sentinel
+    assert quant(A, 32, 512, None, None, B, C, 0, M) == ERR_SHAPE        # columnwise scales
+    assert quant(A, 1 << 30, 1024, B, C, None, None, M, 0) == ERR_SHAPE  # flat block index > 2^32
+    assert quant(A, 4, 512, B, MIS, None, None, M, 0) == ERR_ALIGN       # still checked
+    assert L.mxfp8_rmsnorm_quantize_grouped((N * 1)(N(A, B, 0.0, 1e-6, 4, 96, C, D, A, M)), 1, None) == ERR_SHAPE
+    assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 4, 96, 0, C, M)), 1, 0, None) == ERR_SHAPE
+    assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 512, 1, C, M)), 1, 0, None) == ERR_SHAPE
+    g = L.mxfp8_gemm
+    assert g(A, B, C, D, 4, 4, 256, M, 0, A, 0, None) == ERR_SHAPE       # K % 512
+    assert g(A, B, C, D, 4, 4, 640, 0, M, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 512, -2, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 512, M, M, MIS, 0, None) == ERR_ALIGN     # reaches the later checks
+
+
+def test_mfma_scale_plane_shapes():
+    """Host-side: a contiguous [cols/512, rows, 16] tensor is a plane in the
+    MFMA order; other 3-D shapes and non-contiguous ones are rejected."""
+    import torch
+    assert mx.mfma_scale_shape(100, 1536) == (3, 100, 16)
+    with pytest.raises(ValueError):
+        mx.mfma_scale_shape(100, 1056)
+    t = torch.zeros(3, 100, 16, dtype=torch.uint8)
+    assert mx._scale_pitch(t, (100, 48), t.device, "s")[1] == -1
+    with pytest.raises(ValueError):
+        mx._scale_pitch(t, (100, 32), t.device, "s")
+    with pytest.raises(ValueError):
+        mx._scale_pitch(torch.zeros(100, 3, 16, dtype=torch.uint8).transpose(0, 1), (100, 48), t.device, "s")
+    s, pitch = mx._scale_pitch(None, (100, 48), t.device, "s", mfma=True)
+    assert tuple(s.shape) == (3, 100, 16) and pitch == -1
+    with pytest.raises(ValueError):
+        mx._mfma("cols")
 
 
 def test_padded_scale_plane_views():
