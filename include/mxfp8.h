@@ -253,12 +253,16 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
  * positive multiple of 128 (MXFP8_ERR_SHAPE otherwise); M == 0 or N == 0 is
  * a no-op.  sa_pitch and sb_pitch are the bytes between scale rows of A and
  * of B (0: compact, K/32), or MXFP8_SCALES_MFMA for a plane in the MFMA order
- * (see "Scale pitches").
+ * (see "Scale pitches").  out_pitch is the number of elements between output
+ * rows (0: N; else at least N, MXFP8_ERR_SHAPE otherwise), so the product can
+ * fill a column slice of a wider matrix; elements past column N of a row are
+ * never written.
  */
 mxfp8_status mxfp8_gemm(const void *qa, const void *sa, const void *qb,
                         const void *sb, int64_t M, int64_t N, int64_t K,
                         int64_t sa_pitch, int64_t sb_pitch, void *out,
-                        mxfp8_out_dtype out_dtype, void *stream);
+                        int64_t out_pitch, mxfp8_out_dtype out_dtype,
+                        void *stream);
 
 /*
  * Grouped calls: one launch over a list of independent 2D tensors of any

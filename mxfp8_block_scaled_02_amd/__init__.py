@@ -93,7 +93,7 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_quantize_f32.argtypes = [p, i64, i64, p, p, p, p, p]
     L.mxfp8_quantize_f32_grouped.argtypes = [ctypes.POINTER(_QuantDesc), i32, p]
     L.mxfp8_rmsnorm_quantize_grouped.argtypes = [ctypes.POINTER(_NormDesc), i32, p]
-    L.mxfp8_gemm.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, ctypes.c_int, p]
+    L.mxfp8_gemm.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, i64, ctypes.c_int, p]
     L.mxfp8_dequantize_grouped.argtypes = [ctypes.POINTER(_DeqDesc), i32, ctypes.c_int, p]
     for name in ("mxfp8_quantize", "mxfp8_rmsnorm_quantize", "mxfp8_dequantize",
                  "mxfp8_quantize_grouped", "mxfp8_rmsnorm_quantize_grouped",
@@ -422,7 +422,9 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
     """out[M, N] = A . B^T from rowwise planes A = (qa [M, K], sa [M, K/32]) and
     B = (qb [N, K], sb [N, K/32]) (quantization.utils page, mm_mxfp8: a
     quantized activation times a pre-quantized weight [out, in]).  Either
-    scale plane may be in the MFMA order ([K/512, rows, 16], K % 512 == 0)."""
+    scale plane may be in the MFMA order ([K/512, rows, 16], K % 512 == 0).
+    ``out`` may be a view whose rows lie further apart than N (a column slice
+    of a wider matrix); only its [M, N] elements are written."""
     code = _out_code(dtype)
     qa2 = _as2d(qa, "qa", torch.uint8)
     qb2 = _as2d(qb, "qb", torch.uint8, device=qa.device)
@@ -434,8 +436,17 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
     # 3-D planes in the MFMA order
     sa2, pa = _scale_pitch(sa, (M, K // BLOCK), qa.device, "sa", allocate=False)
     sb2, pb = _scale_pitch(sb, (N, K // BLOCK), qa.device, "sb", allocate=False)
-    o = _out(out, (M, N), dtype, qa.device, "out")
+    # out may be a column slice of a wider matrix: rows stride(0) elements apart
+    if out is None:
+        o, po = torch.empty((M, N), dtype=dtype, device=qa.device), 0
+    else:
+        o = out
+        if (tuple(o.shape) != (M, N) or o.dtype != dtype or o.device != qa.device
+                or (N > 1 and o.stride(1) != 1) or (M > 1 and o.stride(0) < N)):
+            raise ValueError("out must be a %s tensor of shape %s on %s with unit column stride and a "
+                             "row stride >= %d" % (dtype, (M, N), qa.device, N))
+        po = o.stride(0) if M > 1 and o.stride(0) != N else 0
     with _on(qa.device):
-        _check(lib().mxfp8_gemm(_ptr(qa2), _ptr(sa2), _ptr(qb2), _ptr(sb2), M, N, K, pa, pb, _ptr(o), code,
+        _check(lib().mxfp8_gemm(_ptr(qa2), _ptr(sa2), _ptr(qb2), _ptr(sb2), M, N, K, pa, pb, _ptr(o), po, code,
                                 _stream(qa.device)))
     return o

@@ -366,9 +366,10 @@ mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc* descs, int32_t n,
 
 mxfp8_status mxfp8_gemm(const void* qa, const void* sa, const void* qb, const void* sb,
                         int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
-                        void* out, mxfp8_out_dtype out_dtype, void* stream) {
+                        void* out, int64_t out_pitch, mxfp8_out_dtype out_dtype, void* stream) {
   if (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16) return MXFP8_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || !fits(M, K) || !fits(N, K) || !fits(M, N)) return MXFP8_ERR_SHAPE;
+  if (out_pitch < 0 || (out_pitch && (out_pitch < N || !fits(M, out_pitch)))) return MXFP8_ERR_SHAPE;
   if ((sa_pitch < 0 && sa_pitch != MXFP8_SCALES_MFMA) || (sb_pitch < 0 && sb_pitch != MXFP8_SCALES_MFMA))
     return MXFP8_ERR_SHAPE;
   if (!mfma_order_ok(sa_pitch, K) || !mfma_order_ok(sb_pitch, K)) return MXFP8_ERR_SHAPE;
@@ -388,7 +389,8 @@ mxfp8_status mxfp8_gemm(const void* qa, const void* sa, const void* qb, const vo
   (void)hipGetLastError();
   return hip_status(mx::launch_gemm(static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa),
                                     static_cast<const uint8_t*>(qb), static_cast<const uint8_t*>(sb),
-                                    M, N, K, sas, sbs, out, out_dtype == MXFP8_OUT_BF16,
+                                    M, N, K, sas, sbs, out, out_pitch ? out_pitch : N,
+                                    out_dtype == MXFP8_OUT_BF16,
                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -69,6 +69,7 @@ struct GemmParams {
   int64_t sa_ld, sb_ld;       // bytes between scale rows of A and of B
   int64_t sa_gs, sb_gs;       // bytes between 16-block scale groups of a row
                               // (16 compact or padded, rows * 16 in the MFMA order)
+  int64_t ldo;                // elements between output rows (>= N)
   int32_t out_bf16;
   int32_t tiles_m, tiles_n;
 };
@@ -91,15 +92,15 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v16f& acc,
     const int64_t row = row0 + 8 * (r / 4) + 4 * h + (r % 4);
     if (row >= p.M) continue;
     if (p.out_bf16)
-      reinterpret_cast<uint16_t*>(p.out)[row * p.N + col] = (uint16_t)f32_to_bf16(acc[r]);
+      reinterpret_cast<uint16_t*>(p.out)[row * p.ldo + col] = (uint16_t)f32_to_bf16(acc[r]);
     else
-      __builtin_nontemporal_store(acc[r], reinterpret_cast<float*>(p.out) + row * p.N + col);
+      __builtin_nontemporal_store(acc[r], reinterpret_cast<float*>(p.out) + row * p.ldo + col);
   }
 }
 
 // bf16 output of two 32 x 32 tiles side by side (columns col .. col + 63,
 // rows row0 + 8 (r / 4) + 4 h + r % 4; the columns lie inside the output and
-// N is even; ROWS_IN says every row lies inside too, else rows past M are
+// N and the row pitch are even; ROWS_IN says every row lies inside too, else rows past M are
 // skipped), written as whole 128-byte row segments.  Lane fr
 // packs its values of the two tiles (columns fr and 32 + fr) into one dword;
 // lane d then takes columns 2d and 2d + 1 from lanes 2d and 2d + 1 (mod 32,
@@ -120,7 +121,7 @@ __device__ __forceinline__ void store_bf16_pair(const GemmParams& p, const v16f&
     const int64_t row = row0 + 8 * (r / 4) + 4 * h + (r % 4);
     if (ROWS_IN || row < p.M)
       __builtin_nontemporal_store(__builtin_amdgcn_perm(x1, x0, sel),
-                                  reinterpret_cast<uint32_t*>(o + row * p.N));
+                                  reinterpret_cast<uint32_t*>(o + row * p.ldo));
   }
 }
 
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const GemmPar
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, fr = lane & 31;
   const int64_t r0 = m0 + wm * (BM / 2), c0 = n0 + wn * (BN / 2) + fr;
-  if (m0 + BM <= p.M && n0 + BN <= p.N && p.out_bf16 && (p.N & 1) == 0) {
+  if (m0 + BM <= p.M && n0 + BN <= p.N && p.out_bf16 && ((p.N | p.ldo) & 1) == 0) {
     // a full tile with bf16 output: whole row segments
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const GemmPar
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t at = (r0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4)) * p.N + c0 + 32 * j;
+          const int64_t at = (r0 + 32 * i + 8 * (r / 4) + 4 * h + (r % 4)) * p.ldo + c0 + 32 * j;
           if (p.out_bf16)
             reinterpret_cast<uint16_t*>(p.out)[at] = (uint16_t)f32_to_bf16(t.acc[i][j][r]);
           else
@@ -565,12 +566,12 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
     __syncthreads();
   }
 
-  if (m0 + kGT <= p.M && n0 + kGT <= p.N && p.out_bf16 && (p.N & 1) == 0) {
+  if (m0 + kGT <= p.M && n0 + kGT <= p.N && p.out_bf16 && ((p.N | p.ldo) & 1) == 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) store_bf16_pair(p, acc[i][0], acc[i][1], m0 + wm * 64 + 32 * i, n0 + wn * 64, fr, h);
     return;
   }
-  if (p.out_bf16 && (p.N & 1) == 0 && n0 + wn * 64 + 64 <= p.N) {
+  if (p.out_bf16 && ((p.N | p.ldo) & 1) == 0 && n0 + wn * 64 + 64 <= p.N) {
     // a partial tile whose wave columns lie inside N: rows past M skipped
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -906,7 +907,7 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
 #pragma unroll
       for (int w = 1; w < kSkinnyWaves; ++w) sum += part[w][e >> 5][col];
       if (row < p.M && n0 + col < p.N) {
-        const int64_t at = row * p.N + n0 + col;
+        const int64_t at = row * p.ldo + n0 + col;
         if (p.out_bf16)
           reinterpret_cast<uint16_t*>(p.out)[at] = (uint16_t)f32_to_bf16(sum);
         else
@@ -935,11 +936,12 @@ void launch_skinny(const GemmParams& p, int64_t workgroups, hipStream_t s) {
 
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
-                       void* out, bool out_bf16, hipStream_t s) {
+                       void* out, int64_t out_ld, bool out_bf16, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   GemmParams p;
   p.qa = qa; p.sa = sa; p.qb = qb; p.sb = sb; p.out = out;
   p.M = M; p.N = N; p.K = K;
+  p.ldo = out_ld;
   p.sa_ld = sa_stride.row; p.sb_ld = sb_stride.row;
   p.sa_gs = sa_stride.grp; p.sb_gs = sb_stride.grp;
   p.out_bf16 = out_bf16 ? 1 : 0;

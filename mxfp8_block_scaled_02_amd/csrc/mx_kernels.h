@@ -162,10 +162,10 @@ hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipSt
 // out[M, N] (float32, or bf16 if out_bf16) = A . B^T for rowwise planes
 // A = (qa [M, K], sa [M, K/32]), B = (qb [N, K], sb [N, K/32]); K % 128 == 0.
 // The scale planes' strides are sa and sb (row strides multiples of 4; the
-// MFMA order only with K % 512 == 0).
+// MFMA order only with K % 512 == 0); output rows are out_ld elements apart.
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
-                       void* out, bool out_bf16, hipStream_t s);
+                       void* out, int64_t out_ld, bool out_bf16, hipStream_t s);
 
 // The tensor of a launch's table that task belongs to: the last i with
 // start[i] <= task, by binary search over the prefix sum of task counts.

@@ -91,21 +91,25 @@ def test_dequantize_argument_checks(L):
 
 def test_gemm_argument_checks(L):
     g = L.mxfp8_gemm
-    assert g(A, B, C, D, 4, 4, 96, 0, 0, A, 0, None) == ERR_SHAPE       # K % 128
-    assert g(A, B, C, D, 4, 4, 0, 0, 0, A, 0, None) == ERR_SHAPE
-    assert g(A, B, C, D, -1, 4, 128, 0, 0, A, 0, None) == ERR_SHAPE
-    assert g(A, None, C, D, 4, 4, 128, 0, 0, A, 0, None) == ERR_NULL
-    assert g(A, B, C, D, 4, 4, 128, 0, 0, MIS, 0, None) == ERR_ALIGN
-    assert g(A, B, C, D, 4, 4, 128, 0, 0, A, 5, None) == ERR_ARG
-    assert g(None, None, None, None, 0, 4, 128, 0, 0, None, 0, None) == OK
+    assert g(A, B, C, D, 4, 4, 96, 0, 0, A, 0, 0, None) == ERR_SHAPE       # K % 128
+    assert g(A, B, C, D, 4, 4, 0, 0, 0, A, 0, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, -1, 4, 128, 0, 0, A, 0, 0, None) == ERR_SHAPE
+    assert g(A, None, C, D, 4, 4, 128, 0, 0, A, 0, 0, None) == ERR_NULL
+    assert g(A, B, C, D, 4, 4, 128, 0, 0, MIS, 0, 0, None) == ERR_ALIGN
+    assert g(A, B, C, D, 4, 4, 128, 0, 0, A, 0, 5, None) == ERR_ARG
+    assert g(None, None, None, None, 0, 4, 128, 0, 0, None, 0, 0, None) == OK
     # scale pitches: at least K/32 bytes, a multiple of 4, not negative
-    assert g(A, B, C, D, 4, 4, 256, 4, 0, A, 0, None) == ERR_SHAPE
-    assert g(A, B, C, D, 4, 4, 256, 0, 6, A, 0, None) == ERR_SHAPE
-    assert g(A, B, C, D, 4, 4, 256, 10, 0, A, 0, None) == ERR_ALIGN
-    assert g(A, B, C, D, 4, 4, 256, -8, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 256, 4, 0, A, 0, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 256, 0, 6, A, 0, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 256, 10, 0, A, 0, 0, None) == ERR_ALIGN
+    assert g(A, B, C, D, 4, 4, 256, -8, 0, A, 0, 0, None) == ERR_SHAPE
+    # output pitch: 0 or at least N
+    assert g(A, B, C, D, 4, 4, 256, 0, 0, A, 3, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 256, 0, 0, A, -4, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 256, 0, 0, A, 1 << 62, 0, None) == ERR_SHAPE
     # more output tiles than 32-bit grid and tile indices hold
-    assert g(A, B, C, D, 1, 1 << 40, 128, 0, 0, A, 0, None) == ERR_SHAPE
-    assert g(A, B, C, D, 1 << 21, 1 << 21, 128, 0, 0, A, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 1, 1 << 40, 128, 0, 0, A, 0, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 1 << 21, 1 << 21, 128, 0, 0, A, 0, 0, None) == ERR_SHAPE
 
 
 def test_grouped_checks_every_descriptor_first(L):
@@ -166,10 +170,10 @@ def test_mfma_scale_order_checks(L):
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 4, 96, 0, C, M)), 1, 0, None) == ERR_SHAPE
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 512, 1, C, M)), 1, 0, None) == ERR_SHAPE
     g = L.mxfp8_gemm
-    assert g(A, B, C, D, 4, 4, 256, M, 0, A, 0, None) == ERR_SHAPE       # K % 512
-    assert g(A, B, C, D, 4, 4, 640, 0, M, A, 0, None) == ERR_SHAPE
-    assert g(A, B, C, D, 4, 4, 512, -2, 0, A, 0, None) == ERR_SHAPE
-    assert g(A, B, C, D, 4, 4, 512, M, M, MIS, 0, None) == ERR_ALIGN     # reaches the later checks
+    assert g(A, B, C, D, 4, 4, 256, M, 0, A, 0, 0, None) == ERR_SHAPE       # K % 512
+    assert g(A, B, C, D, 4, 4, 640, 0, M, A, 0, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 512, -2, 0, A, 0, 0, None) == ERR_SHAPE
+    assert g(A, B, C, D, 4, 4, 512, M, M, MIS, 0, 0, None) == ERR_ALIGN     # reaches the later checks
 
 
 def test_mfma_scale_plane_shapes():

@@ -210,3 +210,36 @@ def test_gemm_skinny_decode(orc, mnk):
     qa, sa = quantized(M, K, 1.0, seed=M + 11 * K)
     qb, sb = quantized(N, K, 0.02, seed=N + 13 * K)
     run(orc, qa, sa, qb, sb, "skinny")
+
+
+@pytest.mark.parametrize("mnk", [(1000, 4096, 384), (260, 130, 128), (256, 256, 512), (300, 2048, 4096),
+                                 (4352, 3840, 640), (129, 1000, 512), (16, 7168, 7168), (100, 200, 512),
+                                 (5, 96, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gemm_output_guard_bands(mnk, dtype):
+    """The product written into an [M, N] view of a larger buffer filled with
+    0xA5 bytes, rows a pitch apart (N + 37: odd, N + 64: even), with padding
+    before and after: every output equals the contiguous call's bit for bit,
+    and no byte outside the view changes (ring tiles full and partial, the
+    tile128 tiles, the skinny kernel; bf16 through the paired-row stores when
+    the pitch is even)."""
+    M, N, K = mnk
+    qa, sa = quantized(M, K, 1.0, seed=M + 23 * K)
+    qb, sb = quantized(N, K, 0.05, seed=N + 29 * K)
+    ref = mx.gemm(qa, sa, qb, sb, dtype)
+    bits = torch.int32 if dtype == torch.float32 else torch.int16
+    fill = -0x5A5A5A5B if dtype == torch.float32 else -0x5A5B          # 0xA5A5A5A5 / 0xA5A5
+    for ld in (N + 37, N + 64):
+        say("gemm guard bands", mnk, dtype, ld)
+        pad = 4096
+        buf = torch.full((pad + M * ld + pad,), fill, dtype=bits, device=DEV)
+        view = buf[pad:pad + M * ld].view(M, ld)[:, :N].view(dtype)
+        out = mx.gemm(qa, sa, qb, sb, dtype, out=view)
+        torch.cuda.synchronize()
+        assert out.data_ptr() == view.data_ptr()
+        assert torch.equal(view.view(bits), ref.view(bits)), "%s ld %d: outputs differ" % (mnk, ld)
+        b = buf.cpu()
+        inside = torch.zeros(b.numel(), dtype=torch.bool)
+        inside[pad:pad + M * ld].view(M, ld)[:, :N] = True
+        assert (b[~inside] == fill).all(), "%s ld %d: %d guard elements written" % (
+            mnk, ld, int((b[~inside] != fill).sum()))
