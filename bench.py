@@ -297,12 +297,16 @@ def bench_gemm(torch, mx, steps):
     T = Timed(torch, EAGER)
     res = {}
     # 4096 x 4096 x 11008: an MLP down projection, K not a multiple of 512
-    for M, N, K in ((8192, 8192, 8192), (1024, 7168, 7168), (4096, 4096, 11008), (128, 7168, 7168),
-                    (16, 7168, 7168)):
+    # "_mfma_scales": both operands' scales in the MFMA order (K % 512 == 0)
+    for M, N, K, order in ((8192, 8192, 8192, "row"), (8192, 8192, 8192, "mfma"),
+                           (1024, 7168, 7168, "row"), (1024, 7168, 7168, "mfma"),
+                           (4096, 4096, 11008, "row"), (128, 7168, 7168, "row"), (128, 7168, 7168, "mfma"),
+                           (16, 7168, 7168, "row"), (16, 7168, 7168, "mfma")):
         g = torch.Generator(device=dev).manual_seed(M + N + K)
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
         b = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
-        pa, pb = mx.quantize(a, True, False), mx.quantize(b, True, False)
+        pa = mx.quantize(a, True, False, scale_order=order)
+        pb = mx.quantize(b, True, False, scale_order=order)
         del a, b
         # the weight rotates over copies that together exceed the Infinity
         # Cache, so every launch reads B from HBM, as a layer's weight is
@@ -322,7 +326,7 @@ def bench_gemm(torch, mx, steps):
             alg = (M + N) * K * (1 + 1 / 32) + M * N * 2
             rec.update({"alg_bytes": int(alg), "GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
                         "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-        res["gemm_bf16out_%dx%dx%d" % (M, N, K)] = rec
+        res["gemm_bf16out_%dx%dx%d%s" % (M, N, K, "_mfma_scales" if order == "mfma" else "")] = rec
         del bs, pa, out
     return res
 
