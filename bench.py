@@ -150,16 +150,49 @@ def rec(ms, alg, elems, launches, **extra):
     return out
 
 
-def bench_headline(torch, mx, synth, steps, warmup):
+def sustained(torch, fn, seconds, per_graph=200):
+    """fn replayed for about `seconds` in graphs of per_graph launches, the
+    host waiting for each replay: the rate once clocks and caches have
+    settled.  Outside the K timed steps; HIP events bracket all replays."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    replays = 0
+    t0 = time.perf_counter()
+    start.record(stream)
+    while replays == 0 or time.perf_counter() - t0 < seconds:
+        g.replay()
+        torch.cuda.synchronize()
+        replays += 1
+    stop.record(stream)
+    torch.cuda.synchronize()
+    launches = replays * per_graph
+    del g
+    return start.elapsed_time(stop) / launches, launches, time.perf_counter() - t0
+
+
+def bench_headline(torch, mx, synth, steps, warmup, sustain_s=0.0):
     """The grouped row + column quantize of 64 expert weights: one launch a step."""
     dev = torch.device("cuda:0")
     xs = synth.workload(HEADLINE, device=dev)["xs"]
     r, c = xs[0].shape
     alg = len(xs) * quant_bytes(r, c, True, True)
     outs = mx.quantize_grouped(xs, True, True)
-    ms, wall = Timed(torch, EAGER).run(lambda i: mx.quantize_grouped(xs, True, True, outs=outs), steps, warmup)
+    fn = lambda i: mx.quantize_grouped(xs, True, True, outs=outs)
+    ms, wall = Timed(torch, EAGER).run(fn, steps, warmup)
+    res = {"ms": ms, "bytes": alg, "elems": 64 * r * c, "wall_s": wall, "shape": [r, c], "tensors": 64}
+    if sustain_s > 0 and not EAGER:
+        sms, n, swall = sustained(torch, fn, sustain_s)
+        gbs = alg / (sms * 1e-3) / 1e9
+        res["sustained"] = {"launches": n, "seconds": round(swall, 2), "ms_per_launch": round(sms, 5),
+                            "GB_s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
     del xs, outs
-    return {"ms": ms, "bytes": alg, "elems": 64 * r * c, "wall_s": wall, "shape": [r, c], "tensors": 64}
+    return res
 
 
 def bench_configs(torch, mx, synth, steps):
@@ -443,12 +476,12 @@ def trace_summary(trace_csv: str) -> str:
                 continue
             key = (short_kernel_name(name), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
             agg[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines = ["%-60s %10s %6s %10s %10s %10s %10s %10s" % ("kernel", "workgroups", "calls", "mean_us",
+    lines = ["%-80s %10s %6s %10s %10s %10s %10s %10s" % ("kernel", "workgroups", "calls", "mean_us",
                                                           "p10_us", "median_us", "p90_us", "min_us")]
     for (name, wgs), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         v.sort()
-        lines.append("%-60s %10d %6d %10.3f %10.3f %10.3f %10.3f %10.3f" % (
-            name[-60:], wgs, len(v), sum(v) / len(v) / 1e3, percentile(v, 10) / 1e3, v[len(v) // 2] / 1e3,
+        lines.append("%-80s %10d %6d %10.3f %10.3f %10.3f %10.3f %10.3f" % (
+            name[-80:], wgs, len(v), sum(v) / len(v) / 1e3, percentile(v, 10) / 1e3, v[len(v) // 2] / 1e3,
             percentile(v, 90) / 1e3, v[0] / 1e3))
     return "\n".join(lines)
 
@@ -526,6 +559,9 @@ def main():
     ap.add_argument("--no-other-rows", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time plain launches instead of one graph replay (counter runs)")
+    ap.add_argument("--sustain", type=float, default=8.0,
+                    help="after the timed steps, replay the headline launch for this many "
+                         "seconds and report the settled rate (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference that "
                          "scales HBM byte counters")
@@ -550,7 +586,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    main_run = bench_headline(torch, mx, synth, args.steps, args.warmup)
+    main_run = bench_headline(torch, mx, synth, args.steps, args.warmup, args.sustain)
     ms = main_run["ms"]
     gbs = main_run["bytes"] / (ms * 1e-3) / 1e9
     line = {
@@ -576,6 +612,8 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(HEADLINE_KERNEL), "kernel": HEADLINE_KERNEL},
     }
+    if "sustained" in main_run:
+        line["sustained"] = main_run["sustained"]
     if not args.no_other_rows:
         line["configs"] = bench_configs(torch, mx, synth, args.steps)
         line["other_entry_points"] = bench_other_rows(torch, mx, synth, max(args.steps // 2, 20))
