@@ -110,8 +110,10 @@ const char *mxfp8_status_string(mxfp8_status status);
  *
  * A plane whose two pointers are NULL is not requested; one NULL and one set
  * is MXFP8_ERR_NULL; both planes NULL is MXFP8_ERR_NO_OUTPUT.  A rowwise
- * request needs cols % 32 == 0, a columnwise request rows % 32 == 0 and
- * cols % 8 == 0 (MXFP8_ERR_SHAPE otherwise).
+ * request needs cols % 32 == 0, a columnwise request rows % 32 == 0
+ * (MXFP8_ERR_SHAPE otherwise).  A columnwise-only request with cols % 8 != 0
+ * runs a narrow path of element-sized accesses (the same bytes, at a fraction
+ * of the tiles' bandwidth).
  */
 mxfp8_status mxfp8_quantize(const void *x, int64_t rows, int64_t cols,
                             void *q_row, void *s_row, void *q_col, void *s_col,
@@ -180,7 +182,8 @@ mxfp8_status mxfp8_rmsnorm_quantize(const void *x, const void *gamma,
  * The check that compares a dequantized tensor with a fresh quantize
  * (quantization.utils page, _verify_te_to_mcore_mxfp8_conversion) needs it.
  * axis picks the scale layout: MXFP8_ROWWISE s [rows, cols/32] (cols % 32 ==
- * 0), MXFP8_COLUMNWISE s [rows/32, cols] (rows % 32 == 0, cols % 8 == 0).
+ * 0), MXFP8_COLUMNWISE s [rows/32, cols] (rows % 32 == 0; cols % 8 != 0
+ * takes a narrow path of element-sized accesses).
  * out is float32 or bf16 [rows, cols]: the exact value rounded to nearest
  * even.  Float32 results are exact (values from 2^-136 up), except that
  * scale bytes above 246, which no quantize of bf16 input produces, can push a
@@ -207,7 +210,8 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
  *
  *   rowwise scales     pitch >= cols/32 (any value), and rows * cols/32 < 2^32
  *                      when the rowwise plane is the only one requested;
- *   columnwise scales  pitch >= cols and a multiple of 8 (MXFP8_ERR_ALIGN);
+ *   columnwise scales  pitch >= cols, and a multiple of 8 when cols % 8 == 0
+ *                      (MXFP8_ERR_ALIGN);
  *   matrix product     pitch >= K/32 and a multiple of 4.
  *
  * A pitch below the plane's width is MXFP8_ERR_SHAPE.

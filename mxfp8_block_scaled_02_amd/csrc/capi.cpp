@@ -42,7 +42,7 @@ mxfp8_status check_quant(const mxfp8_quant_desc& d) {
   if (!row && !col) return MXFP8_ERR_NO_OUTPUT;
   if (d.x == nullptr) return MXFP8_ERR_NULL;
   if (row && d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
-  if (col && (d.rows % MXFP8_BLOCK || d.cols % 8)) return MXFP8_ERR_SHAPE;
+  if (col && d.rows % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
   if (misaligned(d.x) || misaligned(d.q_row) || misaligned(d.s_row) ||
       misaligned(d.q_col) || misaligned(d.s_col))
     return MXFP8_ERR_ALIGN;
@@ -55,7 +55,8 @@ mxfp8_status check_quant(const mxfp8_quant_desc& d) {
   }
   if (col && d.s_col_pitch) {
     if (d.s_col_pitch < d.cols || !fits(d.rows / MXFP8_BLOCK, d.s_col_pitch)) return MXFP8_ERR_SHAPE;
-    if (d.s_col_pitch % 8) return MXFP8_ERR_ALIGN;
+    // the tiles store 8 scale bytes at a time; rows of other lengths store bytes
+    if (d.cols % 8 == 0 && d.s_col_pitch % 8) return MXFP8_ERR_ALIGN;
   }
   return MXFP8_OK;
 }
@@ -85,8 +86,7 @@ mxfp8_status check_deq(const mxfp8_deq_desc& d) {
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   if (!d.q || !d.s || !d.out) return MXFP8_ERR_NULL;
   if (d.axis == MXFP8_ROWWISE && d.cols % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
-  if (d.axis == MXFP8_COLUMNWISE && (d.rows % MXFP8_BLOCK || d.cols % 8))
-    return MXFP8_ERR_SHAPE;
+  if (d.axis == MXFP8_COLUMNWISE && d.rows % MXFP8_BLOCK) return MXFP8_ERR_SHAPE;
   if (misaligned(d.q) || misaligned(d.s) || misaligned(d.out)) return MXFP8_ERR_ALIGN;
   if (d.s_pitch == MXFP8_SCALES_MFMA) {
     if (!flat_blocks_fit(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
@@ -98,7 +98,7 @@ mxfp8_status check_deq(const mxfp8_deq_desc& d) {
       if (d.s_pitch != d.cols / MXFP8_BLOCK && !flat_blocks_fit(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
     } else {
       if (d.s_pitch < d.cols) return MXFP8_ERR_SHAPE;
-      if (d.s_pitch % 8) return MXFP8_ERR_ALIGN;
+      if (d.cols % 8 == 0 && d.s_pitch % 8) return MXFP8_ERR_ALIGN;
     }
   }
   return MXFP8_OK;

@@ -82,7 +82,29 @@ __device__ void deq_col_task(const DeqDesc& d, ScaleStride ss, bool bf16, int64_
   for (int r = 0; r < kDeqRows; ++r) put4(d.out, bf16, (r0 + r) * cols + c, q[r], sc);
 }
 
-template <class Args>
+// Columnwise planes on the narrow path (narrow_deq): kDeqRows rows x 64
+// columns per wave task, one column per lane, element-sized accesses (the
+// rows start off the 16-byte grid).
+__device__ void deq_col_narrow_task(const DeqDesc& d, ScaleStride ss, bool bf16, int64_t task, int lane) {
+  const int64_t cols = d.cols;
+  const int64_t col_tiles = (cols + kWave - 1) / kWave;
+  const int64_t r0 = (task / col_tiles) * kDeqRows;
+  const int64_t c = (task % col_tiles) * kWave + lane;
+  if (c >= cols) return;
+  const float sc = e8m0_value(load1_cached(d.s + (r0 / kBlock) * ss.row + c));
+#pragma unroll
+  for (int r = 0; r < kDeqRows; ++r) {
+    const int64_t e = (r0 + r) * cols + c;
+    const float f = decode_e4m3(*gload_ptr<uint8_t>(d.q + e), sc);
+    if (bf16)
+      *gstore_ptr<uint16_t>(reinterpret_cast<uint16_t*>(d.out) + e) = (uint16_t)f32_to_bf16(f);
+    else
+      *gstore_ptr<float>(reinterpret_cast<float*>(d.out) + e) = f;
+  }
+}
+
+// NARROW: some tensor of the launch takes the narrow columnwise path.
+template <class Args, bool NARROW = false>
 __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const Args a) {
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -103,6 +125,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const Args a
     if (task >= total0) return;
     if (d0.axis == 0)
       deq_flat_task(d0, p0, a.out_bf16 != 0, task, lane);
+    else if (NARROW && narrow_deq(d0))
+      deq_col_narrow_task(d0, p0, a.out_bf16 != 0, task, lane);
     else
       deq_col_task(d0, p0, a.out_bf16 != 0, task, lane);
     return;
@@ -114,8 +138,23 @@ __global__ __launch_bounds__(kThreads) void mxfp8_dequantize_kernel(const Args a
   const int64_t local = task - a.task_start[i];
   if (d.axis == 0)
     deq_flat_task(d, pi, a.out_bf16 != 0, local, lane);
+  else if (NARROW && narrow_deq(d))
+    deq_col_narrow_task(d, pi, a.out_bf16 != 0, local, lane);
   else
     deq_col_task(d, pi, a.out_bf16 != 0, local, lane);
+}
+
+template <class Args>
+hipError_t launch_deq(const Args& a, int64_t total_tasks, hipStream_t s) {
+  if (total_tasks <= 0) return hipSuccess;
+  bool narrow = false;
+  for (int i = 0; i < a.n; ++i) narrow |= narrow_deq(a.d[i]);
+  const dim3 grid((uint32_t)((total_tasks + kWavesPerGroup - 1) / kWavesPerGroup)), block(kThreads);
+  if (narrow)
+    hipLaunchKernelGGL((mxfp8_dequantize_kernel<Args, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((mxfp8_dequantize_kernel<Args>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -127,21 +166,16 @@ int64_t deq_tasks(const DeqDesc& d) {
     const int64_t per = (int64_t)kWave * kDeqUnroll;
     return (units + per - 1) / per;
   }
+  if (narrow_deq(d)) return (d.rows / kDeqRows) * ((d.cols + kWave - 1) / kWave);
   return (d.rows / kDeqRows) * ((d.cols + kDeqTileCols - 1) / kDeqTileCols);
 }
 
 hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s) {
-  if (total_tasks <= 0) return hipSuccess;
-  const int64_t groups = (total_tasks + kWavesPerGroup - 1) / kWavesPerGroup;
-  hipLaunchKernelGGL(mxfp8_dequantize_kernel<DeqArgs>, dim3((uint32_t)groups), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_deq(a, total_tasks, s);
 }
 
 hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipStream_t s) {
-  if (total_tasks <= 0) return hipSuccess;
-  const int64_t groups = (total_tasks + kWavesPerGroup - 1) / kWavesPerGroup;
-  hipLaunchKernelGGL(mxfp8_dequantize_kernel<DeqArgsPitched>, dim3((uint32_t)groups), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_deq(a, total_tasks, s);
 }
 
 }  // namespace mx

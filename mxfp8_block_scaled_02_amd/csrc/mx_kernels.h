@@ -76,9 +76,15 @@ struct QuantArgsPitched {
   QuantPitch p[kMax];
   __device__ QuantPitch pitch(int i) const { return p[i]; }
 };
+// A columnwise-only request whose rows are not a multiple of 8 elements: its
+// rows start off the 16-byte grid, so it takes the narrow path (one thread per
+// column of a 32-row block, element-sized accesses) instead of the tiles.
+__host__ __device__ inline bool narrow_col(const QuantDesc& d) {
+  return d.q_col != nullptr && d.q_row == nullptr && (d.cols & 7) != 0;
+}
 // Workgroup tasks a tensor needs: 32 x 512 tiles when a columnwise plane is
-// requested, otherwise 256 x flat_unroll 8-element pieces of the flattened
-// tensor.
+// requested (32-row blocks of 256 columns on the narrow path), otherwise
+// 256 x flat_unroll 8-element pieces of the flattened tensor.
 int64_t quant_tasks(const QuantDesc& d);
 hipError_t launch_quantize(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
 hipError_t launch_quantize(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s);
@@ -154,6 +160,9 @@ struct DeqArgsPitched {
   ScaleStride p[kMax];   // columnwise planes: p.row is the row pitch
   __device__ ScaleStride pitch(int i) const { return p[i]; }
 };
+// Columnwise planes whose rows are not a multiple of 8 elements take a
+// narrow path: one lane per column, element-sized accesses.
+__host__ __device__ inline bool narrow_deq(const DeqDesc& d) { return d.axis == 1 && (d.cols & 7) != 0; }
 int64_t deq_tasks(const DeqDesc& d);
 hipError_t launch_dequantize(const DeqArgs& a, int64_t total_tasks, hipStream_t s);
 hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipStream_t s);

@@ -74,6 +74,44 @@ __device__ void quant_flat_task(const QuantDesc& d, const QuantPitch& pitch, int
     quant_flat_pieces<NT, kFlatUnroll>(d, pitch, task, tid, npieces);
 }
 
+// The narrow columnwise path (narrow_col): the workgroup takes 256 columns of
+// one 32-row block, one column per thread.  A column's 32 values are packed
+// into four 8-value chunks and scaled and encoded by the rowwise block code,
+// which computes the same rule on any 32 values.  Loads and stores are
+// element-sized, so every access is aligned whatever the row length; across a
+// wave they cover 64 consecutive columns of one row.
+template <bool NT>
+__device__ void quant_col_narrow_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid) {
+  const int64_t cols = d.cols;
+  const int64_t col_tasks = (cols + kThreads - 1) / kThreads;
+  const int64_t rb = task / col_tasks;
+  const int64_t c = (task % col_tasks) * kThreads + tid;
+  if (c >= cols) return;                                   // no barrier follows
+  const uint16_t* xp = d.x + rb * kBlock * cols + c;
+  u32x4 v[kBlock / kChunk];
+#pragma unroll
+  for (int j = 0; j < kBlock / kChunk; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = *gload_ptr<uint16_t>(xp + (8 * j + 2 * k) * cols);
+      const uint32_t hi = *gload_ptr<uint16_t>(xp + (8 * j + 2 * k + 1) * cols);
+      v[j][k] = lo | (hi << 16);
+    }
+  uint32_t key = 0;
+#pragma unroll
+  for (int j = 0; j < kBlock / kChunk; ++j) key = max(key, chunk_key(v[j]));
+  const RowScale rs = row_scale_key(key);
+  uint8_t* qp = d.q_col + rb * kBlock * cols + c;
+#pragma unroll
+  for (int j = 0; j < kBlock / kChunk; ++j) {
+    const u32x2 e = encode_chunk_row(v[j], rs);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      *gstore_ptr<uint8_t>(qp + (8 * j + k) * cols) = (uint8_t)((k < 4 ? e.x : e.y) >> (8 * (k & 3)));
+  }
+  store_scale<NT>(d.s_col + rb * pitch.s_col + c, rs.sbyte);
+}
+
 // Packed magnitude maxima of the lane's 8 columns over the wave's rows (word j
 // holds columns 2j, 2j + 1), also written to the lane's LDS slot.
 __device__ __forceinline__ u32x4 wave_col_max(const u32x4 (&v)[kRowsPerWave][kCh], u32x4* slot) {
@@ -203,8 +241,9 @@ __device__ void quant_tile_task(const QuantDesc& d, const QuantPitch& pitch, int
 // NT: stream the rowwise scale bytes (see store_scale and the launcher).
 // ROWCOL: every tensor of the launch requests both planes (the launcher
 // checks), so only that tile path is compiled in; compiled together with the
-// other paths, it would share their code and registers.
-template <class Args, bool NT, bool ROWCOL>
+// other paths, it would share their code and registers.  NARROW: some tensor
+// takes the narrow columnwise path (only such launches carry its code).
+template <class Args, bool NT, bool ROWCOL, bool NARROW = false>
 __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const Args a) {
   __shared__ u32x4 colmax[kThreads * kCh];
   const int tid = threadIdx.x;
@@ -237,6 +276,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const Args a) 
     if (d0.q_col) {
       if (d0.q_row)
         quant_tile_task<NT, true>(d0, p0, local, wave, lane, colmax);
+      else if (NARROW && narrow_col(d0))
+        quant_col_narrow_task<NT>(d0, p0, local, tid);
       else
         quant_tile_task<NT, false>(d0, p0, local, wave, lane, colmax);
     } else {
@@ -249,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_kernel(const Args a) 
 
 int64_t quant_tasks(const QuantDesc& d) {
   if (d.rows == 0 || d.cols == 0) return 0;
+  if (narrow_col(d)) return (d.rows / kBlock) * ((d.cols + kThreads - 1) / kThreads);
   if (d.q_col)
     return (d.rows / kTileRows) * ((d.cols + kTileCols - 1) / kTileCols);
   const int64_t pieces = d.rows * d.cols / kLaneCols;
@@ -267,17 +309,24 @@ constexpr int64_t kResidentTasks = 4 * 256;
 template <class Args>
 hipError_t launch_quantize_args(const Args& a, int64_t total_tasks, hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
-  bool rowcol = true;
-  for (int i = 0; i < a.n; ++i) rowcol &= a.d[i].q_row != nullptr && a.d[i].q_col != nullptr;
+  bool rowcol = true, narrow = false;
+  for (int i = 0; i < a.n; ++i) {
+    rowcol &= a.d[i].q_row != nullptr && a.d[i].q_col != nullptr;
+    narrow |= narrow_col(a.d[i]);
+  }
   const dim3 grid((uint32_t)total_tasks), block(kThreads);
   if (total_tasks <= kResidentTasks) {
     if (rowcol)
       hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, true, true>), grid, block, 0, s, a);
+    else if (narrow)
+      hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, true, false, true>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, true, false>), grid, block, 0, s, a);
   } else {
     if (rowcol)
       hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, false, true>), grid, block, 0, s, a);
+    else if (narrow)
+      hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, false, false, true>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((mxfp8_quantize_kernel<Args, false, false>), grid, block, 0, s, a);
   }

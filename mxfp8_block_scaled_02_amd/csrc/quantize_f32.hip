@@ -72,6 +72,35 @@ __device__ __forceinline__ uint32_t encode4_row(u32x4 v, const F32Scale& sc) {
   return __builtin_bit_cast(uint32_t, a) | (sc.nan ? 0x7F7F7F7Fu : 0u);
 }
 
+// The narrow columnwise path (narrow_col), as for bf16: one column of a
+// 32-row block per thread, element-sized accesses, the rowwise block code on
+// the column's 32 values.
+__device__ void quant_f32_col_narrow_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid) {
+  const int64_t cols = d.cols;
+  const int64_t col_tasks = (cols + kThreads - 1) / kThreads;
+  const int64_t rb = task / col_tasks;
+  const int64_t c = (task % col_tasks) * kThreads + tid;
+  if (c >= cols) return;                                   // no barrier follows
+  const float* xp = reinterpret_cast<const float*>(d.x) + rb * kBlock * cols + c;
+  u32x4 v[kBlock / 4];
+  uint32_t key = 0;
+#pragma unroll
+  for (int j = 0; j < kBlock / 4; ++j) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[j][k] = *gload_ptr<uint32_t>(xp + (4 * j + k) * cols);
+    key = max(key, f32_key4(v[j]));
+  }
+  const F32Scale sc = f32_scale_key(key);
+  uint8_t* qp = d.q_col + rb * kBlock * cols + c;
+#pragma unroll
+  for (int j = 0; j < kBlock / 4; ++j) {
+    const uint32_t e = encode4_row(v[j], sc);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *gstore_ptr<uint8_t>(qp + (4 * j + k) * cols) = (uint8_t)(e >> (8 * k));
+  }
+  store_scale<false>(d.s_col + rb * pitch.s_col + c, sc.sbyte);
+}
+
 __device__ void quant_f32_flat_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid) {
   const float* x = reinterpret_cast<const float*>(d.x);
   const int64_t npieces = d.rows * d.cols / kF32Lane;    // whole blocks: cols % 32 == 0
@@ -219,7 +248,9 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch,
 // checks), so only that tile path is compiled in.  Compiled together, the two
 // tile paths share their loads and columnwise part and need 79 VGPRs against
 // 47 for this one, which would cut the waves a SIMD holds from 8 to 5.
-template <class Args, bool ROWCOL>
+// ROWCOL: every tensor requests both planes; NARROW: some tensor takes the
+// narrow columnwise path (only such launches carry its code).
+template <class Args, bool ROWCOL, bool NARROW = false>
 __global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const Args a) {
   __shared__ u32x4 colmax[kThreads];
   const int tid = threadIdx.x;
@@ -251,6 +282,8 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const Args
     if (d0.q_col) {
       if (d0.q_row)
         quant_f32_tile_task<true>(d0, p0, local, wave, lane, colmax);
+      else if (NARROW && narrow_col(d0))
+        quant_f32_col_narrow_task(d0, p0, local, tid);
       else
         quant_f32_tile_task<false>(d0, p0, local, wave, lane, colmax);
     } else {
@@ -263,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_kernel(const Args
 
 int64_t quant_f32_tasks(const QuantDesc& d) {
   if (d.rows == 0 || d.cols == 0) return 0;
+  if (narrow_col(d)) return (d.rows / kBlock) * ((d.cols + kThreads - 1) / kThreads);
   if (d.q_col)
     return (d.rows / kTileRows) * ((d.cols + kF32TileCols - 1) / kF32TileCols);
   const int64_t pieces = d.rows * d.cols / kF32Lane;
@@ -273,12 +307,18 @@ int64_t quant_f32_tasks(const QuantDesc& d) {
 template <class Args>
 hipError_t launch_f32(const Args& a, int64_t total_tasks, hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
-  bool rowcol = true;
-  for (int i = 0; i < a.n; ++i) rowcol &= a.d[i].q_row != nullptr && a.d[i].q_col != nullptr;
+  bool rowcol = true, narrow = false;
+  for (int i = 0; i < a.n; ++i) {
+    rowcol &= a.d[i].q_row != nullptr && a.d[i].q_col != nullptr;
+    narrow |= narrow_col(a.d[i]);
+  }
+  const dim3 grid((uint32_t)total_tasks), block(kThreads);
   if (rowcol)
-    hipLaunchKernelGGL((mxfp8_quantize_f32_kernel<Args, true>), dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mxfp8_quantize_f32_kernel<Args, true>), grid, block, 0, s, a);
+  else if (narrow)
+    hipLaunchKernelGGL((mxfp8_quantize_f32_kernel<Args, false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((mxfp8_quantize_f32_kernel<Args, false>), dim3((uint32_t)total_tasks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mxfp8_quantize_f32_kernel<Args, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ def test_quantize_argument_checks(L):
     assert q(A, -1, 32, B, C, None, None, None) == ERR_SHAPE
     assert q(A, 4, 48, B, C, None, None, None) == ERR_SHAPE          # partial row block
     assert q(A, 48, 32, None, None, B, C, None) == ERR_SHAPE         # partial column block
-    assert q(A, 32, 36, None, None, B, C, None) == ERR_SHAPE         # cols % 8
+    assert q(A, 40, 36, None, None, B, C, None) == ERR_SHAPE         # narrow columnwise: rows % 32 still
     assert q(A, 4, 32, B, None, None, None, None) == ERR_NULL        # half a plane
     assert q(A, 32, 32, None, None, None, C, None) == ERR_NULL
     assert q(None, 4, 32, B, C, None, None, None) == ERR_NULL
@@ -125,7 +125,7 @@ def test_grouped_checks_every_descriptor_first(L):
     assert L.mxfp8_rmsnorm_quantize_grouped(n, 1, None) == ERR_ARG
     dq = (mx._DeqDesc * 1)(mx._DeqDesc(A, B, 32, 40, 1, MIS))
     assert L.mxfp8_dequantize_grouped(dq, 1, 0, None) == ERR_ALIGN
-    dq = (mx._DeqDesc * 1)(mx._DeqDesc(A, B, 32, 36, 1, C))
+    dq = (mx._DeqDesc * 1)(mx._DeqDesc(A, B, 40, 36, 1, C))        # narrow columnwise: rows % 32 still
     assert L.mxfp8_dequantize_grouped(dq, 1, 0, None) == ERR_SHAPE
 
 
@@ -137,6 +137,7 @@ def test_scale_pitch_checks(L):
     assert quant(A, 4, 64, B, C, None, None, -4, 0) == ERR_SHAPE
     assert quant(A, 32, 64, None, None, B, C, 0, 60) == ERR_SHAPE        # columnwise pitch < 64
     assert quant(A, 32, 64, None, None, B, C, 0, 68) == ERR_ALIGN        # not a multiple of 8
+    assert quant(A, 32, 60, None, None, B, C, 0, 58) == ERR_SHAPE        # narrow columnwise: pitch < cols
     # a pitch whose last scale row would overflow 64-bit offsets
     assert quant(A, 1 << 20, 64, B, C, None, None, 1 << 60, 0) == ERR_SHAPE
     assert quant(A, 1 << 20, 64, None, None, B, C, 0, 1 << 60) == ERR_SHAPE
