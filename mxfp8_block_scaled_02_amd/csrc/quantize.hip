@@ -60,7 +60,9 @@ __device__ void quant_flat_pieces(const QuantDesc& d, const QuantPitch& pitch, i
       for (int h = 0; h < kCh; ++h)
         store8(d.q_row + p * kLaneCols + h * kChunk, encode_chunk_row(v[u][h], rs));
       if ((tid & (kBlock / kLaneCols - 1)) == 0)
-        store_scale<NT>(d.s_row + pitched_block(p * kLaneCols / kBlock, d.cols >> 5, ScaleStride{pitch.s_row, pitch.s_grp}), rs.sbyte);
+        store_scale<NT>(d.s_row + pitched_block(p * kLaneCols / kBlock, d.cols >> 5,
+                                                ScaleStride{pitch.s_row, pitch.s_grp}),
+                        rs.sbyte);
     }
   }
 }
@@ -234,7 +236,8 @@ __device__ void quant_tile_task(const QuantDesc& d, const QuantPitch& pitch, int
   if (ROW && (lane & (kBlock / kLaneCols - 1)) == 0) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r)
-      store_scale<NT>(d.s_row + scale_at(r0 + r, ce >> 5, pitch.s_row, pitch.s_grp), row_sb[r / 4] >> (8 * (r % 4)));
+      store_scale<NT>(d.s_row + scale_at(r0 + r, ce >> 5, pitch.s_row, pitch.s_grp),
+                      row_sb[r / 4] >> (8 * (r % 4)));
   }
 }
 

@@ -118,7 +118,9 @@ __device__ void quant_f32_flat_task(const QuantDesc& d, const QuantPitch& pitch,
     const uint32_t q = encode4_row(v[u], sc);
     if (p < npieces) {
       store4(reinterpret_cast<uint32_t*>(d.q_row) + p, q);
-      if ((tid & 7) == 0) store_scale<false>(d.s_row + pitched_block(p >> 3, d.cols >> 5, ScaleStride{pitch.s_row, pitch.s_grp}), sc.sbyte);
+      if ((tid & 7) == 0)
+        store_scale<false>(d.s_row + pitched_block(p >> 3, d.cols >> 5, ScaleStride{pitch.s_row, pitch.s_grp}),
+                           sc.sbyte);
     }
   }
 }
@@ -240,7 +242,8 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch,
   if (ROW && (lane & 7) == 0) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r)
-      store_scale<false>(d.s_row + scale_at(r0 + r, ce >> 5, pitch.s_row, pitch.s_grp), row_sb[r / 4] >> (8 * (r % 4)));
+      store_scale<false>(d.s_row + scale_at(r0 + r, ce >> 5, pitch.s_row, pitch.s_grp),
+                         row_sb[r / 4] >> (8 * (r % 4)));
   }
 }
 

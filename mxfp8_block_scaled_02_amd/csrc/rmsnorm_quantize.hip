@@ -138,7 +138,8 @@ __device__ __forceinline__ void finish_chunk(const NormDesc& d, ScaleStride ss, 
     const int64_t e = row * (int64_t)d.cols + c * kChunk;
     store16(d.normed + e, y);
     store8(d.q + e, q);
-    if (ALLQ || (t & 3) == 0) store_scale<false>(d.s + scale_at(row, (c * kChunk) >> 5, ss.row, ss.grp), rs.sbyte);
+    if (ALLQ || (t & 3) == 0)
+      store_scale<false>(d.s + scale_at(row, (c * kChunk) >> 5, ss.row, ss.grp), rs.sbyte);
   }
 }
 
@@ -393,33 +394,40 @@ int norm_rows_per_task(int64_t total_rows, int variant) {
   return (int)(g * slots);
 }
 
+// One kernel shape; the prefetching instantiation exists only where a slot
+// can hold two rows (CAN_PF).
+template <class Args, int WPR, int NCH, int WAVES = kWavesPerGroup, bool CAN_PF = true>
+void launch_shape(const Args& a, dim3 grid, int rows_per_task, bool pf, hipStream_t s) {
+  const dim3 block(64 * WAVES);
+  if constexpr (CAN_PF) {
+    if (pf) {
+      hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, WPR, NCH, WAVES, true>), grid, block, 0, s, a,
+                         rows_per_task);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, WPR, NCH, WAVES, false>), grid, block, 0, s, a,
+                     rows_per_task);
+}
+
 template <class Args>
 hipError_t launch_norm(const Args& a, int64_t total_tasks, int variant, int rows_per_task,
                        hipStream_t s) {
   if (total_tasks <= 0) return hipSuccess;
-  const dim3 block(kThreads), wide(64 * 16);
   const dim3 grid((uint32_t)total_tasks);
   const int r = rows_per_task;
   // two rows a slot: prefetch the second (see norm_rows)
   const bool pf = rows_per_task > (variant < 10 ? kWavesPerGroup : 1);
-  switch (variant * 2 + (pf ? 1 : 0)) {
-    case 161 * 2:
-    case 161 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 16, 1, 16>), grid, wide, 0, s, a, r); break;
-    case 162 * 2:
-    case 162 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 16, 2, 16>), grid, wide, 0, s, a, r); break;
-    case 1 * 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 1>), grid, block, 0, s, a, r); break;
-    case 1 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 1, kWavesPerGroup, true>), grid, block, 0, s, a, r); break;
-    case 2 * 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 2>), grid, block, 0, s, a, r); break;
-    case 2 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 1, 2, kWavesPerGroup, true>), grid, block, 0, s, a, r); break;
-    case 11 * 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 1>), grid, block, 0, s, a, r); break;
-    case 11 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 1, kWavesPerGroup, true>), grid, block, 0, s, a, r); break;
-    case 12 * 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 2>), grid, block, 0, s, a, r); break;
-    case 12 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 2, kWavesPerGroup, true>), grid, block, 0, s, a, r); break;
-    case 14 * 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 4>), grid, block, 0, s, a, r); break;
-    case 14 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 4, kWavesPerGroup, true>), grid, block, 0, s, a, r); break;
-    case 18 * 2: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 8>), grid, block, 0, s, a, r); break;
-    case 18 * 2 + 1: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 8, kWavesPerGroup, true>), grid, block, 0, s, a, r); break;
-    default: hipLaunchKernelGGL((mxfp8_rmsnorm_quantize_kernel<Args, 4, 0>), grid, block, 0, s, a, r); break;
+  switch (variant) {
+    case 161: launch_shape<Args, 16, 1, 16, false>(a, grid, r, pf, s); break;
+    case 162: launch_shape<Args, 16, 2, 16, false>(a, grid, r, pf, s); break;
+    case 1: launch_shape<Args, 1, 1>(a, grid, r, pf, s); break;
+    case 2: launch_shape<Args, 1, 2>(a, grid, r, pf, s); break;
+    case 11: launch_shape<Args, 4, 1>(a, grid, r, pf, s); break;
+    case 12: launch_shape<Args, 4, 2>(a, grid, r, pf, s); break;
+    case 14: launch_shape<Args, 4, 4>(a, grid, r, pf, s); break;
+    case 18: launch_shape<Args, 4, 8>(a, grid, r, pf, s); break;
+    default: launch_shape<Args, 4, 0, kWavesPerGroup, false>(a, grid, r, pf, s); break;
   }
   return hipGetLastError();
 }
