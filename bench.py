@@ -42,7 +42,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "mxfp8_block_scaled_02_amd", "csrc")
 HEADLINE = "grouped_64x2048x7168"
 # the headline step's one launch: 64 x (2048 / 32) x (7168 / 512) tiles
-HEADLINE_KERNEL = "mx::mxfp8_quantize_kernel<mx::QuantArgs, false, true>/57344"
+HEADLINE_KERNEL = "mx::mxfp8_quantize_kernel<mx::QuantArgs, false, true, false>/57344"
 
 # the sources each kernel family is built from: a stored traffic figure is
 # valid only while they are unchanged
