@@ -92,7 +92,9 @@ class Timed:
         self.torch = torch
         self.eager = eager
 
-    def run(self, fn, steps, warmup):
+    def run(self, fn, steps, warmup, replays=1):
+        """replays > 1: the graph is replayed that many times, each timed on
+        its own, and the median replay is reported (eager: ignored)."""
         torch = self.torch
         for i in range(warmup):
             fn(i)
@@ -114,17 +116,19 @@ class Timed:
                 fn(i)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        start.record(stream)
-        g.replay()
-        stop.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = start.elapsed_time(stop) / steps
+        times, wall = [], 0.0
+        for _ in range(replays):
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            start.record(stream)
+            g.replay()
+            stop.record(stream)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+            times.append(start.elapsed_time(stop) / steps)
         del g
-        return ms, wall
+        return sorted(times)[len(times) // 2], wall
 
 
 def rotation(per_set_bytes: int) -> int:
@@ -349,7 +353,9 @@ def bench_gemm(torch, mx, steps):
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         fn = lambda i: mx.gemm(pa.rowwise_data, pa.rowwise_scale, bs[i % sets][0], bs[i % sets][1],
                                torch.bfloat16, out=out)
-        ms, _ = T.run(fn, max(steps // 4, 10), 3)
+        # the median of 5 replays: one replay of a few launches of the large
+        # products varies by several percent with the clock
+        ms, _ = T.run(fn, max(steps // 4, 10), 3, replays=5)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         rec = {"ms_per_launch": round(ms, 5), "TFLOP_s": round(tf, 1),
                "frac_mfma_fp8": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)}
