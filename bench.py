@@ -14,14 +14,16 @@ over copies of their inputs and outputs, so every launch streams from HBM.
 The timed steps are captured into one HIP graph and replayed once between
 HIP events on the launch stream, so the figure is GPU time, not Python's
 per-call overhead.  Each workload times at least 50 launches (20 for the
-prefill), after at least 5 warm-up launches.
+prefill), after at least 5 warm-up launches.  After the timed steps the
+headline launch is replayed for about 8 s ("sustained"; not part of the
+value), and the matrix-product lines report the median of 5 replays.
 
 Printed: one JSON line with GB/s of algorithmic bytes (input read once plus
 every output written once), its fraction of the 8 TB/s HBM peak, the five
 workloads, the other entry points, a plain device copy for context, and the
 CPU oracle timed on bounded samples of every workload on this host.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--sustain S] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
