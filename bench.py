@@ -15,10 +15,11 @@ The timed steps are captured into one HIP graph and replayed once between
 HIP events on the launch stream, so the figure is GPU time, not Python's
 per-call overhead.  Each workload times at least 50 launches (20 for the
 prefill), after at least 5 warm-up launches; every line but the headline
-first replays its graph once untimed, since the clocks ramp up over the first
-milliseconds of work after an idle gap such as the capture.  After the timed steps the
-headline launch is replayed for about 8 s ("sustained"; not part of the
-value), and the matrix-product lines report the median of 5 replays.
+first replays its graph untimed for 25 ms, since the clocks ramp up over the
+first milliseconds of work after an idle gap such as the capture.  After the
+timed steps the headline launch is replayed for about 8 s ("sustained"; not
+part of the value), and the matrix-product lines report the median of 5
+replays.
 
 Printed: one JSON line with GB/s of algorithmic bytes (input read once plus
 every output written once), its fraction of the 8 TB/s HBM peak, the five
@@ -92,17 +93,17 @@ class Timed:
     the GPU's and not Python's per-call overhead.  HIP events on the replay
     stream bracket the replay; the host synchronizes on both sides."""
 
-    def __init__(self, torch, eager=False, warm=0):
+    def __init__(self, torch, eager=False, warm_ms=0.0):
         self.torch = torch
         self.eager = eager
-        self.warm = warm
+        self.warm_ms = warm_ms
 
-    def run(self, fn, steps, warmup, replays=1, warm=None):
+    def run(self, fn, steps, warmup, replays=1):
         """replays > 1: the graph is replayed that many times, each timed on
-        its own, and the median replay is reported.  warm: untimed replays
-        first (the clocks ramp up over the first ten or so milliseconds of
-        work after an idle gap, such as the capture itself).  Eager: both
-        ignored."""
+        its own, and the median replay is reported.  warm_ms: the graph is
+        first replayed untimed until that much time has passed (the clocks
+        ramp up over the first ten or so milliseconds of work after an idle
+        gap, such as the capture itself).  Eager: both ignored."""
         torch = self.torch
         for i in range(warmup):
             fn(i)
@@ -124,9 +125,10 @@ class Timed:
                 fn(i)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        for _ in range(self.warm if warm is None else warm):
+        t_warm = time.perf_counter()
+        while self.warm_ms > 0 and (time.perf_counter() - t_warm) * 1e3 < self.warm_ms:
             g.replay()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         times, wall = [], 0.0
         for _ in range(replays):
             start = torch.cuda.Event(enable_timing=True)
@@ -212,9 +214,9 @@ def bench_headline(torch, mx, synth, steps, warmup, sustain_s=0.0):
 
 def bench_configs(torch, mx, synth, steps):
     """The other four workloads, each at least 50 launches (20 for the 65536-row
-    prefill) after 5 warm-up launches and one untimed replay of the graph."""
+    prefill) after 5 warm-up launches and 25 ms of untimed graph replays."""
     dev = torch.device("cuda:0")
-    T = Timed(torch, EAGER, warm=1)   # one untimed replay: the clocks settle first
+    T = Timed(torch, EAGER, warm_ms=25.0)   # untimed replays first: the clocks settle
     res = {}
     k_small = max(50, steps // 2)
     k_large = max(20, steps // 10)
@@ -271,7 +273,7 @@ def bench_other_rows(torch, mx, synth, steps):
     """The entry points outside the five workloads, each on its own input."""
     dev = torch.device("cuda:0")
     res = {}
-    T = Timed(torch, EAGER, warm=1)   # one untimed replay: the clocks settle first
+    T = Timed(torch, EAGER, warm_ms=25.0)   # untimed replays first: the clocks settle
 
     x = synth.workload("rowwise_8192x7168", device=dev)["x"]
     r, c = x.shape
@@ -342,7 +344,7 @@ def bench_gemm(torch, mx, steps):
     """The MXFP8 product of a quantized activation and a quantized weight:
     TFLOP/s (2 M N K per launch) against the dense fp8 matrix-core peak."""
     dev = torch.device("cuda:0")
-    T = Timed(torch, EAGER, warm=1)   # one untimed replay: the clocks settle first
+    T = Timed(torch, EAGER, warm_ms=25.0)   # untimed replays first: the clocks settle
     res = {}
     # 4096 x 4096 x 11008: an MLP down projection, K not a multiple of 512
     # "_mfma_scales": both operands' scales in the MFMA order (K % 512 == 0)
