@@ -1,13 +1,18 @@
 """A seeded sweep of random shapes through every route of the library,
-against the oracle: rowwise-only (flat tasks), columnwise-only and both
-planes (tile tasks), bf16 and float32 input, compact and padded scale planes,
-and the matrix product on each of its tilings."""
+against the oracle: rowwise-only (flat tasks), columnwise-only (tiles, and
+the narrow path for rows of any length) and both planes, bf16 and float32
+input, compact and padded scale planes, grouped lists spanning launches, the
+fused RMSNorm, dequantize on both axes, and the matrix product on each of its
+tilings (within the accumulation bound)."""
 import numpy as np
 import pytest
 import torch
 
 import mxfp8_block_scaled_02_amd as mx
 from mxfp8_block_scaled_02_amd import synth
+from tests import gemm_accuracy as acc
+from tests import oracle_pins as P
+from tests.test_gpu_parity import check_fused_out
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -23,7 +28,11 @@ def random_case(g):
     if kind == 0:
         return int(g.integers(1, 300)), 32 * int(g.integers(1, 80)), True, False
     rows = 32 * int(g.integers(1, 9))
-    cols = 8 * int(g.integers(1, 400)) if kind == 1 else 32 * int(g.integers(1, 100))
+    if kind == 1:
+        # columnwise only: rows of any length (not a multiple of 8: the narrow path)
+        cols = 8 * int(g.integers(1, 400)) if g.random() < 0.6 else int(g.integers(1, 3200))
+    else:
+        cols = 32 * int(g.integers(1, 100))
     return rows, cols, kind == 2, True
 
 
@@ -96,4 +105,85 @@ def test_random_gemm_shapes(orc, seed):
         got = mx.gemm(pa.rowwise_data, pa.rowwise_scale, pb.rowwise_data, pb.rowwise_scale, torch.float32)
         torch.cuda.synchronize()
         err = np.abs(got.cpu().numpy().astype(np.float64) - C)
-        assert (err <= 2.0 ** -10 * mag).all(), "gemm %s beyond tolerance" % ((M, N, K),)
+        tol = acc.bound(*(t.cpu().numpy() for t in (pa.rowwise_data, pa.rowwise_scale,
+                                                     pb.rowwise_data, pb.rowwise_scale)))
+        assert (err <= tol).all(), "gemm %s beyond the accumulation bound" % ((M, N, K),)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_rmsnorm(orc, seed):
+    """Rows of every RMSNorm variant (one wave, four waves, sixteen waves a row,
+    rows read twice past 16384 columns), random offsets and epsilons, row
+    scales over 2^-20 .. 2^20."""
+    g = np.random.default_rng(3000 + seed)
+    for case in range(8):
+        rows = int(g.choice([int(g.integers(1, 17)), int(g.integers(17, 300)), int(g.integers(300, 1200))]))
+        cols = 32 * int(g.choice([int(g.integers(1, 64)), int(g.integers(64, 300)), int(g.integers(300, 700))]))
+        off = float(g.choice([0.0, 1.0, -0.25]))
+        eps = float(g.choice([1e-6, 1e-5, 1e-3]))
+        say("rmsnorm seed", seed, "case", case, (rows, cols), off, eps)
+        x = input_tensor(rows, cols, g, torch.bfloat16)
+        gamma = torch.from_numpy((1.0 + 0.1 * g.standard_normal(cols)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+        normed, q, s = mx.rmsnorm_quantize(x, gamma, off, eps)
+        torch.cuda.synchronize()
+        check_fused_out(orc, synth.bf16_bits(x), synth.bf16_bits(gamma), off, eps, synth.bf16_bits(normed),
+                        q.cpu().numpy(), s.cpu().numpy(), "rmsnorm %s" % ((rows, cols),))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_dequantize(orc, seed):
+    """Random codes (NaN codes included) under random scale bytes (0xFF
+    included), both axes, rows of any length on the columnwise axis, float32
+    and bf16 output."""
+    g = np.random.default_rng(4000 + seed)
+    for case in range(10):
+        axis = mx.ROWWISE if g.random() < 0.5 else mx.COLUMNWISE
+        if axis == mx.ROWWISE:
+            rows, cols = int(g.integers(1, 300)), 32 * int(g.integers(1, 80))
+            sshape = (rows, cols // 32)
+        else:
+            rows = 32 * int(g.integers(1, 9))
+            cols = 8 * int(g.integers(1, 400)) if g.random() < 0.6 else int(g.integers(1, 3200))
+            sshape = (rows // 32, cols)
+        dtype = torch.float32 if g.random() < 0.5 else torch.bfloat16
+        say("dequantize seed", seed, "case", case, (rows, cols), axis, dtype)
+        q = g.integers(0, 256, (rows, cols), dtype=np.uint8)
+        s = g.integers(90, 170, sshape, dtype=np.uint8)
+        s[g.random(sshape) < 0.02] = 0xFF
+        got = mx.dequantize(torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV), axis, dtype)
+        torch.cuda.synchronize()
+        want = orc.dequantize(q, s, axis)
+        if dtype == torch.bfloat16:
+            want = P.bf16_values(orc.round_bf16(want))
+        g64 = got.float().cpu().numpy().astype(np.float64)
+        assert ((g64 == want) | (np.isnan(g64) & np.isnan(want))).all(), "dequantize %s" % ((rows, cols),)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_grouped(orc, seed):
+    """Lists of up to 90 tensors of random shapes (more than one launch past
+    64), one request for the whole list, bf16 or float32."""
+    g = np.random.default_rng(5000 + seed)
+    n = int(g.integers(1, 91))
+    rw, cw = [(True, False), (False, True), (True, True)][int(g.integers(0, 3))]
+    dtype = torch.bfloat16 if g.random() < 0.6 else torch.float32
+    shapes = []
+    for _ in range(n):
+        rows = 32 * int(g.integers(1, 4)) if cw else int(g.integers(1, 100))
+        cols = 32 * int(g.integers(1, 33)) if rw else (8 * int(g.integers(1, 130)) if g.random() < 0.7
+                                                          else int(g.integers(1, 1000)))
+        shapes.append((rows, cols))
+    say("grouped seed", seed, n, "tensors", "row" if rw else "", "col" if cw else "", dtype)
+    xs = [input_tensor(r, c, g, dtype) for r, c in shapes]
+    ps = mx.quantize_grouped(xs, rw, cw)
+    torch.cuda.synchronize()
+    for i, (x, p) in enumerate(zip(xs, ps)):
+        xb = host_bits(x)
+        if rw:
+            q, s = orc.quantize_rowwise(xb)
+            assert np.array_equal(p.rowwise_data.cpu().numpy(), q), "tensor %d rowwise data" % i
+            assert np.array_equal(p.rowwise_scale.cpu().numpy(), s), "tensor %d rowwise scales" % i
+        if cw:
+            q, s = orc.quantize_colwise(xb)
+            assert np.array_equal(p.columnwise_data.cpu().numpy(), q), "tensor %d columnwise data" % i
+            assert np.array_equal(p.columnwise_scale.cpu().numpy(), s), "tensor %d columnwise scales" % i
