@@ -13,6 +13,7 @@ import torch
 
 import mxfp8_block_scaled_02_amd as mx
 from mxfp8_block_scaled_02_amd import synth
+from tests import gemm_accuracy as acc
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -165,10 +166,10 @@ def test_gemm_padded_scales_large(orc, mnk, pitch):
     g = np.random.default_rng(5)
     ms, ns = g.integers(0, M, 3000), g.integers(0, N, 3000)
     host = lambda t: t.cpu().numpy()
-    C, mag = orc.gemm_at(host(pa.rowwise_data), host(pa.rowwise_scale), host(pb.rowwise_data),
-                         host(pb.rowwise_scale), ms, ns)
+    planes = [host(pa.rowwise_data), host(pa.rowwise_scale), host(pb.rowwise_data), host(pb.rowwise_scale)]
+    C, _ = orc.gemm_at(*planes, ms, ns)
     err = np.abs(host(got)[ms, ns].astype(np.float64) - C)
-    assert (err <= 2.0 ** -10 * mag).all()
+    assert (err <= acc.bound_at(*planes, ms, ns)).all()
 
 
 def test_scale_view_strides_checked():
