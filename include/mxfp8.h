@@ -44,8 +44,10 @@
  *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
  *     it and the call returns at once; results are ready when the stream is.
  *   - Every argument is checked before anything is launched, so a call that
- *     returns an error has written nothing.  rows == 0 or cols == 0 is a
- *     no-op that returns MXFP8_OK.  Device faults surface at the caller's
+ *     returns an argument error has enqueued nothing.  (MXFP8_ERR_HIP from a
+ *     grouped call long enough to need several launches can follow launches
+ *     already enqueued.)  rows == 0 or cols == 0 is a no-op that returns
+ *     MXFP8_OK.  Device faults surface at the caller's
  *     next synchronization, as with any HIP work.
  *   - The library keeps no state: calls may come from any thread.
  */
