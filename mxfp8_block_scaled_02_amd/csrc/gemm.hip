@@ -830,15 +830,29 @@ struct Skinny {
   }
 };
 
-template <int MT, int SC>
-__global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams p) {
+template <int MT, int SC, bool RB = false>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams pp) {
+  // RB, row blocks (for weights too narrow to give every CU a column strip):
+  // workgroups R i .. R i + R - 1 (R = tiles_m) take rows 32 MT r .. of A
+  // for column strip i.
+  GemmParams p = pp;
+  uint32_t bid = blockIdx.x;
+  if constexpr (RB) {
+    const uint32_t nrb = (uint32_t)pp.tiles_m, rb = bid % nrb;
+    bid /= nrb;
+    const int64_t r0 = (int64_t)rb * 32 * MT;
+    p.qa += r0 * p.K;
+    p.sa += r0 * p.sa_ld;
+    p.out = static_cast<uint8_t*>(p.out) + r0 * p.ldo * (p.out_bf16 ? 2 : 4);
+    p.M = min(p.M - r0, (int64_t)(32 * MT));
+  }
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSkinnyWaves * (1 + MT) * kSkinnyRegion];
   __shared__ uint32_t slds[SC == kSkinnyStaged ? kSkinnyWaves * (1 + MT) * staged_tile<MT>() : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 31, h = lane >> 5;
-  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const int64_t n0 = (int64_t)bid * 32;
   const int64_t units = p.K / 128;
   constexpr bool kPaired = SC == kSkinnyPaired;
   // PAIRED: every wave's range starts at an even unit, so each pair of scale
@@ -926,15 +940,16 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
 // staged scale words when every wave's range fits the staging area (K up to
 // 16384 for one or two A tiles, 8192 for four), otherwise paired loads (which
 // need K >= 256, true whenever staging does not fit)
-template <int MT>
+// RB: the workgroups are column strips times the row blocks in p.tiles_m
+template <int MT, bool RB = false>
 void launch_skinny(const GemmParams& p, int64_t workgroups, hipStream_t s) {
   const int64_t units = p.K / 128, per_wave = (units + kSkinnyWaves - 1) / kSkinnyWaves;
   const bool staged = per_wave <= staged_units<MT>();
   if (staged)
-    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, kSkinnyStaged>), dim3((uint32_t)workgroups),
+    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, kSkinnyStaged, RB>), dim3((uint32_t)workgroups),
                        dim3(kSkinnyWaves * 64), 0, s, p);
   else
-    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, kSkinnyPaired>), dim3((uint32_t)workgroups),
+    hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<MT, kSkinnyPaired, RB>), dim3((uint32_t)workgroups),
                        dim3(kSkinnyWaves * 64), 0, s, p);
 }
 
@@ -952,7 +967,20 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.sa_gs = sa_stride.grp; p.sb_gs = sb_stride.grp;
   p.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t skinny = (N + 31) / 32;
-  if (M <= 32) {
+  // A weight of few column strips leaves CUs idle (each workgroup streams its
+  // strip at a fixed rate): rows are then split into blocks of 32, or else of
+  // 64, over more workgroups while those still fit one per CU (measured with
+  // the weight read from HBM: 128 x 1024 x 4096 18.0 -> 10.6 us, 128 x 4096 x
+  // 4096 19.2 -> 14.8 us, 80 x 4096 x 14336 50.1 -> 35.3 us, 64 x 4096 x 4096
+  // 13.0 -> 11.2 us; splitting further than one workgroup per CU is slower,
+  // 128 x 7168 x 7168 in 64-row halves 28.9 -> 39.4 us)
+  if (M > 32 && M <= 128 && ((M + 31) / 32) * skinny <= kCUs) {
+    p.tiles_m = (int32_t)((M + 31) / 32);
+    launch_skinny<1, true>(p, p.tiles_m * skinny, s);
+  } else if (M > 64 && M <= 128 && 2 * skinny <= kCUs) {
+    p.tiles_m = (int32_t)((M + 63) / 64);
+    launch_skinny<2, true>(p, p.tiles_m * skinny, s);
+  } else if (M <= 32) {
     launch_skinny<1>(p, skinny, s);
   } else if (M <= 64) {
     launch_skinny<2>(p, skinny, s);

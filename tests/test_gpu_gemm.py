@@ -191,18 +191,22 @@ def test_gemm_bf16_output_is_rounded_f32_output(mnk):
                                  (31, 33, 640), (17, 2048, 1152),
                                  # K = 256: two units; a wave's only unit may be the second of two
                                  (8, 64, 256), (20, 300, 256), (40, 130, 256),
-                                 # scale words loaded in pairs instead of staged in LDS: more than
-                                 # 32 units per wave (one or two A tiles), more than 16 (four)
-                                 (16, 96, 16896), (40, 130, 16512), (100, 64, 8320),
-                                 # K = 128: one unit, one active wave, staged words of one unit
-                                 # with two and four A tiles
+                                 # scale words loaded in pairs instead of staged in LDS (more than
+                                 # 32 units per wave with one or two A tiles, more than 16 with
+                                 # four): one tile, one tile per 32-row block
+                                 (16, 96, 16896), (40, 130, 16512),
+                                 # K = 128: one unit, one active wave
                                  (33, 64, 128), (100, 200, 128),
-                                 # two 32-row A tiles per workgroup
-                                 (64, 7168, 7168), (48, 2048, 1024), (33, 100, 384), (64, 4096, 128),
-                                 # four 32-row A tiles (64 < M <= 128)
-                                 (128, 7168, 7040), (97, 1000, 640), (65, 2048, 256),
-                                 # 64 < M <= 128 with K % 512 == 0: also four A tiles
-                                 (128, 7168, 7168), (97, 3000, 2048), (65, 200, 512)])
+                                 # 32 < M <= 128 with (M / 32 rounded up) x (N / 32 rounded up) <= 256
+                                 # workgroups: one 32-row block per workgroup, the last one ragged
+                                 (48, 2048, 1024), (33, 100, 384), (64, 4096, 128), (97, 1000, 640),
+                                 (65, 2048, 256), (65, 200, 512), (100, 64, 8320),
+                                 # two 32-row A tiles per workgroup (32 < M <= 64, N > 4096)
+                                 (64, 7168, 7168), (40, 4200, 16512),
+                                 # two A tiles per 64-row block (64 < M <= 128, 2 x N / 32 <= 256)
+                                 (97, 3000, 2048), (65, 2750, 16512),
+                                 # four 32-row A tiles (64 < M <= 128, N > 4096)
+                                 (128, 7168, 7040), (128, 7168, 7168), (100, 4200, 8320)])
 def test_gemm_skinny_decode(orc, mnk):
     """A few activation rows (decode): the K-split skinny path, including K
     with fewer 128-deep units than waves and N not a multiple of 32."""
