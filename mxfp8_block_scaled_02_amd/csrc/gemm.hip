@@ -967,19 +967,26 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.sa_gs = sa_stride.grp; p.sb_gs = sb_stride.grp;
   p.out_bf16 = out_bf16 ? 1 : 0;
   const int64_t skinny = (N + 31) / 32;
+  const int64_t r32 = (M + 31) / 32, r64 = (M + 63) / 64, r128 = (M + 127) / 128;
   // A weight of few column strips leaves CUs idle (each workgroup streams its
-  // strip at a fixed rate): rows are then split into blocks of 32, or else of
-  // 64, over more workgroups while those still fit one per CU (measured with
-  // the weight read from HBM: 128 x 1024 x 4096 18.0 -> 10.6 us, 128 x 4096 x
-  // 4096 19.2 -> 14.8 us, 80 x 4096 x 14336 50.1 -> 35.3 us, 64 x 4096 x 4096
-  // 13.0 -> 11.2 us; splitting further than one workgroup per CU is slower,
-  // 128 x 7168 x 7168 in 64-row halves 28.9 -> 39.4 us)
-  if (M > 32 && M <= 128 && ((M + 31) / 32) * skinny <= kCUs) {
-    p.tiles_m = (int32_t)((M + 31) / 32);
-    launch_skinny<1, true>(p, p.tiles_m * skinny, s);
-  } else if (M > 64 && M <= 128 && 2 * skinny <= kCUs) {
-    p.tiles_m = (int32_t)((M + 63) / 64);
-    launch_skinny<2, true>(p, p.tiles_m * skinny, s);
+  // strip at a fixed rate, and the ring tiles of such a product are few): the
+  // rows are then split into blocks of 32, else 64, else (M <= 512) 128 rows,
+  // one workgroup per block and strip, while those still fit one per CU.
+  // Measured with the weight read from HBM: 128 x 1024 x 4096 18.0 -> 10.8
+  // us, 80 x 4096 x 14336 50.1 -> 35.2 us, 192 x 1024 x 7168 (ring tiles
+  // before) 39.5 -> 16.9 us, 512 x 1024 x 7168 39.6 -> 24.5 us, 512 x 2048 x
+  // 7168 40.5 -> 31.2 us.  128-row blocks past M = 512 measured 0.95 to 1.09
+  // times the ring tiles and are not taken; splitting further than one
+  // workgroup per CU loses (128 x 7168 x 7168 in 64-row halves 28.9 -> 39.4 us)
+  if (M > 32 && r32 * skinny <= kCUs) {
+    p.tiles_m = (int32_t)r32;
+    launch_skinny<1, true>(p, r32 * skinny, s);
+  } else if (M > 64 && r64 * skinny <= kCUs) {
+    p.tiles_m = (int32_t)r64;
+    launch_skinny<2, true>(p, r64 * skinny, s);
+  } else if (M > 128 && M <= 512 && r128 * skinny <= kCUs) {
+    p.tiles_m = (int32_t)r128;
+    launch_skinny<4, true>(p, r128 * skinny, s);
   } else if (M <= 32) {
     launch_skinny<1>(p, skinny, s);
   } else if (M <= 64) {

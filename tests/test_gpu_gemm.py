@@ -59,7 +59,9 @@ def run(orc, qa, sa, qb, sb, what):
 
 
 @pytest.mark.parametrize("mnk", [(128, 128, 128), (256, 384, 512), (100, 130, 256), (1, 512, 1024),
-                                 (300, 7, 128), (257, 129, 384)])
+                                 (300, 7, 128), (257, 129, 384),
+                                 # ring tiles (64 x 128) and the tile128 tiles, ragged both ways
+                                 (600, 900, 512), (600, 900, 384)])
 def test_gemm_quantized_activation_and_weight(orc, mnk):
     M, N, K = mnk
     qa, sa = quantized(M, K, 1.0, seed=M + K)
@@ -75,7 +77,7 @@ def random_planes(rows, K, seed, lo=110, hi=145):
     return torch.from_numpy(q).to(DEV), torch.from_numpy(s).to(DEV)
 
 
-@pytest.mark.parametrize("mnk", [(128, 128, 256), (192, 320, 640)])
+@pytest.mark.parametrize("mnk", [(128, 128, 256), (192, 320, 640), (600, 900, 640)])
 def test_gemm_random_planes_full_range(orc, mnk):
     M, N, K = mnk
     qa, sa = random_planes(M, K, seed=1)
@@ -112,8 +114,8 @@ def test_gemm_nan_in_short_last_group(orc):
     k 448..511 with scale bytes 0.  NaN data and NaN scales in the repeated
     stage and in the live part of the short group give NaN exactly where the
     oracle's product has it."""
-    qa, sa = quantized(256, 640, 1.0, seed=12)
-    qb, sb = quantized(320, 640, 0.05, seed=13)
+    qa, sa = quantized(600, 640, 1.0, seed=12)
+    qb, sb = quantized(900, 640, 0.05, seed=13)
     qa[5, 460] = 0x7F                                     # NaN element in the repeated stage
     qb[9, 600] = 0xFF                                     # NaN element past k 512
     sa[4, 14] = 0xFF                                      # NaN scale of k 448..479
@@ -138,13 +140,16 @@ def test_gemm_nan_scale(orc):
     # 128 x 128 tiles:
     (500, 7000, 1024), (400, 6000, 512),
     # 64 x 128 tiles (few tiles in all):
-    (300, 2048, 4096), (129, 1000, 512), (200, 300, 1024),
+    (600, 2048, 4096), (520, 1000, 512), (520, 900, 1024),
     # K % 512 != 0 with K >= 512: the ring tiles' short last group, whose first
     # 2, 4 or 6 stages repeat the stage before with scales 0, on each tile size
-    (4352, 3840, 640), (4096, 4096 + 256, 896), (500, 7000, 768), (129, 1000, 1152),
-    (300, 2048, 11008), (2000, 1000, 4224),
+    (4352, 3840, 640), (4096, 4096 + 256, 896), (500, 7000, 768), (520, 1000, 1152),
+    (600, 2048, 11008), (2000, 1000, 4224),
     # K < 512: the register-staged 128 x 128 tiling, odd 128-deep stage counts
-    (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (300, 500, 256)])
+    (4096 - 37, 4096 + 100, 384), (4096, 4096, 128), (600, 900, 256),
+    # the skinny kernel's row blocks past 128 rows with paired scale words
+    # (128-row blocks of four A tiles; 64-row blocks of two) and staged ones
+    (300, 2048, 11008), (129, 2752, 8320), (140, 1700, 16512), (300, 2048, 4096)])
 def test_gemm_large_tiles_ragged_sampled(orc, mnk):
     """Large problems: sampled outputs, every column of the last row and every
     row of the last column."""
@@ -165,10 +170,11 @@ def test_gemm_large_tiles_ragged_sampled(orc, mnk):
         check_close(got, C, tol, dtype == torch.bfloat16, "large tiles %s" % ((M, N, K),))
 
 
-@pytest.mark.parametrize("mnk", [(256, 256, 512), (4352, 3840, 640), (4096, 4096 + 256, 1024), (500, 7000, 768),
-                                 (129, 1000, 1152), (512, 1030, 512), (300, 2047, 640), (260, 130, 128),
-                                 (40, 300, 1024), (256, 384, 256), (384, 1152, 384), (4096, 4096, 128),
-                                 (1000, 4096, 384)])
+@pytest.mark.parametrize("mnk", [(1024, 1024, 512), (4352, 3840, 640), (4096, 4096 + 256, 1024), (500, 7000, 768),
+                                 (520, 1000, 1152), (520, 1030, 512), (600, 2047, 640), (2000, 260, 128),
+                                 (2100, 384, 256), (700, 1152, 384), (4096, 4096, 128), (1000, 4096, 384),
+                                 # the skinny kernel: one, two and four A tiles per row block
+                                 (129, 1000, 1152), (40, 300, 1024), (384, 1152, 384), (300, 2047, 640)])
 def test_gemm_bf16_output_is_rounded_f32_output(mnk):
     """The bf16 output equals the float32 output of the same call rounded to
     nearest even, element for element.  Full ring tiles with an even N store
@@ -206,7 +212,11 @@ def test_gemm_bf16_output_is_rounded_f32_output(mnk):
                                  # two A tiles per 64-row block (64 < M <= 128, 2 x N / 32 <= 256)
                                  (97, 3000, 2048), (65, 2750, 16512),
                                  # four 32-row A tiles (64 < M <= 128, N > 4096)
-                                 (128, 7168, 7040), (128, 7168, 7168), (100, 4200, 8320)])
+                                 (128, 7168, 7040), (128, 7168, 7168), (100, 4200, 8320),
+                                 # M > 128 with a narrow weight: 32-row blocks (up to 32 per strip),
+                                 # 64-row blocks (65 per strip; the last of two rows), 128-row blocks
+                                 (200, 1000, 640), (1000, 100, 384), (4100, 40, 256), (300, 1500, 1024),
+                                 (130, 1700, 512), (500, 2000, 1024)])
 def test_gemm_skinny_decode(orc, mnk):
     """A few activation rows (decode): the K-split skinny path, including K
     with fewer 128-deep units than waves and N not a multiple of 32."""
@@ -216,9 +226,11 @@ def test_gemm_skinny_decode(orc, mnk):
     run(orc, qa, sa, qb, sb, "skinny")
 
 
-@pytest.mark.parametrize("mnk", [(1000, 4096, 384), (260, 130, 128), (256, 256, 512), (300, 2048, 4096),
-                                 (4352, 3840, 640), (129, 1000, 512), (16, 7168, 7168), (100, 200, 512),
-                                 (5, 96, 128)])
+@pytest.mark.parametrize("mnk", [(1000, 4096, 384), (2000, 260, 128), (1024, 1024, 512), (520, 1000, 512),
+                                 (4352, 3840, 640), (16, 7168, 7168), (5, 96, 128),
+                                 # the skinny kernel's row blocks: 32, 64 and 128 rows
+                                 (100, 200, 512), (260, 130, 128), (129, 1000, 512), (384, 1152, 384),
+                                 (300, 2048, 4096)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_gemm_output_guard_bands(mnk, dtype):
     """The product written into an [M, N] view of a larger buffer filled with

@@ -149,8 +149,8 @@ def test_dequantize(shape):
 
 
 @pytest.mark.parametrize("mnk", [
-    (256, 256, 512), (1024, 7168, 7168), (4352, 3840, 1536), (300, 2048, 4096),   # ring tiles
-    (16, 4096, 4096), (40, 1000, 2048), (100, 200, 512),                          # skinny, staged words
+    (1024, 1024, 512), (1024, 7168, 7168), (4352, 3840, 1536), (600, 2048, 4096),  # ring tiles
+    (16, 4096, 4096), (40, 1000, 2048), (100, 200, 512), (300, 2048, 4096),       # skinny, staged words
     (16, 96, 16896), (40, 130, 16896), (100, 64, 8704)])                          # skinny, paired words
 def test_gemm_matches_compact_scales(mnk):
     """The product from MFMA-order scale planes equals the product from the

@@ -93,9 +93,11 @@ def test_random_shapes_and_routes(orc, seed):
 def test_random_gemm_shapes(orc, seed):
     g = np.random.default_rng(2000 + seed)
     for case in range(8):
-        M = int(g.choice([int(g.integers(1, 33)), int(g.integers(33, 129)), int(g.integers(129, 400))]))
-        N = int(g.integers(1, 700))
-        K = 128 * int(g.integers(1, 9))
+        M = int(g.choice([int(g.integers(1, 33)), int(g.integers(33, 129)), int(g.integers(129, 400)),
+                          int(g.integers(513, 1200))]))
+        # a wide weight under many rows takes the ring or tile128 tiles
+        N = int(g.integers(1, 700)) if M <= 512 else int(g.integers(700, 1500))
+        K = 128 * int(g.integers(1, 9 if M <= 512 else 5))
         say("gemm seed", seed, "case", case, (M, N, K))
         a = input_tensor(M, K, g, torch.bfloat16)
         b = input_tensor(N, K, g, torch.bfloat16)
