@@ -346,11 +346,13 @@ def bench_gemm(torch, mx, steps):
     dev = torch.device("cuda:0")
     T = Timed(torch, EAGER, warm_ms=25.0)   # untimed replays first: the clocks settle
     res = {}
-    # 4096 x 4096 x 11008: an MLP down projection, K not a multiple of 512
+    # 4096 x 4096 x 11008: an MLP down projection, K not a multiple of 512;
+    # 256 x 2048 x 7168: 256 tokens through one 2048 x 7168 expert weight
     # "_mfma_scales": both operands' scales in the MFMA order (K % 512 == 0)
     for M, N, K, order in ((8192, 8192, 8192, "row"), (8192, 8192, 8192, "mfma"),
                            (1024, 7168, 7168, "row"), (1024, 7168, 7168, "mfma"),
-                           (4096, 4096, 11008, "row"), (128, 7168, 7168, "row"), (128, 7168, 7168, "mfma"),
+                           (4096, 4096, 11008, "row"), (256, 2048, 7168, "row"),
+                           (128, 7168, 7168, "row"), (128, 7168, 7168, "mfma"),
                            (16, 7168, 7168, "row"), (16, 7168, 7168, "mfma")):
         g = torch.Generator(device=dev).manual_seed(M + N + K)
         a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
@@ -372,7 +374,7 @@ def bench_gemm(torch, mx, steps):
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         rec = {"ms_per_launch": round(ms, 5), "TFLOP_s": round(tf, 1),
                "frac_mfma_fp8": round(tf / FP8_MFMA_PEAK_TFLOPS, 4)}
-        if M <= 128:
+        if M <= 512:
             # a few rows against a large weight: bound by streaming the planes
             # of B (and A) once and writing the output
             alg = (M + N) * K * (1 + 1 / 32) + M * N * 2

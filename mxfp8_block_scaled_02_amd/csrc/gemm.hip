@@ -833,11 +833,17 @@ struct Skinny {
 template <int MT, int SC, bool RB = false>
 __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams pp) {
   // RB, row blocks (for weights too narrow to give every CU a column strip):
-  // workgroups R i .. R i + R - 1 (R = tiles_m) take rows 32 MT r .. of A
-  // for column strip i.
+  // tasks R i .. R i + R - 1 (R = tiles_m) take rows 32 MT r .. of A for
+  // column strip i.
   GemmParams p = pp;
   uint32_t bid = blockIdx.x;
   if constexpr (RB) {
+    // workgroups go round-robin over the 8 XCDs: XCD x takes the x-th
+    // contiguous run of tasks, so the row blocks of a strip share its L2 and
+    // its B strip is fetched once (256 x 2048 x 7168: 22.7 -> 18.3 us, fetched
+    // bytes 0.45 times; 512 x 1024 x 7168: 25.2 -> 17.8 us)
+    const uint32_t T = gridDim.x, xcd = bid % 8, slot = bid / 8, per = T / 8, rem = T % 8;
+    bid = xcd * per + (xcd < rem ? xcd : rem) + slot;
     const uint32_t nrb = (uint32_t)pp.tiles_m, rb = bid % nrb;
     bid /= nrb;
     const int64_t r0 = (int64_t)rb * 32 * MT;
