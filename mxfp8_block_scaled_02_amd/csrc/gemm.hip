@@ -19,7 +19,7 @@
 //
 // Three kinds of tiling share that fragment layout:
 //
-// * ring tiles (M > 128, K >= 512): a workgroup of
+// * ring tiles (M > 128, K >= 512, a weight wide enough to fill the CUs): a workgroup of
 //   four waves (2 x 2) computes a 256 x 256, 128 x 256, 128 x 128 or 64 x 128
 //   tile, one workgroup per CU.  K advances in stages of 64 bytes through a ring of four
 //   LDS slots that the loads fill directly (global_load_lds_dwordx4, no
@@ -37,10 +37,13 @@
 //   the 256 CUs take least time: large tiles move fewer bytes per MFMA, small
 //   ones keep more CUs busy when M or N is small.
 // * tile128: 128 x 128 tiles (four waves of 64 x 64) staged through registers
-//   into padded LDS rows; it takes the problems with M > 128 and K < 512.
-// * skinny (decode and small batches, M <= 128): 32 output columns per
-//   workgroup, K split over its waves, B streamed once through LDS (see the
-//   section below).
+//   into padded LDS rows; it takes the problems with M > 128 and K < 512 that
+//   the skinny kernel does not.
+// * skinny (decode and small batches, M <= 128; or any M whose 32-, 64- or,
+//   up to 512 rows, 128-row blocks times the 32-column strips of B fit one
+//   workgroup per CU): 32 output columns of one row block per workgroup, K
+//   split over its waves, B streamed once through LDS (see the section
+//   below).
 //
 // Rows of A or B past M or N read a valid row (the last one) and their
 // outputs are not stored.  K must be a multiple of 128, and the scale planes'
@@ -602,7 +605,10 @@ __global__ __launch_bounds__(kThreads) void mxfp8_gemm_tile128_kernel(const Gemm
 // 8 rows x 128 bytes (1 KiB).  It writes them into its own LDS region (the
 // 16-byte chunk c of row r at chunk c ^ (r % 8) ^ ((r / 8) % 2)), reads the
 // MFMA fragments back, and multiplies.  A rows past M are zero.  The four
-// partial tiles meet in LDS and are summed in wave order.
+// partial tiles meet in LDS and are summed in wave order.  Under a weight of
+// few strips the rows are cut into blocks, one workgroup per block and
+// strip, and the blocks of a strip run on one XCD so that its L2 serves them
+// the strip (the launcher's notes give the rule and its measurements).
 //
 // Measured on 16 x 7168 x 7168 with the weight read from HBM (rotating
 // copies): loading B straight into LDS (global_load_lds) and the A fragments
