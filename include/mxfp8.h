@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MXFP8_ABI_VERSION 3
+#define MXFP8_ABI_VERSION 4
 #define MXFP8_BLOCK 32
 /* Descriptors handled by one kernel launch in the grouped calls; longer
  * lists are processed in consecutive launches of at most this many.  A list
@@ -71,6 +71,9 @@ extern "C" {
 /* A rowwise scale pitch of this value selects the MFMA order (see "Scale
  * pitches"). */
 #define MXFP8_SCALES_MFMA ((int64_t)-1)
+/* A columnwise scale pitch of this value in a quantize descriptor stores the
+ * columnwise plane transposed (see "Transposed columnwise plane"). */
+#define MXFP8_COLUMNWISE_T ((int64_t)-2)
 
 typedef enum {
     MXFP8_OK = 0,
@@ -231,6 +234,35 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
  * Quantize, the fused RMSNorm and dequantize write or read it in their one
  * pass; the matrix product loads each 512-deep group's scales of 64 rows as
  * one contiguous 1 KiB run instead of 64 separate 16-byte pieces.
+ */
+
+/*
+ * Transposed columnwise plane (quantize descriptors only; s_col_pitch
+ * MXFP8_COLUMNWISE_T).  The columnwise plane's blocks run down the columns of
+ * x (quantized_dbuffer page, _block_atomic_to_flat), and the pages store it
+ * in x's layout.  Each training phase installs the planes it uses
+ * (quantized_dbuffer page, update_mxfp8_tensor); the library's reading is
+ * the usual one, the columnwise planes serve the backward products, which
+ * contract over the rows of x: the input gradient takes the weight's
+ * columnwise plane, the weight gradient both activations'.  mxfp8_gemm, like
+ * gfx950's block-scaled MFMA whose operand fragments hold consecutive k of
+ * one row, reads operands whose 32-element blocks are contiguous.  With this
+ * pitch the quantize writes the columnwise plane in that order, in the same
+ * pass, with the same bytes:
+ *
+ *   q_col  uint8 e4m3 [cols, rows]   q_col[c, r] = the e4m3 byte of x[r, c]
+ *   s_col  uint8 e8m0 [cols, rows/32] s_col[c, b] = the scale of rows
+ *                                     32 b .. 32 b + 31 of column c
+ *
+ * so (q_col, s_col) is a rowwise plane of x^T, ready to be an operand of
+ * mxfp8_gemm (K = rows) or to be dequantized as a rowwise plane of
+ * [cols, rows].  Required: rows % 32 == 0 and cols % 8 == 0
+ * (MXFP8_ERR_SHAPE otherwise); the rowwise plane, if requested, follows its
+ * usual rules, pitches and MFMA order included.  mxfp8_quantize_grouped only
+ * (a single tensor is a grouped call with n == 1); mxfp8_quantize_f32_grouped
+ * refuses the pitch with MXFP8_ERR_SHAPE.  A grouped list that mixes
+ * transposed and untransposed columnwise planes takes one launch sequence for
+ * each kind.
  */
 
 /*

@@ -30,7 +30,7 @@ __all__ = [
 ]
 
 BLOCK = 32
-ABI_VERSION = 3
+ABI_VERSION = 4
 ROWWISE, COLUMNWISE = 0, 1
 _OUT_F32, _OUT_BF16 = 0, 1
 # Rowwise scales in the MFMA order (see include/mxfp8.h, "Scale pitches"):
@@ -38,6 +38,9 @@ _OUT_F32, _OUT_BF16 = 0, 1
 # passed to the library with the pitch MXFP8_SCALES_MFMA.
 MFMA_GROUP = 512
 _SCALES_MFMA = -1
+# The columnwise plane stored transposed (include/mxfp8.h, MXFP8_COLUMNWISE_T):
+# data [cols, rows], scales [cols, rows/32], a rowwise plane of x^T.
+_COLUMNWISE_T = -2
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
 _lib = None
@@ -251,19 +254,26 @@ def padded_scale_plane(rows: int, cols: int, axis: int = 0, row_multiple: int = 
     return buf, buf[:shape[0], :shape[1]]
 
 
-def _quant_desc(x, rowwise, columnwise, out, mfma=False):
+def _quant_desc(x, rowwise, columnwise, out, mfma=False, transposed=False):
     if x.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("x must be bfloat16 or float32, got %s" % x.dtype)
+    if transposed and x.dtype != torch.bfloat16:
+        raise ValueError("the transposed columnwise plane is written from bfloat16 input only")
     x2 = _as2d(x, "x", x.dtype)
     rows, cols = x2.shape
     o = out or MXFP8Planes(None, None, None, None)
     dev = x.device
     qr = _out(o.rowwise_data, (rows, cols), torch.uint8, dev, "rowwise_data") if rowwise else None
-    qc = _out(o.columnwise_data, (rows, cols), torch.uint8, dev, "columnwise_data") if columnwise else None
     sr, pr = (_scale_pitch(o.rowwise_scale, (rows, cols // BLOCK), dev, "rowwise_scale", mfma=mfma)
               if rowwise else (None, 0))
-    sc, pc = (_scale_pitch(o.columnwise_scale, (rows // BLOCK, cols), dev, "columnwise_scale")
-              if columnwise else (None, 0))
+    if columnwise and transposed:
+        qc = _out(o.columnwise_data, (cols, rows), torch.uint8, dev, "columnwise_data")
+        sc = _out(o.columnwise_scale, (cols, rows // BLOCK), torch.uint8, dev, "columnwise_scale")
+        pc = _COLUMNWISE_T
+    else:
+        qc = _out(o.columnwise_data, (rows, cols), torch.uint8, dev, "columnwise_data") if columnwise else None
+        sc, pc = (_scale_pitch(o.columnwise_scale, (rows // BLOCK, cols), dev, "columnwise_scale")
+                  if columnwise else (None, 0))
     if pc == _SCALES_MFMA:
         raise ValueError("columnwise_scale: the MFMA order is for rowwise scales only")
     d = _QuantDesc(_ptr(x2), rows, cols, _ptr(qr), _ptr(sr), _ptr(qc), _ptr(sc), pr, pc)
@@ -271,15 +281,20 @@ def _quant_desc(x, rowwise, columnwise, out, mfma=False):
 
 
 def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
-             out: Optional[MXFP8Planes] = None, scale_order: str = "row") -> MXFP8Planes:
+             out: Optional[MXFP8Planes] = None, scale_order: str = "row",
+             columnwise_transposed: bool = False) -> MXFP8Planes:
     """Quantize x [rows, cols] (bf16, or a float32 master weight) into the
     requested planes in one launch.
 
     ``out`` supplies persistent plane buffers that are overwritten in place
     (Megatron-Core quantization.utils page, quantize_params_to_mxfp8).
     ``scale_order="mfma"`` writes the rowwise scales in the MFMA order
-    (cols % 512 == 0), which ``gemm`` and ``dequantize`` accept as they are."""
-    d, planes = _quant_desc(x, rowwise, columnwise, out, _mfma(scale_order))
+    (cols % 512 == 0), which ``gemm`` and ``dequantize`` accept as they are.
+    ``columnwise_transposed=True`` (bf16 input, cols % 8 == 0) stores the
+    columnwise plane transposed, data [cols, rows] and scales
+    [cols, rows/32]: a rowwise plane of x^T, which ``gemm`` takes as an
+    operand contracting over the rows of x."""
+    d, planes = _quant_desc(x, rowwise, columnwise, out, _mfma(scale_order), columnwise_transposed)
     with _on(x.device):
         if d.s_row_pitch or d.s_col_pitch:
             # padded scale planes: a one-entry grouped call carries the pitches
@@ -292,8 +307,10 @@ def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
 
 
 def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwise: bool = False,
-                     outs: Optional[Sequence[MXFP8Planes]] = None, scale_order: str = "row") -> list:
-    """Quantize a list of tensors of any shapes (all bf16 or all float32) in one launch."""
+                     outs: Optional[Sequence[MXFP8Planes]] = None, scale_order: str = "row",
+                     columnwise_transposed: bool = False) -> list:
+    """Quantize a list of tensors of any shapes (all bf16 or all float32) in one
+    launch (``columnwise_transposed``: see ``quantize``)."""
     mfma = _mfma(scale_order)
     if not xs:
         return []
@@ -302,7 +319,7 @@ def quantize_grouped(xs: Sequence[torch.Tensor], rowwise: bool = True, columnwis
     for i, x in enumerate(xs):
         if x.device != dev or x.dtype != dt:
             raise ValueError("all tensors must share one device and one dtype")
-        d, p = _quant_desc(x, rowwise, columnwise, outs[i] if outs else None, mfma)
+        d, p = _quant_desc(x, rowwise, columnwise, outs[i] if outs else None, mfma, columnwise_transposed)
         descs.append(d)
         planes.append(p)
     arr = (_QuantDesc * len(descs))(*descs)

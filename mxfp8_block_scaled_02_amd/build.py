@@ -22,8 +22,8 @@ LIB = os.path.join(HERE, "libmxfp8.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "quantize_f32.hip", "rmsnorm_quantize.hip", "dequantize.hip", "gemm.hip",
-           "capi.cpp"]
+SOURCES = ["quantize.hip", "quantize_colt.hip", "quantize_f32.hip", "rmsnorm_quantize.hip", "dequantize.hip",
+           "gemm.hip", "capi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I", INCLUDE, "-I", CSRC,

@@ -31,9 +31,16 @@ bool flat_blocks_fit(int64_t rows, int64_t cols) { return rows * (cols / MXFP8_B
 // A rowwise scale plane in the MFMA order needs whole 512-element groups.
 bool mfma_order_ok(int64_t pitch, int64_t cols) { return pitch != MXFP8_SCALES_MFMA || cols % 512 == 0; }
 
+// The columnwise plane of d is requested and stored transposed.
+bool col_t(const mxfp8_quant_desc& d) {
+  return d.s_col_pitch == MXFP8_COLUMNWISE_T && (d.q_col != nullptr || d.s_col != nullptr);
+}
+
 mxfp8_status check_quant(const mxfp8_quant_desc& d) {
   if (d.rows < 0 || d.cols < 0 || !fits(d.rows, d.cols)) return MXFP8_ERR_SHAPE;
-  if ((d.s_row_pitch < 0 && d.s_row_pitch != MXFP8_SCALES_MFMA) || d.s_col_pitch < 0) return MXFP8_ERR_SHAPE;
+  if ((d.s_row_pitch < 0 && d.s_row_pitch != MXFP8_SCALES_MFMA) ||
+      (d.s_col_pitch < 0 && d.s_col_pitch != MXFP8_COLUMNWISE_T))
+    return MXFP8_ERR_SHAPE;
   if (!mfma_order_ok(d.s_row_pitch, d.cols)) return MXFP8_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return MXFP8_OK;
   const bool row = d.q_row || d.s_row, col = d.q_col || d.s_col;
@@ -53,7 +60,10 @@ mxfp8_status check_quant(const mxfp8_quant_desc& d) {
     if (!col && d.s_row_pitch != d.cols / MXFP8_BLOCK && !flat_blocks_fit(d.rows, d.cols))
       return MXFP8_ERR_SHAPE;
   }
-  if (col && d.s_col_pitch) {
+  if (col && d.s_col_pitch == MXFP8_COLUMNWISE_T) {
+    // the transposing tiles read 16-byte chunks of a row (no narrow path)
+    if (d.cols % 8) return MXFP8_ERR_SHAPE;
+  } else if (col && d.s_col_pitch) {
     if (d.s_col_pitch < d.cols || !fits(d.rows / MXFP8_BLOCK, d.s_col_pitch)) return MXFP8_ERR_SHAPE;
     // the tiles store 8 scale bytes at a time; rows of other lengths store bytes
     if (d.cols % 8 == 0 && d.s_col_pitch % 8) return MXFP8_ERR_ALIGN;
@@ -223,7 +233,7 @@ QuantItem to_item(const mxfp8_quant_desc& d) {
   const mx::ScaleStride sr = row_scale_stride(d.s_row_pitch, d.rows, wr);
   it.p.s_row = sr.row;
   it.p.s_grp = sr.grp;
-  it.p.s_col = d.s_col_pitch ? d.s_col_pitch : wc;
+  it.p.s_col = d.s_col_pitch > 0 ? d.s_col_pitch : wc;   // unused by the transposing tiles
   it.pitched = (d.s_row && !compact(sr, wr)) || (d.s_col && it.p.s_col != wc);
   return it;
 }
@@ -274,15 +284,21 @@ mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc* descs, int32_t n, vo
   if (n < 0) return MXFP8_ERR_ARG;
   if (n == 0) return MXFP8_OK;
   if (!descs) return MXFP8_ERR_NULL;
-  std::vector<QuantItem> v;
+  // tensors whose columnwise plane is stored transposed go to their own tiles
+  std::vector<QuantItem> v, vt;
   v.reserve(n);
   for (int32_t i = 0; i < n; ++i) {
     if (mxfp8_status st = check_quant(descs[i])) return st;
-    v.push_back(to_item(descs[i]));
+    (col_t(descs[i]) ? vt : v).push_back(to_item(descs[i]));
   }
+  for (const QuantItem& it : vt)   // before any launch
+    if (mx::quant_colt_tasks(it.d) > kMaxTasksPerLaunch) return MXFP8_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mxfp8_status st = run_items<mx::QuantArgs, mx::QuantArgsPitched>(
+          v, mx::quant_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize(args, t, s); }))
+    return st;
   return run_items<mx::QuantArgs, mx::QuantArgsPitched>(
-      v, mx::quant_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize(args, t, s); });
+      vt, mx::quant_colt_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize_colt(args, t, s); });
 }
 
 mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc* descs, int32_t n,
@@ -293,6 +309,7 @@ mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc* descs, int32_t n
   std::vector<QuantItem> v;
   v.reserve(n);
   for (int32_t i = 0; i < n; ++i) {
+    if (descs[i].s_col_pitch == MXFP8_COLUMNWISE_T) return MXFP8_ERR_SHAPE;   // bf16 input only
     if (mxfp8_status st = check_quant(descs[i])) return st;
     v.push_back(to_item(descs[i]));
   }

@@ -232,6 +232,18 @@ __device__ __forceinline__ u32x2 encode_col_quad(uint32_t wr_a, uint32_t wr1_a,
   return u32x2{__builtin_amdgcn_perm(ub, ua, 0x06040200u), __builtin_amdgcn_perm(ub, ua, 0x07050301u)};
 }
 
+// e4m3 bytes of rows r (wr) and r+1 (wr1) of the two columns of pair-dword j,
+// in column order: (r, 2j), (r+1, 2j), (r, 2j+1), (r+1, 2j+1).
+__device__ __forceinline__ uint32_t encode_col_pair(uint32_t wr, uint32_t wr1, const ColPair& pc) {
+  const uint32_t c0 = clamp_mag(wr, pc.lim), c1 = clamp_mag(wr1, pc.lim);
+  const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x05040100u);
+  v2i16 d = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      __builtin_bit_cast(v2i16, lo), __builtin_bit_cast(v2bf16, lo), pc.div_lo, false);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+      d, __builtin_bit_cast(v2bf16, __builtin_amdgcn_perm(c1, c0, 0x07060302u)), pc.div_hi, true);
+  return __builtin_bit_cast(uint32_t, d);
+}
+
 // ---- decode ----------------------------------------------------------------
 
 // Exact float32 value of e4m3 byte b times 2^(S - 127); NaN for element

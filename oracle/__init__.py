@@ -125,6 +125,14 @@ class Oracle:
         getattr(self.lib, "mxfp8_oracle_quantize_colwise" + sfx)(_ptr(x), rows, cols, _ptr(q), _ptr(s))
         return q, s
 
+    def quantize_colwise_t(self, x):
+        """The columnwise plane stored transposed (the library's
+        MXFP8_COLUMNWISE_T layout): q_t [cols, rows] with q_t[c, r] = q[r, c]
+        and s_t [cols, rows/32] with s_t[c, b] = s[b, c], for (q, s) the
+        columnwise plane above."""
+        q, s = self.quantize_colwise(x)
+        return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
+
     def dequantize(self, q, s, axis: int):
         """Exact float64 values of a plane; axis 0 = rowwise scales, 1 = columnwise."""
         q = np.ascontiguousarray(q, np.uint8)

@@ -314,6 +314,17 @@ def check_col_is_row_of_transpose(orc, xs):
         assert (qc == qr.T).all() and (sc == sr.T).all(), "columnwise != rowwise(x^T)^T"
 
 
+def check_col_t_is_row_of_transpose(orc, xs):
+    """The transposed columnwise plane is, byte for byte and shape for shape,
+    the rowwise plane of x^T: a plane left untransposed, or scales indexed
+    the other way, fails (the tensors are not square)."""
+    for x in xs:
+        qt, st = orc.quantize_colwise_t(x)
+        qr, sr = orc.quantize_rowwise(np.ascontiguousarray(x.T))
+        assert qt.shape == qr.shape and st.shape == sr.shape, "transposed plane shapes"
+        assert (qt == qr).all() and (st == sr).all(), "transposed columnwise != rowwise(x^T)"
+
+
 def check_row_col_agree(orc, xs):
     for x in xs:
         vals = bf16_values(x)

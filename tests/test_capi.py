@@ -41,7 +41,7 @@ def test_every_declared_function_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.mxfp8_abi_version() == 3
+    assert L.mxfp8_abi_version() == 4
     for code in range(7):
         assert L.mxfp8_status_string(code)
     assert b"unknown" in L.mxfp8_status_string(99)
@@ -153,6 +153,27 @@ def test_scale_pitch_checks(L):
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 72 + 4)), 1, 0, None) == ERR_ALIGN
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 32)), 1, 0, None) == ERR_SHAPE
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 1 << 20, 64, 0, C, 1 << 60)), 1, 0, None) == ERR_SHAPE
+
+
+def test_transposed_columnwise_checks(L):
+    """Columnwise pitch MXFP8_COLUMNWISE_T (-2): bf16 quantize only, rows % 32
+    and cols % 8; every descriptor of a mixed list is checked, and every
+    tensor's task count too, before the first launch.  Only rejected calls
+    are made here (no GPU)."""
+    Q, T = mx._QuantDesc, -2
+    def quant(*ds):
+        return L.mxfp8_quantize_grouped((Q * len(ds))(*[Q(*d) for d in ds]), len(ds), None)
+    assert quant((A, 32, 12, None, None, B, C, 0, T)) == ERR_SHAPE       # cols % 8
+    assert quant((A, 48, 64, None, None, B, C, 0, T)) == ERR_SHAPE       # rows % 32
+    assert quant((A, 32, 48, D, A, B, C, 0, T)) == ERR_SHAPE             # rowwise plane: cols % 32
+    assert quant((A, 32, 64, None, None, B, C, 0, -3)) == ERR_SHAPE      # no other sentinel
+    assert quant((A, 32, 64, None, None, B, MIS, 0, T)) == ERR_ALIGN
+    assert quant((A, 32, 64, None, None, B, None, 0, T)) == ERR_NULL
+    # more tasks than one launch carries: refused before the valid first
+    # tensor is launched (a launch would fail here with ERR_HIP)
+    assert quant((A, 32, 64, B, C, None, None, 0, 0),
+                 (A, 1 << 24, 1 << 23, None, None, B, C, 0, T)) == ERR_SHAPE
+    assert L.mxfp8_quantize_f32_grouped((Q * 1)(Q(A, 32, 64, None, None, B, C, 0, T)), 1, None) == ERR_SHAPE
 
 
 def test_mfma_scale_order_checks(L):

@@ -68,6 +68,10 @@ def test_columnwise_is_rowwise_of_transpose(orc, xs):
     P.check_col_is_row_of_transpose(orc, xs)
 
 
+def test_transposed_columnwise_is_rowwise_of_transpose(orc, xs):
+    P.check_col_t_is_row_of_transpose(orc, xs)
+
+
 def test_row_and_column_planes_agree(orc, xs):
     P.check_row_col_agree(orc, xs)
 
