@@ -96,10 +96,10 @@ hipError_t launch_quantize_f32(const QuantArgsPitched& a, int64_t total_tasks, h
 
 // Transposed columnwise plane (a quantize descriptor whose columnwise scale
 // pitch is MXFP8_COLUMNWISE_T): q_col [cols, rows], s_col [cols, rows/32],
-// written from 128 x 128 tiles (rows % 32 == 0, cols % 8 == 0); the rowwise
+// written from 128 x 256 tiles (rows % 32 == 0, cols % 8 == 0); the rowwise
 // plane, when requested, as usual.  Workgroup tasks: one per tile.
 constexpr int kTRows = 128;          // rows of a transposing tile (4 waves x one 32-row block)
-constexpr int kTCols = 128;          // columns of a transposing tile (16 lanes x 8)
+constexpr int kTCols = 256;          // columns of a transposing tile (32 lanes x 8)
 int64_t quant_colt_tasks(const QuantDesc& d);
 hipError_t launch_quantize_colt(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
 hipError_t launch_quantize_colt(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s);

@@ -8,19 +8,21 @@
 // include/mxfp8.h, "Transposed columnwise plane").  The bytes are those of
 // the untransposed plane: the same block rule and the same encode.
 //
-// A workgroup owns a 128 x 128 tile, read from HBM once for both planes.
+// A workgroup owns a 128 x 256 tile, read from HBM once for both planes.
 // Wave w takes rows 32 w .. 32 w + 31 of the tile (one columnwise block) and
-// all 128 columns; lane l holds the 8 columns 8 (l % 16) .. of rows
-// 8 (l / 16) .. 8 (l / 16) + 7 of the wave's block, one 16-byte load per row
-// (each load instruction reads 4 rows x 256 contiguous bytes).
+// all 256 columns; lane l holds the 8 columns 8 (l % 32) .. of rows
+// 16 (l / 32) .. 16 (l / 32) + 15 of the wave's block, one 16-byte load per
+// row (each load instruction reads 2 rows x 512 contiguous bytes).
 //   rowwise    a block is a lane quad (DPP), as in the other tile kernels;
-//   columnwise a block is the 4 lanes l, l ^ 16, l ^ 32, l ^ 48: each lane
-//              reduces its 8 rows in registers, then two lane exchanges.
-// The encoded column bytes go through a 16 KiB transposed tile in LDS
-// (column-major, 128 bytes per column), so that each lane then stores 16
-// bytes of one output row and each store instruction writes 8 whole 128-byte
-// lines of q_col.  The tile's column scale bytes meet in LDS as well: 4 bytes
-// per column, one 4-byte store each.
+//   columnwise a block is the lane pair l, l ^ 32: each lane reduces its 16
+//              rows in registers, then one lane exchange.
+// The encoded column bytes go through a 32 KiB transposed tile in LDS
+// (column-major, 128 bytes per column; each lane writes its 16 rows of a
+// column as one 16-byte chunk), so that each lane then stores 16 bytes of
+// one output row and each store instruction writes 8 whole 128-byte lines of
+// q_col.  The scale bytes meet in LDS as well and leave as one 4-byte store
+// per column (its 4 row blocks) and one 8-byte store per row (its 8 column
+// blocks).
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -30,72 +32,82 @@ namespace {
 
 constexpr int kTRowsPerWave = kTRows / kWavesPerGroup;   // one 32-row column block
 constexpr int kTLaneCols = 8;                             // columns a lane holds
-constexpr int kTLaneRows = 8;                             // rows a lane holds
-static_assert(kTCols == 16 * kTLaneCols && kTRowsPerWave == 4 * kTLaneRows && kTRowsPerWave == kBlock,
+constexpr int kTLaneRows = 16;                            // rows a lane holds
+constexpr int kTColLanes = kTCols / kTLaneCols;           // lanes across the tile's columns
+static_assert(kTColLanes == 32 && kTRowsPerWave == 2 * kTLaneRows && kTRowsPerWave == kBlock,
               "lane grid of the transposing tile");
+constexpr int kTRowBlocks = kTCols / kBlock;              // rowwise blocks per tile row (8)
+constexpr int kTColBlocks = kTRows / kBlock;              // columnwise blocks per tile column (4)
 
 // Byte offset of 16-byte chunk k (rows 16 k .. 16 k + 15) of tile column cl in
 // the transposed tile: 128-byte columns whose chunks are XOR-swizzled by the
-// column's lane (cl / 8), so that the 16 lanes that write one column index
-// at a time fall on 8 different chunk positions.
+// column's lane (cl / 8), so that the lanes that write one column index at a
+// time fall on 8 different chunk positions.
 __device__ __forceinline__ int colt_at(int cl, int k) {
   return cl * kTRows + ((k ^ ((cl >> 3) & 7)) << 4);
 }
 
+// LDS of a workgroup: the transposed tile, then the column scale bytes
+// (4 per column, one per wave) and the row scale bytes (8 per row).
+struct ColtLds {
+  uint8_t tile[kTCols * kTRows];
+  uint32_t scol[kTCols];
+  u32x2 srow[kTRows];
+};
+
 // ROW: the rowwise plane is requested too (then cols % 32 == 0).
 template <bool ROW>
 __device__ void quant_colt_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid,
-                                int wave, uint8_t* tl, uint32_t* ssc) {
+                                int wave, ColtLds& lds) {
   const int lane = tid & (kWave - 1);
   const int64_t rows = d.rows, cols = d.cols;
   const int64_t col_tiles = (cols + kTCols - 1) / kTCols;
   const int64_t r0 = (task / col_tiles) * kTRows, c0 = (task % col_tiles) * kTCols;
-  const int cc = lane & 15, rg = lane >> 4;
-  // rows % 32 == 0: a wave's block lies wholly inside the tensor or wholly
-  // past its end (the last tile of a tensor whose rows are not a multiple of
-  // 128); cols % 8 == 0: so does a lane's chunk
-  const bool wave_on = r0 + kTRowsPerWave * wave < rows;
-  const int64_t c = c0 + kTLaneCols * cc;
-  const bool ok = wave_on && c < cols;
+  const int cc = lane & (kTColLanes - 1), rg = lane / kTColLanes;
   const int ro = kTRowsPerWave * wave + kTLaneRows * rg;   // the lane's first row in the tile
-  // Loads are never skipped (a skipped load behind a branch makes the
-  // compiler wait on every load before each store): a lane outside the
-  // tensor reads rows 0..7 of its first 8 columns (rows >= 32) and stores
-  // nothing.  Its columns are its own, so its values reach no block of the
-  // tensor; a rowwise quad lies wholly outside with it (cols % 32 == 0).
-  const uint16_t* xp = d.x + (ok ? (r0 + ro) * cols + c : 0);
+  // No load or store before the tile's final stores sits behind a branch
+  // (the compiler cannot know whether a store inside an `if` was issued, as
+  // stores count in vmcnt, so it would wait on more loads and hold more
+  // registers).  Lanes outside the tensor work on a mirror instead:
+  //   rows % 32 == 0, so a wave's block lies wholly inside the tensor or
+  //   wholly past its end (in the last tile of a tensor whose rows are not a
+  //   multiple of 128); a wave past the end takes the tensor's last block;
+  //   cols % 8 == 0, so a lane's chunk lies wholly inside or past the end; a
+  //   lane past the end takes columns (l % 4) * 8 of its rows.  With the
+  //   rowwise plane (cols % 32 == 0) its quad then covers columns 0..31 of
+  //   those rows exactly and rewrites the very bytes their owners write;
+  //   without it, its rows hold at least 8 columns.
+  // A mirror's columnwise results land in LDS rows or columns past the
+  // tensor, which the final stores skip.
+  const int64_t c = c0 + kTLaneCols * cc;
+  const int64_t ce = c < cols ? c : (ROW ? (int64_t)(lane & 3) * kTLaneCols : 0);
+  const int64_t rbase = r0 + ro < rows ? r0 + ro : rows - kTRowsPerWave + kTLaneRows * rg;
+  const uint16_t* xp = d.x + rbase * cols + ce;
   u32x4 v[kTLaneRows];
 #pragma unroll
   for (int r = 0; r < kTLaneRows; ++r) v[r] = load16(xp + r * cols);
 
   if constexpr (ROW) {
+    uint8_t* srow8 = reinterpret_cast<uint8_t*>(lds.srow);
 #pragma unroll
     for (int r = 0; r < kTLaneRows; ++r) {
       const RowScale rs = row_scale_key(quad_max(chunk_key(v[r])));
-      const u32x2 q = encode_chunk_row(v[r], rs);
-      if (ok) {
-        const int64_t row = r0 + ro + r;
-        store8(d.q_row + row * cols + c, q);
-        if ((cc & 3) == 0)
-          store_scale<false>(d.s_row + scale_at(row, c >> 5, pitch.s_row, pitch.s_grp), rs.sbyte);
-      }
+      store8(d.q_row + (rbase + r) * cols + ce, encode_chunk_row(v[r], rs));
+      if ((cc & 3) == 0) srow8[(ro + r) * kTRowBlocks + (cc >> 2)] = (uint8_t)rs.sbyte;
     }
   }
 
-  // column maxima: the lane's 8 rows, then the other 3 lanes of the block
+  // column maxima: the lane's 16 rows, then the other lane of the block
   u32x4 m = kZero4;
 #pragma unroll
   for (int r = 0; r < kTLaneRows; ++r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) m[j] = pk_max_u16(m[j], mag2(v[r][j]));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    m[j] = pk_max_u16(m[j], (uint32_t)__shfl_xor((int)m[j], 16));
-    m[j] = pk_max_u16(m[j], (uint32_t)__shfl_xor((int)m[j], 32));
-  }
+  for (int j = 0; j < 4; ++j) m[j] = pk_max_u16(m[j], (uint32_t)__shfl_xor((int)m[j], kTColLanes));
 
-  if (wave_on) {
-    uint8_t* ssc8 = reinterpret_cast<uint8_t*>(ssc);
+  {
+    uint8_t* scol8 = reinterpret_cast<uint8_t*>(lds.scol);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const ColPair cp = col_pair(m[j]);
@@ -104,17 +116,19 @@ __device__ void quant_colt_task(const QuantDesc& d, const QuantPitch& pitch, int
       uint32_t da[kTLaneRows / 2];
 #pragma unroll
       for (int p = 0; p < kTLaneRows / 2; ++p) da[p] = encode_col_pair(v[2 * p][j], v[2 * p + 1][j], cp) | nm;
-      // 8 rows of column 2j (low bytes of each row pair) and of column 2j + 1
-      const u32x2 lo = {__builtin_amdgcn_perm(da[1], da[0], 0x05040100u),
-                        __builtin_amdgcn_perm(da[3], da[2], 0x05040100u)};
-      const u32x2 hi = {__builtin_amdgcn_perm(da[1], da[0], 0x07060302u),
-                        __builtin_amdgcn_perm(da[3], da[2], 0x07060302u)};
+      // 16 rows of column 2j (low bytes of each row pair) and of column 2j + 1
+      u32x4 lo, hi;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        lo[h] = __builtin_amdgcn_perm(da[2 * h + 1], da[2 * h], 0x05040100u);
+        hi[h] = __builtin_amdgcn_perm(da[2 * h + 1], da[2 * h], 0x07060302u);
+      }
       const int cl = kTLaneCols * cc + 2 * j;
-      *reinterpret_cast<u32x2*>(tl + colt_at(cl, ro >> 4) + (ro & 15)) = lo;
-      *reinterpret_cast<u32x2*>(tl + colt_at(cl + 1, ro >> 4) + (ro & 15)) = hi;
+      *reinterpret_cast<u32x4*>(lds.tile + colt_at(cl, ro >> 4)) = lo;
+      *reinterpret_cast<u32x4*>(lds.tile + colt_at(cl + 1, ro >> 4)) = hi;
       if (rg == 0) {
-        ssc8[cl * 4 + wave] = (uint8_t)cp.sbytes;
-        ssc8[(cl + 1) * 4 + wave] = (uint8_t)(cp.sbytes >> 16);
+        scol8[cl * kTColBlocks + wave] = (uint8_t)cp.sbytes;
+        scol8[(cl + 1) * kTColBlocks + wave] = (uint8_t)(cp.sbytes >> 16);
       }
     }
   }
@@ -127,10 +141,12 @@ __device__ void quant_colt_task(const QuantDesc& d, const QuantPitch& pitch, int
   for (int q = 0; q < kTCols * kTRows / 16 / kThreads; ++q) {
     const int id = tid + kThreads * q, cl = id >> 3, k = id & 7;
     if (c0 + cl < cols && 16 * k < trows)
-      store16(d.q_col + (c0 + cl) * rows + r0 + 16 * k, *reinterpret_cast<const u32x4*>(tl + colt_at(cl, k)));
+      store16(d.q_col + (c0 + cl) * rows + r0 + 16 * k, *reinterpret_cast<const u32x4*>(lds.tile + colt_at(cl, k)));
   }
-  if (tid < kTCols && c0 + tid < cols) {
-    const uint32_t w = ssc[tid];
+  // column scales: thread t takes tile column t
+  static_assert(kThreads == kTCols, "one thread per tile column");
+  if (c0 + tid < cols) {
+    const uint32_t w = lds.scol[tid];
     uint8_t* sp = d.s_col + (c0 + tid) * (rows / kBlock) + r0 / kBlock;
     if (rows % kTRows == 0) {
       store4_cached(sp, w);                     // 4-byte aligned: rows / 32 % 4 == 0
@@ -138,12 +154,27 @@ __device__ void quant_colt_task(const QuantDesc& d, const QuantPitch& pitch, int
       for (int b = 0; b < trows / kBlock; ++b) *gstore_ptr<uint8_t>(sp + b) = (uint8_t)(w >> (8 * b));
     }
   }
+  // row scales: thread t < 128 takes tile row t
+  if constexpr (ROW) {
+    if (tid < trows) {
+      const int64_t row = r0 + tid, b0 = c0 / kBlock;
+      const u32x2 w = lds.srow[tid];
+      // 8 blocks in a row of the plane (8-byte aligned: b0 % 8 == 0, and in
+      // the MFMA order b0 % 16 is 0 or 8) when the tile is whole
+      if (pitch.s_row % 8 == 0 && c0 + kTCols <= cols) {
+        *gstore_ptr<u32x2>(d.s_row + scale_at(row, b0, pitch.s_row, pitch.s_grp)) = w;
+      } else {
+        for (int b = 0; b < kTRowBlocks && (b0 + b) * kBlock < cols; ++b)
+          *gstore_ptr<uint8_t>(d.s_row + scale_at(row, b0 + b, pitch.s_row, pitch.s_grp)) =
+              (uint8_t)((b < 4 ? w.x : w.y) >> (8 * (b & 3)));
+      }
+    }
+  }
 }
 
 template <class Args>
 __global__ __launch_bounds__(kThreads) void mxfp8_quantize_colt_kernel(const Args a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tl[kTCols * kTRows];
-  __shared__ uint32_t ssc[kTCols];
+  __shared__ __attribute__((aligned(16))) ColtLds lds;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t task = (int32_t)blockIdx.x;
@@ -152,9 +183,9 @@ __global__ __launch_bounds__(kThreads) void mxfp8_quantize_colt_kernel(const Arg
   const QuantPitch p = a.pitch(i);
   const int64_t local = task - a.task_start[i];
   if (d.q_row != nullptr)
-    quant_colt_task<true>(d, p, local, tid, wave, tl, ssc);
+    quant_colt_task<true>(d, p, local, tid, wave, lds);
   else
-    quant_colt_task<false>(d, p, local, tid, wave, tl, ssc);
+    quant_colt_task<false>(d, p, local, tid, wave, lds);
 }
 
 template <class Args>
