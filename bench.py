@@ -53,6 +53,7 @@ HEADLINE_KERNEL = "mx::mxfp8_quantize_kernel<mx::QuantArgs, false, true, false>/
 # valid only while they are unchanged
 KERNEL_SOURCES = {
     "mx::mxfp8_quantize_kernel": ("mx_device.h", "mx_kernels.h", "quantize.hip"),
+    "mx::mxfp8_quantize_colt_kernel": ("mx_device.h", "mx_kernels.h", "quantize_colt.hip"),
     "mx::mxfp8_quantize_f32_kernel": ("mx_device.h", "mx_kernels.h", "quantize_f32.hip"),
     "mx::mxfp8_rmsnorm_quantize_kernel": ("mx_device.h", "mx_kernels.h", "rmsnorm_quantize.hip"),
     "mx::mxfp8_dequantize_kernel": ("mx_device.h", "mx_kernels.h", "dequantize.hip"),
@@ -321,6 +322,22 @@ def bench_other_rows(torch, mx, synth, steps):
     ms, _ = T.run(lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets]), steps, 5)
     res["rowcol_4096x4096_padded_scales"] = (ms, alg, r * c)
     del xs, outs
+
+    # the columnwise plane stored transposed ([cols, rows], the operand order
+    # of the backward products): the same algorithmic bytes as both planes
+    xs = [x.clone() for _ in range(sets)]
+    outs = [mx.quantize(xi, True, True, columnwise_transposed=True) for xi in xs]
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets], columnwise_transposed=True),
+                  steps, 5)
+    res["rowcol_4096x4096_transposed_columnwise"] = (ms, alg, r * c)
+    del xs, outs
+    ws = synth.workload(HEADLINE, device=dev)["xs"]
+    wr, wc = ws[0].shape
+    outs = mx.quantize_grouped(ws, True, True, columnwise_transposed=True)
+    ms, _ = T.run(lambda i: mx.quantize_grouped(ws, True, True, outs=outs, columnwise_transposed=True),
+                  max(20, steps // 10), 3)
+    res[HEADLINE + "_transposed_columnwise"] = (ms, len(ws) * quant_bytes(wr, wc, True, True), len(ws) * wr * wc)
+    del ws, outs
 
     p = mx.quantize(x, True, True)
     for axis, q, s in ((0, p.rowwise_data, p.rowwise_scale), (1, p.columnwise_data, p.columnwise_scale)):

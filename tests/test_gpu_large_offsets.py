@@ -60,6 +60,22 @@ def test_quantize_bf16(orc):
         del p
 
 
+def test_quantize_bf16_transposed_columnwise(orc):
+    """The columnwise plane stored transposed, [32768, 65600]: its rows'
+    offsets pass 2^31 (and the rowwise plane of the same launch)."""
+    x = big(ROWS, COLS, 1)
+    say("large quantize bf16, transposed columnwise", (ROWS, COLS))
+    p = mx.quantize(x, True, True, columnwise_transposed=True)
+    torch.cuda.synchronize()
+    for r0 in strips(ROWS):
+        bits = synth.bf16_bits(x[r0:r0 + 32])
+        check_planes(orc, bits, p, r0, True, False, "bf16 transposed")
+        qc, sc = orc.quantize_colwise(bits)
+        assert_same(host(p.columnwise_data[:, r0:r0 + 32]), np.ascontiguousarray(qc.T),
+                    "q_colT rows %d.." % r0)
+        assert_same(host(p.columnwise_scale[:, r0 // 32]), sc[0], "s_colT block %d" % (r0 // 32))
+
+
 def test_quantize_f32(orc):
     x = big(ROWS, COLS, 2, torch.float32, 0.02)
     for row, col in ((True, True), (True, False)):
