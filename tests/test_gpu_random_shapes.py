@@ -1,9 +1,10 @@
 """A seeded sweep of random shapes through every route of the library,
 against the oracle: rowwise-only (flat tasks), columnwise-only (tiles, and
 the narrow path for rows of any length) and both planes, bf16 and float32
-input, compact and padded scale planes, grouped lists spanning launches, the
-fused RMSNorm, dequantize on both axes, and the matrix product on each of its
-tilings (within the accumulation bound)."""
+input, compact and padded scale planes, the columnwise plane stored
+transposed, grouped lists spanning launches, the fused RMSNorm, dequantize on
+both axes, and the matrix product on each of its tilings (within the
+accumulation bound)."""
 import numpy as np
 import pytest
 import torch
@@ -83,6 +84,47 @@ def test_random_shapes_and_routes(orc, seed):
             q, s = orc.quantize_colwise(xb)
             assert np.array_equal(p.columnwise_data.cpu().numpy(), q), "columnwise data"
             assert np.array_equal(p.columnwise_scale.cpu().numpy(), s), "columnwise scales"
+        for b, v in bufs:
+            mask = torch.ones_like(b, dtype=torch.bool)
+            mask[:v.shape[0], :v.shape[1]] = False
+            assert bool((b[mask] == 0xA5).all()), "padding written"
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_transposed_columnwise(orc, seed):
+    """The columnwise plane stored transposed, with or without the rowwise
+    plane (compact or in a padded allocation), single and grouped calls."""
+    g = np.random.default_rng(3000 + seed)
+    for case in range(6):
+        n = int(g.integers(1, 4))
+        rw = g.random() < 0.6
+        shapes = [(32 * int(g.integers(1, 20)), (32 if rw else 8) * int(g.integers(1, 300 if rw else 1200)))
+                  for _ in range(n)]
+        padded = rw and g.random() < 0.4
+        say("seed", seed, "case", case, shapes, "row" if rw else "", "transposed col", "padded" if padded else "")
+        xs = [input_tensor(r, c, g, torch.bfloat16) for r, c in shapes]
+        outs, bufs = [], []
+        for r, c in shapes:
+            sr = None
+            if padded:
+                b, sr = mx.padded_scale_plane(r, c, mx.ROWWISE, int(g.integers(1, 5)), int(g.integers(1, 9)),
+                                              device=DEV, fill=0xA5)
+                bufs.append((b, sr))
+            outs.append(mx.MXFP8Planes(None, None, sr, None))
+        if n == 1:
+            planes = [mx.quantize(xs[0], rw, True, out=outs[0], columnwise_transposed=True)]
+        else:
+            planes = mx.quantize_grouped(xs, rw, True, outs=outs, columnwise_transposed=True)
+        torch.cuda.synchronize()
+        for x, p in zip(xs, planes):
+            xb = host_bits(x)
+            q, sc = orc.quantize_colwise_t(xb)
+            assert np.array_equal(p.columnwise_data.cpu().numpy(), q), "transposed columnwise data"
+            assert np.array_equal(p.columnwise_scale.cpu().numpy(), sc), "transposed columnwise scales"
+            if rw:
+                q, sr = orc.quantize_rowwise(xb)
+                assert np.array_equal(p.rowwise_data.cpu().numpy(), q), "rowwise data"
+                assert np.array_equal(p.rowwise_scale.cpu().numpy(), sr), "rowwise scales"
         for b, v in bufs:
             mask = torch.ones_like(b, dtype=torch.bool)
             mask[:v.shape[0], :v.shape[1]] = False
