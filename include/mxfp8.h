@@ -258,9 +258,10 @@ mxfp8_status mxfp8_dequantize(const void *q, const void *s, int64_t rows,
  * mxfp8_gemm (K = rows) or to be dequantized as a rowwise plane of
  * [cols, rows].  Required: rows % 32 == 0 and cols % 8 == 0
  * (MXFP8_ERR_SHAPE otherwise); the rowwise plane, if requested, follows its
- * usual rules, pitches and MFMA order included.  mxfp8_quantize_grouped only
- * (a single tensor is a grouped call with n == 1); mxfp8_quantize_f32_grouped
- * refuses the pitch with MXFP8_ERR_SHAPE.  A grouped list that mixes
+ * usual rules, pitches and MFMA order included.  mxfp8_quantize_grouped and
+ * mxfp8_quantize_f32_grouped (a single tensor is a grouped call with
+ * n == 1; a float32 master weight's transposed plane serves the input
+ * gradient).  A grouped list that mixes
  * transposed and untransposed columnwise planes takes one launch sequence for
  * each kind.
  */

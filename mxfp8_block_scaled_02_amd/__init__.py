@@ -257,8 +257,6 @@ def padded_scale_plane(rows: int, cols: int, axis: int = 0, row_multiple: int = 
 def _quant_desc(x, rowwise, columnwise, out, mfma=False, transposed=False):
     if x.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("x must be bfloat16 or float32, got %s" % x.dtype)
-    if transposed and x.dtype != torch.bfloat16:
-        raise ValueError("the transposed columnwise plane is written from bfloat16 input only")
     x2 = _as2d(x, "x", x.dtype)
     rows, cols = x2.shape
     o = out or MXFP8Planes(None, None, None, None)
@@ -290,7 +288,7 @@ def quantize(x: torch.Tensor, rowwise: bool = True, columnwise: bool = False,
     (Megatron-Core quantization.utils page, quantize_params_to_mxfp8).
     ``scale_order="mfma"`` writes the rowwise scales in the MFMA order
     (cols % 512 == 0), which ``gemm`` and ``dequantize`` accept as they are.
-    ``columnwise_transposed=True`` (bf16 input, cols % 8 == 0) stores the
+    ``columnwise_transposed=True`` (cols % 8 == 0) stores the
     columnwise plane transposed, data [cols, rows] and scales
     [cols, rows/32]: a rowwise plane of x^T, which ``gemm`` takes as an
     operand contracting over the rows of x."""

@@ -306,16 +306,21 @@ mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc* descs, int32_t n
   if (n < 0) return MXFP8_ERR_ARG;
   if (n == 0) return MXFP8_OK;
   if (!descs) return MXFP8_ERR_NULL;
-  std::vector<QuantItem> v;
+  std::vector<QuantItem> v, vt;
   v.reserve(n);
   for (int32_t i = 0; i < n; ++i) {
-    if (descs[i].s_col_pitch == MXFP8_COLUMNWISE_T) return MXFP8_ERR_SHAPE;   // bf16 input only
     if (mxfp8_status st = check_quant(descs[i])) return st;
-    v.push_back(to_item(descs[i]));
+    (col_t(descs[i]) ? vt : v).push_back(to_item(descs[i]));
   }
+  for (const QuantItem& it : vt)   // before any launch
+    if (mx::quant_f32_colt_tasks(it.d) > kMaxTasksPerLaunch) return MXFP8_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mxfp8_status st = run_items<mx::QuantArgs, mx::QuantArgsPitched>(
+          v, mx::quant_f32_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize_f32(args, t, s); }))
+    return st;
   return run_items<mx::QuantArgs, mx::QuantArgsPitched>(
-      v, mx::quant_f32_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize_f32(args, t, s); });
+      vt, mx::quant_f32_colt_tasks,
+      [&](const auto& args, int64_t t) { return mx::launch_quantize_f32_colt(args, t, s); });
 }
 
 mxfp8_status mxfp8_quantize_f32(const void* x, int64_t rows, int64_t cols, void* q_row,

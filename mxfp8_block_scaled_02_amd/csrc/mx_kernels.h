@@ -103,6 +103,10 @@ constexpr int kTCols = 256;          // columns of a transposing tile (32 lanes 
 int64_t quant_colt_tasks(const QuantDesc& d);
 hipError_t launch_quantize_colt(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
 hipError_t launch_quantize_colt(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s);
+// The same for float32 input: 128 x 128 tiles.
+int64_t quant_f32_colt_tasks(const QuantDesc& d);
+hipError_t launch_quantize_f32_colt(const QuantArgs& a, int64_t total_tasks, hipStream_t s);
+hipError_t launch_quantize_f32_colt(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s);
 
 // ---- RMSNorm + rowwise quantize ------------------------------------------
 struct NormDesc {

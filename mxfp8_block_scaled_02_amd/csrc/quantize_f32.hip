@@ -10,6 +10,14 @@
 // request) are 32 rows x 256 columns per workgroup, 8 rows per wave; flat
 // tasks (rowwise only) walk 256 x kFlatUnroll pieces of 4 elements.
 //
+// The columnwise plane stored transposed (q_col [cols, rows], see
+// quantize_colt.hip for the bf16 form) comes from 128 x 128 tiles: wave w
+// takes rows 32 w .. 32 w + 31, lane l holds 4 columns of 16 rows (each load
+// instruction reads 2 rows x 512 contiguous bytes), a rowwise block is 8
+// lanes, a columnwise block the lane pair l, l ^ 32.  Each lane converts its
+// 16 rows of a column into one 16-byte chunk of a column-major tile in LDS,
+// which the workgroup then stores as whole 128-byte lines of q_col.
+//
 // Scaling and rounding use v_cvt_scalef32_pk_fp8_f32 with scale operand
 // 2^(S-127), which divides by the scale and rounds to nearest even; like the
 // bf16 form it turns magnitudes >= 464 into NaN, so every input is first
@@ -247,6 +255,140 @@ __device__ void quant_f32_tile_task(const QuantDesc& d, const QuantPitch& pitch,
   }
 }
 
+// ---- transposed columnwise plane -------------------------------------------
+
+constexpr int kF32TRowsPerWave = kTRows / kWavesPerGroup;   // one 32-row column block
+constexpr int kF32TLaneRows = 16;                            // rows a lane holds
+constexpr int kF32TCols = 32 * kF32Lane;                     // 128: 32 lanes x 4 columns
+static_assert(kF32TRowsPerWave == 2 * kF32TLaneRows && kF32TRowsPerWave == kBlock, "lane grid");
+
+// chunk k (rows 16 k ..) of tile column cl: 128-byte columns, chunks
+// XOR-swizzled by the column's lane (cl / 4)
+__device__ __forceinline__ int f32_colt_at(int cl, int k) {
+  return cl * kTRows + ((k ^ ((cl >> 2) & 7)) << 4);
+}
+
+struct F32ColtLds {
+  uint8_t tile[kF32TCols * kTRows];
+  uint32_t scol[kF32TCols];   // 4 column scale bytes per column (one per wave)
+  uint32_t srow[kTRows];      // 4 row scale bytes per row (one per 32 columns)
+};
+
+// ROW: the rowwise plane is requested too (then cols % 32 == 0).  Lanes and
+// waves outside the tensor work on mirrors, as in the bf16 form: a wave past
+// the end takes the tensor's last block; a lane past the end takes columns
+// (l % 8) * 4 of its rows (ROW: its 8-lane group then covers columns 0..31
+// exactly and rewrites its owners' bytes) or 0..3 (columnwise only, cols % 8
+// == 0).  Their columnwise results land in LDS rows or columns past the
+// tensor, which the final stores skip.
+template <bool ROW>
+__device__ void quant_f32_colt_task(const QuantDesc& d, const QuantPitch& pitch, int64_t task, int tid, int wave,
+                                    F32ColtLds& lds) {
+  const float* x = reinterpret_cast<const float*>(d.x);
+  const int lane = tid & (kWave - 1);
+  const int64_t rows = d.rows, cols = d.cols;
+  const int64_t col_tiles = (cols + kF32TCols - 1) / kF32TCols;
+  const int64_t r0 = (task / col_tiles) * kTRows, c0 = (task % col_tiles) * kF32TCols;
+  const int cc = lane & 31, rg = lane >> 5;
+  const int ro = kF32TRowsPerWave * wave + kF32TLaneRows * rg;   // the lane's first row in the tile
+  const int64_t c = c0 + kF32Lane * cc;
+  const int64_t ce = c < cols ? c : (ROW ? (int64_t)(lane & 7) * kF32Lane : 0);
+  const int64_t rbase = r0 + ro < rows ? r0 + ro : rows - kF32TRowsPerWave + kF32TLaneRows * rg;
+  const float* xp = x + rbase * cols + ce;
+  u32x4 v[kF32TLaneRows];
+#pragma unroll
+  for (int r = 0; r < kF32TLaneRows; ++r) v[r] = load16(xp + r * cols);
+
+  if constexpr (ROW) {
+    uint8_t* srow8 = reinterpret_cast<uint8_t*>(lds.srow);
+#pragma unroll
+    for (int r = 0; r < kF32TLaneRows; ++r) {
+      const F32Scale sc = f32_scale_key(oct_max(f32_key4(v[r])));
+      store4(d.q_row + (rbase + r) * cols + ce, encode4_row(v[r], sc));
+      if ((cc & 7) == 0) srow8[(ro + r) * 4 + (cc >> 3)] = (uint8_t)sc.sbyte;
+    }
+  }
+
+  // column maxima: the lane's 16 rows, then the other lane of the block
+  u32x4 m = kZero4;
+#pragma unroll
+  for (int r = 0; r < kF32TLaneRows; ++r) m = __builtin_elementwise_max(m, v[r] & 0x7FFFFFFFu);
+#pragma unroll
+  for (int k = 0; k < kF32Lane; ++k) m[k] = max(m[k], (uint32_t)__shfl_xor((int)m[k], 32));
+
+  uint8_t* scol8 = reinterpret_cast<uint8_t*>(lds.scol);
+#pragma unroll
+  for (int k = 0; k < kF32Lane; ++k) {
+    const F32Scale sc = f32_scale_key(m[k]);
+    // a NaN/Inf column keeps only each element's sign bit; its bytes become sign | 0x7F
+    const uint32_t keep = sc.nan ? 0x80000000u : 0xFFFFFFFFu, nanq = sc.nan ? 0x7F7F7F7Fu : 0u;
+    u32x4 col;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t a0 = v[4 * h][k] & keep, a1 = v[4 * h + 1][k] & keep;
+      const uint32_t a2 = v[4 * h + 2][k] & keep, a3 = v[4 * h + 3][k] & keep;
+      v2i16 t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2i16, a0), med(a0, sc.lim),
+                                                         med(a1, sc.lim), sc.div, false);
+      t = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(t, med(a2, sc.lim), med(a3, sc.lim), sc.div, true);
+      col[h] = __builtin_bit_cast(uint32_t, t) | nanq;   // rows 4h .. 4h + 3 of the column
+    }
+    const int cl = kF32Lane * cc + k;
+    *reinterpret_cast<u32x4*>(lds.tile + f32_colt_at(cl, ro >> 4)) = col;
+    if (rg == 0) scol8[cl * 4 + wave] = (uint8_t)sc.sbyte;
+  }
+  __syncthreads();
+
+  const int64_t trows = rows - r0 < kTRows ? rows - r0 : kTRows;   // 32, 64, 96 or 128
+#pragma unroll
+  for (int q = 0; q < kF32TCols * kTRows / 16 / kThreads; ++q) {
+    const int id = tid + kThreads * q, cl = id >> 3, k = id & 7;
+    if (c0 + cl < cols && 16 * k < trows)
+      store16(d.q_col + (c0 + cl) * rows + r0 + 16 * k, *reinterpret_cast<const u32x4*>(lds.tile + f32_colt_at(cl, k)));
+  }
+  if (tid < kF32TCols) {
+    // column scales: thread t takes tile column t (4 row blocks)
+    if (c0 + tid < cols) {
+      const uint32_t w = lds.scol[tid];
+      uint8_t* sp = d.s_col + (c0 + tid) * (rows / kBlock) + r0 / kBlock;
+      if (rows % kTRows == 0) {
+        store4_cached(sp, w);                   // 4-byte aligned: rows / 32 % 4 == 0
+      } else {
+        for (int b = 0; b < trows / kBlock; ++b) *gstore_ptr<uint8_t>(sp + b) = (uint8_t)(w >> (8 * b));
+      }
+    }
+  } else if (ROW) {
+    // row scales: thread 128 + t takes tile row t (4 column blocks; 4-byte
+    // aligned where the tile is whole: b0 % 4 == 0, also in the MFMA order)
+    const int t = tid - kF32TCols;
+    if (t < trows) {
+      const int64_t row = r0 + t, b0 = c0 / kBlock;
+      const uint32_t w = lds.srow[t];
+      if (pitch.s_row % 4 == 0 && c0 + kF32TCols <= cols) {
+        store4_cached(d.s_row + scale_at(row, b0, pitch.s_row, pitch.s_grp), w);
+      } else {
+        for (int b = 0; b < 4 && (b0 + b) * kBlock < cols; ++b)
+          *gstore_ptr<uint8_t>(d.s_row + scale_at(row, b0 + b, pitch.s_row, pitch.s_grp)) = (uint8_t)(w >> (8 * b));
+      }
+    }
+  }
+}
+
+template <class Args>
+__global__ __launch_bounds__(kThreads) void mxfp8_quantize_f32_colt_kernel(const Args a) {
+  __shared__ __attribute__((aligned(16))) F32ColtLds lds;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t task = (int32_t)blockIdx.x;
+  const int i = a.n == 1 ? 0 : find_desc(a.task_start, a.n, task);
+  const QuantDesc d = a.d[i];
+  const QuantPitch p = a.pitch(i);
+  const int64_t local = task - a.task_start[i];
+  if (d.q_row != nullptr)
+    quant_f32_colt_task<true>(d, p, local, tid, wave, lds);
+  else
+    quant_f32_colt_task<false>(d, p, local, tid, wave, lds);
+}
+
 // ROWCOL: every tensor of the launch requests both planes (the launcher
 // checks), so only that tile path is compiled in.  Compiled together, the two
 // tile paths share their loads and columnwise part and need 79 VGPRs against
@@ -327,6 +469,27 @@ hipError_t launch_f32(const Args& a, int64_t total_tasks, hipStream_t s) {
 
 hipError_t launch_quantize_f32(const QuantArgs& a, int64_t total_tasks, hipStream_t s) {
   return launch_f32(a, total_tasks, s);
+}
+
+int64_t quant_f32_colt_tasks(const QuantDesc& d) {
+  if (d.rows == 0 || d.cols == 0) return 0;
+  return ((d.rows + kTRows - 1) / kTRows) * ((d.cols + kF32TCols - 1) / kF32TCols);
+}
+
+template <class Args>
+hipError_t launch_f32_colt(const Args& a, int64_t total_tasks, hipStream_t s) {
+  if (total_tasks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((mxfp8_quantize_f32_colt_kernel<Args>), dim3((uint32_t)total_tasks), dim3(kThreads), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_f32_colt(const QuantArgs& a, int64_t total_tasks, hipStream_t s) {
+  return launch_f32_colt(a, total_tasks, s);
+}
+
+hipError_t launch_quantize_f32_colt(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s) {
+  return launch_f32_colt(a, total_tasks, s);
 }
 
 hipError_t launch_quantize_f32(const QuantArgsPitched& a, int64_t total_tasks, hipStream_t s) {

@@ -156,8 +156,8 @@ def test_scale_pitch_checks(L):
 
 
 def test_transposed_columnwise_checks(L):
-    """Columnwise pitch MXFP8_COLUMNWISE_T (-2): bf16 quantize only, rows % 32
-    and cols % 8; every descriptor of a mixed list is checked, and every
+    """Columnwise pitch MXFP8_COLUMNWISE_T (-2): rows % 32 and cols % 8, for
+    bf16 and float32 input; every descriptor of a mixed list is checked, and every
     tensor's task count too, before the first launch.  Only rejected calls
     are made here (no GPU)."""
     Q, T = mx._QuantDesc, -2
@@ -173,7 +173,10 @@ def test_transposed_columnwise_checks(L):
     # tensor is launched (a launch would fail here with ERR_HIP)
     assert quant((A, 32, 64, B, C, None, None, 0, 0),
                  (A, 1 << 24, 1 << 23, None, None, B, C, 0, T)) == ERR_SHAPE
-    assert L.mxfp8_quantize_f32_grouped((Q * 1)(Q(A, 32, 64, None, None, B, C, 0, T)), 1, None) == ERR_SHAPE
+    f32 = lambda *ds: L.mxfp8_quantize_f32_grouped((Q * len(ds))(*[Q(*d) for d in ds]), len(ds), None)
+    assert f32((A, 32, 12, None, None, B, C, 0, T)) == ERR_SHAPE
+    assert f32((A, 32, 64, B, C, None, None, 0, 0),
+               (A, 1 << 24, 1 << 22, None, None, B, C, 0, T)) == ERR_SHAPE
 
 
 def test_mfma_scale_order_checks(L):

@@ -12,7 +12,7 @@ import torch
 import mxfp8_block_scaled_02_amd as mx
 from mxfp8_block_scaled_02_amd import synth
 from tests import gemm_accuracy as acc
-from tests.test_gpu_parity import DEV, assert_same, dev_bits, host, say, special_values
+from tests.test_gpu_parity import DEV, assert_same, dev_bits, dev_f32, f32_specials, host, say, special_values
 
 pytestmark = pytest.mark.gpu
 
@@ -28,8 +28,10 @@ def mfma_to_compact(s, rows, cols):
 
 
 def check(orc, bits, rowwise, what, scale_order="row", out=None):
-    say("transposed columnwise", what, bits.shape, "row" if rowwise else "", scale_order)
-    p = mx.quantize(dev_bits(bits), rowwise, True, out=out, scale_order=scale_order, columnwise_transposed=True)
+    """bits: bf16 bit patterns (uint16) or float32 values."""
+    say("transposed columnwise", what, bits.shape, bits.dtype, "row" if rowwise else "", scale_order)
+    x = dev_bits(bits) if bits.dtype == np.uint16 else dev_f32(bits)
+    p = mx.quantize(x, rowwise, True, out=out, scale_order=scale_order, columnwise_transposed=True)
     torch.cuda.synchronize()
     rows, cols = bits.shape
     qt, st = orc.quantize_colwise_t(bits)
@@ -133,10 +135,65 @@ def test_grouped_experts_equal_single_calls():
             assert torch.equal(a, b)
 
 
-def test_float32_input_refused():
-    x = torch.zeros((32, 64), dtype=torch.float32, device=DEV)
-    with pytest.raises(ValueError):
-        mx.quantize(x, True, True, columnwise_transposed=True)
+# float32 input: 128 x 128 tiles, so columns 8 .. 120 past a multiple of 128
+F32_SHAPES = [(32, 8), (32, 32), (128, 128), (96, 136), (160, 264), (256, 1024), (1024, 40), (352, 1184)]
+
+
+@pytest.mark.parametrize("shape", F32_SHAPES)
+def test_transposed_columnwise_f32(orc, shape):
+    """float32 input with specials (NaN, Inf, subnormals, the largest
+    finite values) spread over 60 binades."""
+    rows, cols = shape
+    x = f32_specials(rows, cols, seed=rows + 3 * cols)
+    check(orc, x, False, "f32 columnwise only")
+    if cols % 32 == 0:
+        check(orc, x, True, "f32 rowwise + columnwise")
+
+
+def test_f32_master_weight_4096(orc):
+    """The 4096 x 4096 float32 master weight (outliers, zero and subnormal
+    tiles), both planes, and its rowwise scales in the MFMA order."""
+    x = synth.master_weight_f32().numpy()
+    check(orc, x, True, "f32 master weight")
+    check(orc, x, True, "f32 master weight, mfma rowwise scales", scale_order="mfma")
+
+
+def test_f32_grouped_equals_single_calls():
+    g = torch.Generator().manual_seed(44)
+    xs = [(torch.randn(s, generator=g) * 0.02).to(DEV) for s in ((256, 7168), (96, 520), (2048, 64), (32, 8))]
+    say("f32 grouped transposed", [tuple(x.shape) for x in xs])
+    for rw in (True, False):
+        use = [x for x in xs if not rw or x.shape[1] % 32 == 0]
+        got = mx.quantize_grouped(use, rw, True, columnwise_transposed=True)
+        for x, p in zip(use, got):
+            single = mx.quantize(x, rw, True, columnwise_transposed=True)
+            torch.cuda.synchronize()
+            for a, b in zip(p, single):
+                if a is not None:
+                    assert torch.equal(a, b)
+
+
+def test_input_gradient_from_f32_master_weight(orc):
+    """dx = dy . w with w's transposed columnwise plane quantized from its
+    float32 master copy, against the float64 product of the untransposed
+    planes."""
+    T, N, K = 256, 512, 768
+    g = torch.Generator().manual_seed(55)
+    w = torch.randn(N, K, generator=g) * 0.05
+    dy = (torch.randn(T, N, generator=g) * 0.01).to(torch.bfloat16)
+    say("input gradient from a float32 master weight", (T, N, K))
+    pw = mx.quantize(w.to(DEV), False, True, columnwise_transposed=True)
+    pdy = mx.quantize(dy.to(DEV), True, False)
+    dx = mx.gemm(pdy.rowwise_data, pdy.rowwise_scale, pw.columnwise_data, pw.columnwise_scale, torch.float32)
+    torch.cuda.synchronize()
+    qc, sc = orc.quantize_colwise(w.numpy())
+    q, s = orc.quantize_rowwise(synth.bf16_bits(dy))
+    ref = orc.dequantize(q, s, 0) @ orc.dequantize(qc, sc, 1)
+    hp = [host(t) for t in (pdy.rowwise_data, pdy.rowwise_scale, pw.columnwise_data, pw.columnwise_scale)]
+    C, mag = orc.gemm(*hp)
+    assert (np.abs(C - ref) <= 1e-12 * mag).all(), "the planes do not hold w^T"
+    err = np.abs(host(dx).astype(np.float64) - C)
+    assert (err <= acc.bound(*hp)).all()
 
 
 # the products take the skinny row blocks and, for the input gradient of

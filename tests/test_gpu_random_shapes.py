@@ -101,8 +101,10 @@ def test_random_transposed_columnwise(orc, seed):
         shapes = [(32 * int(g.integers(1, 20)), (32 if rw else 8) * int(g.integers(1, 300 if rw else 1200)))
                   for _ in range(n)]
         padded = rw and g.random() < 0.4
-        say("seed", seed, "case", case, shapes, "row" if rw else "", "transposed col", "padded" if padded else "")
-        xs = [input_tensor(r, c, g, torch.bfloat16) for r, c in shapes]
+        dtype = torch.bfloat16 if g.random() < 0.6 else torch.float32
+        say("seed", seed, "case", case, shapes, dtype, "row" if rw else "", "transposed col",
+            "padded" if padded else "")
+        xs = [input_tensor(r, c, g, dtype) for r, c in shapes]
         outs, bufs = [], []
         for r, c in shapes:
             sr = None
