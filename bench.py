@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "mx::mxfp8_quantize_kernel": ("mx_device.h", "mx_kernels.h", "quantize.hip"),
     "mx::mxfp8_quantize_colt_kernel": ("mx_device.h", "mx_kernels.h", "quantize_colt.hip"),
     "mx::mxfp8_quantize_f32_kernel": ("mx_device.h", "mx_kernels.h", "quantize_f32.hip"),
+    "mx::mxfp8_quantize_f32_colt_kernel": ("mx_device.h", "mx_kernels.h", "quantize_f32.hip"),
     "mx::mxfp8_rmsnorm_quantize_kernel": ("mx_device.h", "mx_kernels.h", "rmsnorm_quantize.hip"),
     "mx::mxfp8_dequantize_kernel": ("mx_device.h", "mx_kernels.h", "dequantize.hip"),
     "mx::mxfp8_gemm": ("mx_device.h", "mx_kernels.h", "gemm.hip"),
@@ -295,6 +296,10 @@ def bench_other_rows(torch, mx, synth, steps):
     outs = [mx.quantize(xi, True, True) for xi in xs]
     ms, _ = T.run(lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets]), steps, 5)
     res["rowcol_f32_4096x4096"] = (ms, alg, r * c)
+    outs = [mx.quantize(xi, True, True, columnwise_transposed=True) for xi in xs]
+    ms, _ = T.run(lambda i: mx.quantize(xs[i % sets], True, True, out=outs[i % sets], columnwise_transposed=True),
+                  steps, 5)
+    res["rowcol_f32_4096x4096_transposed_columnwise"] = (ms, alg, r * c)
     del xs, outs
 
     # context: a plain device copy moving the 4096 x 4096 weight's volume

@@ -304,7 +304,9 @@ __device__ void quant_f32_colt_task(const QuantDesc& d, const QuantPitch& pitch,
 #pragma unroll
     for (int r = 0; r < kF32TLaneRows; ++r) {
       const F32Scale sc = f32_scale_key(oct_max(f32_key4(v[r])));
-      store4(d.q_row + (rbase + r) * cols + ce, encode4_row(v[r], sc));
+      // written back, as in the 32 x 256 tiles (4096 x 4096: 23.1 against 23.4 us
+      // streamed; 8192 x 7168: 67.1 against 71.9 us)
+      store4_cached(d.q_row + (rbase + r) * cols + ce, encode4_row(v[r], sc));
       if ((cc & 7) == 0) srow8[(ro + r) * 4 + (cc >> 3)] = (uint8_t)sc.sbyte;
     }
   }
