@@ -339,6 +339,15 @@ typedef struct {
     int64_t s_pitch; /* bytes between scale rows; 0: compact */
 } mxfp8_deq_desc;
 
+typedef struct {
+    const void *qa, *sa; /* A rowwise plane [M, K], scales [M, K/32] */
+    const void *qb, *sb; /* B rowwise plane [N, K], scales [N, K/32] */
+    int64_t M, N, K;
+    int64_t sa_pitch, sb_pitch; /* as in mxfp8_gemm */
+    void *out;                  /* [M, N] */
+    int64_t out_pitch;          /* elements between output rows; 0: N */
+} mxfp8_gemm_desc;
+
 mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc *descs, int32_t n,
                                     void *stream);
 /* Grouped mxfp8_quantize_f32: each descriptor's x points to float32. */
@@ -348,6 +357,21 @@ mxfp8_status mxfp8_rmsnorm_quantize_grouped(const mxfp8_norm_desc *descs,
                                             int32_t n, void *stream);
 mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc *descs, int32_t n,
                                       mxfp8_out_dtype out_dtype, void *stream);
+
+/*
+ * mxfp8_gemm_grouped - n independent products out = A . B^T, such as the
+ * experts of an MoE layer, each with its own activation rows, weight,
+ * shape and output (quantization.utils page, resolve_mxfp8_backend: grouped
+ * MoE products take MXFP8 expert weights).  Each descriptor follows
+ * mxfp8_gemm's rules and gives the same result as that call; out_dtype
+ * applies to all.  Products of at most 128 rows (a few tokens per expert)
+ * share launches: every one of them is cut into 32-row blocks of 32 output
+ * columns, so even a list of one-token products fills the GPU; larger
+ * products run as single calls.  Every descriptor is checked before the
+ * first launch; n == 0 is a no-op, n < 0 is MXFP8_ERR_ARG.
+ */
+mxfp8_status mxfp8_gemm_grouped(const mxfp8_gemm_desc *descs, int32_t n,
+                                mxfp8_out_dtype out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "MXFP8Planes", "quantize", "rmsnorm_quantize", "dequantize", "quantize_grouped",
-    "rmsnorm_quantize_grouped", "dequantize_grouped", "gemm", "as_fp8", "library_path", "lib",
+    "rmsnorm_quantize_grouped", "dequantize_grouped", "gemm", "gemm_grouped", "as_fp8", "library_path", "lib",
     "BLOCK", "ROWWISE", "COLUMNWISE", "MFMA_GROUP", "mfma_scale_shape",
 ]
 
@@ -64,6 +64,13 @@ class _NormDesc(ctypes.Structure):
                 ("s_row", ctypes.c_void_p), ("s_row_pitch", ctypes.c_int64)]
 
 
+class _GemmDesc(ctypes.Structure):
+    _fields_ = [("qa", ctypes.c_void_p), ("sa", ctypes.c_void_p), ("qb", ctypes.c_void_p),
+                ("sb", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("sa_pitch", ctypes.c_int64), ("sb_pitch", ctypes.c_int64), ("out", ctypes.c_void_p),
+                ("out_pitch", ctypes.c_int64)]
+
+
 class _DeqDesc(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("axis", ctypes.c_int), ("out", ctypes.c_void_p),
@@ -98,10 +105,11 @@ def lib() -> ctypes.CDLL:
     L.mxfp8_rmsnorm_quantize_grouped.argtypes = [ctypes.POINTER(_NormDesc), i32, p]
     L.mxfp8_gemm.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, i64, ctypes.c_int, p]
     L.mxfp8_dequantize_grouped.argtypes = [ctypes.POINTER(_DeqDesc), i32, ctypes.c_int, p]
+    L.mxfp8_gemm_grouped.argtypes = [ctypes.POINTER(_GemmDesc), i32, ctypes.c_int, p]
     for name in ("mxfp8_quantize", "mxfp8_rmsnorm_quantize", "mxfp8_dequantize",
                  "mxfp8_quantize_grouped", "mxfp8_rmsnorm_quantize_grouped",
                  "mxfp8_dequantize_grouped", "mxfp8_quantize_f32", "mxfp8_quantize_f32_grouped",
-                 "mxfp8_gemm"):
+                 "mxfp8_gemm", "mxfp8_gemm_grouped"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -440,7 +448,42 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
     scale plane may be in the MFMA order ([K/512, rows, 16], K % 512 == 0).
     ``out`` may be a view whose rows lie further apart than N (a column slice
     of a wider matrix); only its [M, N] elements are written."""
-    code = _out_code(dtype)
+    d, o = _gemm_desc(qa, sa, qb, sb, dtype, out)
+    with _on(qa.device):
+        _check(lib().mxfp8_gemm(d.qa, d.sa, d.qb, d.sb, d.M, d.N, d.K, d.sa_pitch, d.sb_pitch, d.out, d.out_pitch,
+                                _out_code(dtype), _stream(qa.device)))
+    return o
+
+
+def gemm_grouped(qas: Sequence[torch.Tensor], sas: Sequence[torch.Tensor], qbs: Sequence[torch.Tensor],
+                 sbs: Sequence[torch.Tensor], dtype: torch.dtype = torch.float32,
+                 outs: Optional[Sequence[Optional[torch.Tensor]]] = None) -> list:
+    """n independent products outs[i] = A_i . B_i^T in as few launches as the
+    library can (MoE experts with a few tokens each share launches); each
+    result equals gemm's for the same operands.  Arguments as for gemm, one
+    per product, all on one device."""
+    n = len(qas)
+    if not (len(sas) == len(qbs) == len(sbs) == n) or (outs is not None and len(outs) != n):
+        raise ValueError("gemm_grouped: one qa, sa, qb, sb (and out) per product")
+    if n == 0:
+        return []
+    dev = qas[0].device
+    descs, res = [], []
+    for i in range(n):
+        if qas[i].device != dev:
+            raise ValueError("gemm_grouped: all products must be on one device")
+        d, o = _gemm_desc(qas[i], sas[i], qbs[i], sbs[i], dtype, outs[i] if outs is not None else None)
+        descs.append(d)
+        res.append(o)
+    arr = (_GemmDesc * n)(*descs)
+    with _on(dev):
+        _check(lib().mxfp8_gemm_grouped(arr, n, _out_code(dtype), _stream(dev)))
+    return res
+
+
+def _gemm_desc(qa, sa, qb, sb, dtype, out):
+    """The C descriptor of one product, and its output tensor."""
+    _out_code(dtype)
     qa2 = _as2d(qa, "qa", torch.uint8)
     qb2 = _as2d(qb, "qb", torch.uint8, device=qa.device)
     M, K = qa2.shape
@@ -461,7 +504,4 @@ def gemm(qa: torch.Tensor, sa: torch.Tensor, qb: torch.Tensor, sb: torch.Tensor,
             raise ValueError("out must be a %s tensor of shape %s on %s with unit column stride and a "
                              "row stride >= %d" % (dtype, (M, N), qa.device, N))
         po = o.stride(0) if M > 1 and o.stride(0) != N else 0
-    with _on(qa.device):
-        _check(lib().mxfp8_gemm(_ptr(qa2), _ptr(sa2), _ptr(qb2), _ptr(sb2), M, N, K, pa, pb, _ptr(o), po, code,
-                                _stream(qa.device)))
-    return o
+    return _GemmDesc(_ptr(qa2), _ptr(sa2), _ptr(qb2), _ptr(sb2), M, N, K, pa, pb, _ptr(o), po), o

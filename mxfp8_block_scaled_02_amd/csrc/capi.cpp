@@ -114,6 +114,43 @@ mxfp8_status check_deq(const mxfp8_deq_desc& d) {
   return MXFP8_OK;
 }
 
+mx::ScaleStride row_scale_stride(int64_t pitch, int64_t rows, int64_t w);
+
+// Checks one product and fills its internal descriptor.
+mxfp8_status check_gemm(const mxfp8_gemm_desc& d, mx::GemmDesc& g) {
+  const int64_t M = d.M, N = d.N, K = d.K;
+  if (M < 0 || N < 0 || K < 0 || !fits(M, K) || !fits(N, K) || !fits(M, N)) return MXFP8_ERR_SHAPE;
+  if (d.out_pitch < 0 || (d.out_pitch && (d.out_pitch < N || !fits(M, d.out_pitch)))) return MXFP8_ERR_SHAPE;
+  if ((d.sa_pitch < 0 && d.sa_pitch != MXFP8_SCALES_MFMA) || (d.sb_pitch < 0 && d.sb_pitch != MXFP8_SCALES_MFMA))
+    return MXFP8_ERR_SHAPE;
+  if (!mfma_order_ok(d.sa_pitch, K) || !mfma_order_ok(d.sb_pitch, K)) return MXFP8_ERR_SHAPE;
+  g = mx::GemmDesc{};
+  g.M = M;
+  g.N = N;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (K == 0 || K % 128) return MXFP8_ERR_SHAPE;
+  if (!d.qa || !d.sa || !d.qb || !d.sb || !d.out) return MXFP8_ERR_NULL;
+  if (misaligned(d.qa) || misaligned(d.sa) || misaligned(d.qb) || misaligned(d.sb) || misaligned(d.out))
+    return MXFP8_ERR_ALIGN;
+  const int64_t kb = K / MXFP8_BLOCK;
+  if (d.sa_pitch > 0 && (d.sa_pitch < kb || !fits(M, d.sa_pitch))) return MXFP8_ERR_SHAPE;
+  if (d.sb_pitch > 0 && (d.sb_pitch < kb || !fits(N, d.sb_pitch))) return MXFP8_ERR_SHAPE;
+  if ((d.sa_pitch > 0 && d.sa_pitch % 4) || (d.sb_pitch > 0 && d.sb_pitch % 4)) return MXFP8_ERR_ALIGN;
+  // 64 x 32 outputs bound the smallest workgroup tile of every route, so this
+  // keeps grid sizes and tile indices within 32 bits
+  if (((M + 63) / 64) * ((N + 31) / 32) > kMaxGemmTiles) return MXFP8_ERR_SHAPE;
+  g.qa = static_cast<const uint8_t*>(d.qa);
+  g.sa = static_cast<const uint8_t*>(d.sa);
+  g.qb = static_cast<const uint8_t*>(d.qb);
+  g.sb = static_cast<const uint8_t*>(d.sb);
+  g.K = K;
+  g.sa_stride = row_scale_stride(d.sa_pitch, M, kb);
+  g.sb_stride = row_scale_stride(d.sb_pitch, N, kb);
+  g.out = d.out;
+  g.out_ld = d.out_pitch ? d.out_pitch : N;
+  return MXFP8_OK;
+}
+
 mxfp8_status hip_status(hipError_t e) { return e == hipSuccess ? MXFP8_OK : MXFP8_ERR_HIP; }
 
 // A tensor of a launch with the pitches of its scale planes.
@@ -390,30 +427,26 @@ mxfp8_status mxfp8_gemm(const void* qa, const void* sa, const void* qb, const vo
                         int64_t M, int64_t N, int64_t K, int64_t sa_pitch, int64_t sb_pitch,
                         void* out, int64_t out_pitch, mxfp8_out_dtype out_dtype, void* stream) {
   if (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16) return MXFP8_ERR_ARG;
-  if (M < 0 || N < 0 || K < 0 || !fits(M, K) || !fits(N, K) || !fits(M, N)) return MXFP8_ERR_SHAPE;
-  if (out_pitch < 0 || (out_pitch && (out_pitch < N || !fits(M, out_pitch)))) return MXFP8_ERR_SHAPE;
-  if ((sa_pitch < 0 && sa_pitch != MXFP8_SCALES_MFMA) || (sb_pitch < 0 && sb_pitch != MXFP8_SCALES_MFMA))
-    return MXFP8_ERR_SHAPE;
-  if (!mfma_order_ok(sa_pitch, K) || !mfma_order_ok(sb_pitch, K)) return MXFP8_ERR_SHAPE;
+  const mxfp8_gemm_desc d = {qa, sa, qb, sb, M, N, K, sa_pitch, sb_pitch, out, out_pitch};
+  mx::GemmDesc g;
+  if (mxfp8_status st = check_gemm(d, g)) return st;
   if (M == 0 || N == 0) return MXFP8_OK;
-  if (K == 0 || K % 128) return MXFP8_ERR_SHAPE;
-  if (!qa || !sa || !qb || !sb || !out) return MXFP8_ERR_NULL;
-  if (misaligned(qa) || misaligned(sa) || misaligned(qb) || misaligned(sb) || misaligned(out))
-    return MXFP8_ERR_ALIGN;
-  const int64_t kb = K / MXFP8_BLOCK;
-  if (sa_pitch > 0 && (sa_pitch < kb || !fits(M, sa_pitch))) return MXFP8_ERR_SHAPE;
-  if (sb_pitch > 0 && (sb_pitch < kb || !fits(N, sb_pitch))) return MXFP8_ERR_SHAPE;
-  if ((sa_pitch > 0 && sa_pitch % 4) || (sb_pitch > 0 && sb_pitch % 4)) return MXFP8_ERR_ALIGN;
-  const mx::ScaleStride sas = row_scale_stride(sa_pitch, M, kb), sbs = row_scale_stride(sb_pitch, N, kb);
-  // 64 x 32 outputs bound the smallest workgroup tile of every route, so this
-  // keeps grid sizes and tile indices within 32 bits
-  if (((M + 63) / 64) * ((N + 31) / 32) > kMaxGemmTiles) return MXFP8_ERR_SHAPE;
   (void)hipGetLastError();
-  return hip_status(mx::launch_gemm(static_cast<const uint8_t*>(qa), static_cast<const uint8_t*>(sa),
-                                    static_cast<const uint8_t*>(qb), static_cast<const uint8_t*>(sb),
-                                    M, N, K, sas, sbs, out, out_pitch ? out_pitch : N,
-                                    out_dtype == MXFP8_OUT_BF16,
-                                    static_cast<hipStream_t>(stream)));
+  return hip_status(mx::launch_gemm(g.qa, g.sa, g.qb, g.sb, g.M, g.N, g.K, g.sa_stride, g.sb_stride, g.out,
+                                    g.out_ld, out_dtype == MXFP8_OUT_BF16, static_cast<hipStream_t>(stream)));
+}
+
+mxfp8_status mxfp8_gemm_grouped(const mxfp8_gemm_desc* descs, int32_t n, mxfp8_out_dtype out_dtype,
+                                void* stream) {
+  if (n < 0 || (out_dtype != MXFP8_OUT_F32 && out_dtype != MXFP8_OUT_BF16)) return MXFP8_ERR_ARG;
+  if (n == 0) return MXFP8_OK;
+  if (!descs) return MXFP8_ERR_NULL;
+  std::vector<mx::GemmDesc> v(n);
+  for (int32_t i = 0; i < n; ++i)
+    if (mxfp8_status st = check_gemm(descs[i], v[i])) return st;
+  (void)hipGetLastError();
+  return hip_status(mx::launch_gemm_grouped(v.data(), n, out_dtype == MXFP8_OUT_BF16,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 mxfp8_status mxfp8_dequantize(const void* q, const void* s, int64_t rows, int64_t cols,

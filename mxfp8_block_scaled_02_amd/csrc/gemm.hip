@@ -77,6 +77,16 @@ struct GemmParams {
   int32_t tiles_m, tiles_n;
 };
 
+// A table of products for one grouped launch (the kernel argument segment
+// holds at most 4 KiB).
+constexpr int kGemmGroupMax = 32;
+struct GemmGroupArgs {
+  int32_t n;
+  int32_t task_start[kGemmGroupMax + 1];
+  GemmParams d[kGemmGroupMax];
+};
+static_assert(sizeof(GemmGroupArgs) <= 4096, "kernel arguments");
+
 __device__ __forceinline__ v8i frag(const u32x4& lo, const u32x4& hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
@@ -836,13 +846,17 @@ struct Skinny {
   }
 };
 
-template <int MT, int SC, bool RB = false>
-__global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const GemmParams pp) {
+// Arg: GemmParams, one product; or GemmGroupArgs, a table of products (MoE
+// experts, each with a few rows) in one launch, every one in row blocks.
+template <int MT, int SC, bool RB = false, class Arg = GemmParams>
+__global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(const Arg pp) {
   // RB, row blocks (for weights too narrow to give every CU a column strip):
   // tasks R i .. R i + R - 1 (R = tiles_m) take rows 32 MT r .. of A for
   // column strip i.
-  GemmParams p = pp;
+  constexpr bool kGrouped = !__is_same(Arg, GemmParams);
+  static_assert(!kGrouped || RB, "grouped products run in row blocks");
   uint32_t bid = blockIdx.x;
+  GemmParams p;
   if constexpr (RB) {
     // workgroups go round-robin over the 8 XCDs: XCD x takes the x-th
     // contiguous run of tasks, so the row blocks of a strip share its L2 and
@@ -850,13 +864,23 @@ __global__ __launch_bounds__(kSkinnyWaves * 64) void mxfp8_gemm_skinny_kernel(co
     // bytes 0.45 times; 512 x 1024 x 7168: 25.2 -> 17.8 us)
     const uint32_t T = gridDim.x, xcd = bid % 8, slot = bid / 8, per = T / 8, rem = T % 8;
     bid = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    const uint32_t nrb = (uint32_t)pp.tiles_m, rb = bid % nrb;
+    if constexpr (kGrouped) {
+      // the task's product: binary search over the prefix sum of task counts
+      const int i = find_desc(pp.task_start, pp.n, (int32_t)bid);
+      p = pp.d[i];
+      bid -= (uint32_t)pp.task_start[i];
+    } else {
+      p = pp;
+    }
+    const uint32_t nrb = (uint32_t)p.tiles_m, rb = bid % nrb;
     bid /= nrb;
     const int64_t r0 = (int64_t)rb * 32 * MT;
     p.qa += r0 * p.K;
     p.sa += r0 * p.sa_ld;
     p.out = static_cast<uint8_t*>(p.out) + r0 * p.ldo * (p.out_bf16 ? 2 : 4);
     p.M = min(p.M - r0, (int64_t)(32 * MT));
+  } else {
+    p = pp;
   }
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kSkinnyWaves * (1 + MT) * kSkinnyRegion];
   __shared__ uint32_t slds[SC == kSkinnyStaged ? kSkinnyWaves * (1 + MT) * staged_tile<MT>() : 1];
@@ -967,10 +991,11 @@ void launch_skinny(const GemmParams& p, int64_t workgroups, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
-                       int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
-                       void* out, int64_t out_ld, bool out_bf16, hipStream_t s) {
-  if (M == 0 || N == 0) return hipSuccess;
+namespace {
+
+GemmParams make_params(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb, int64_t M,
+                       int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride, void* out,
+                       int64_t out_ld, bool out_bf16) {
   GemmParams p;
   p.qa = qa; p.sa = sa; p.qb = qb; p.sb = sb; p.out = out;
   p.M = M; p.N = N; p.K = K;
@@ -978,6 +1003,67 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
   p.sa_ld = sa_stride.row; p.sb_ld = sb_stride.row;
   p.sa_gs = sa_stride.grp; p.sb_gs = sb_stride.grp;
   p.out_bf16 = out_bf16 ? 1 : 0;
+  p.tiles_m = p.tiles_n = 0;
+  return p;
+}
+
+// Tasks one grouped launch carries at most (so that the prefix sums stay
+// within 32 bits).
+constexpr int64_t kMaxGroupTasks = (int64_t)1 << 30;
+
+template <int SC>
+hipError_t flush_group(GemmGroupArgs& g, int64_t& tasks, hipStream_t s) {
+  if (g.n == 0) return hipSuccess;
+  hipLaunchKernelGGL((mxfp8_gemm_skinny_kernel<1, SC, true, GemmGroupArgs>), dim3((uint32_t)tasks),
+                     dim3(kSkinnyWaves * 64), 0, s, g);
+  g.n = 0;
+  tasks = 0;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStream_t s) {
+  // two tables: staged scale words (K up to 16384) and paired ones
+  GemmGroupArgs g[2];
+  int64_t tasks[2] = {0, 0};
+  for (int k = 0; k < 2; ++k) {
+    g[k].n = 0;
+    g[k].task_start[0] = 0;
+  }
+  for (int i = 0; i < n; ++i) {
+    const GemmDesc& e = d[i];
+    if (e.M == 0 || e.N == 0) continue;
+    if (e.M > kGemmGroupRows) {
+      if (hipError_t r = launch_gemm(e.qa, e.sa, e.qb, e.sb, e.M, e.N, e.K, e.sa_stride, e.sb_stride, e.out,
+                                     e.out_ld, out_bf16, s))
+        return r;
+      continue;
+    }
+    GemmParams p = make_params(e.qa, e.sa, e.qb, e.sb, e.M, e.N, e.K, e.sa_stride, e.sb_stride, e.out, e.out_ld,
+                               out_bf16);
+    p.tiles_m = (int32_t)((e.M + 31) / 32);
+    const int64_t t = p.tiles_m * ((e.N + 31) / 32);
+    const int64_t per_wave = (e.K / 128 + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int k = per_wave <= staged_units<1>() ? 0 : 1;
+    if (g[k].n == kGemmGroupMax || tasks[k] + t > kMaxGroupTasks) {
+      const hipError_t r = k == 0 ? flush_group<kSkinnyStaged>(g[0], tasks[0], s)
+                                  : flush_group<kSkinnyPaired>(g[1], tasks[1], s);
+      if (r != hipSuccess) return r;
+    }
+    g[k].d[g[k].n] = p;
+    tasks[k] += t;
+    g[k].task_start[++g[k].n] = (int32_t)tasks[k];
+  }
+  if (hipError_t r = flush_group<kSkinnyStaged>(g[0], tasks[0], s)) return r;
+  return flush_group<kSkinnyPaired>(g[1], tasks[1], s);
+}
+
+hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
+                       int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
+                       void* out, int64_t out_ld, bool out_bf16, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmParams p = make_params(qa, sa, qb, sb, M, N, K, sa_stride, sb_stride, out, out_ld, out_bf16);
   const int64_t skinny = (N + 31) / 32;
   const int64_t r32 = (M + 31) / 32, r64 = (M + 63) / 64, r128 = (M + 127) / 128;
   // A weight of few column strips leaves CUs idle (each workgroup streams its

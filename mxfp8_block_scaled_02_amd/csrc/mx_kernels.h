@@ -189,6 +189,19 @@ hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipSt
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
                        void* out, int64_t out_ld, bool out_bf16, hipStream_t s);
+// A list of products (MoE experts): those with at most kGemmGroupRows rows
+// share launches of the skinny kernel in 32-row blocks (a table of up to 32
+// products each, one table for each scale-word mode); larger ones take
+// launch_gemm's routes one by one.
+struct GemmDesc {
+  const uint8_t *qa, *sa, *qb, *sb;
+  int64_t M, N, K;
+  ScaleStride sa_stride, sb_stride;
+  void* out;
+  int64_t out_ld;
+};
+constexpr int64_t kGemmGroupRows = 128;
+hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStream_t s);
 
 // The tensor of a launch's table that task belongs to: the last i with
 // start[i] <= task, by binary search over the prefix sum of task counts.

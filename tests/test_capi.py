@@ -35,7 +35,7 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), "missing export " + n
 
@@ -153,6 +153,26 @@ def test_scale_pitch_checks(L):
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 72 + 4)), 1, 0, None) == ERR_ALIGN
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 32, 64, 1, C, 32)), 1, 0, None) == ERR_SHAPE
     assert L.mxfp8_dequantize_grouped((Dq * 1)(Dq(A, B, 1 << 20, 64, 0, C, 1 << 60)), 1, 0, None) == ERR_SHAPE
+
+
+def test_grouped_gemm_checks(L):
+    """Every product of a grouped call is checked before the first launch,
+    with mxfp8_gemm's rules.  Only rejected calls are made here (no GPU)."""
+    G = mx._GemmDesc
+    def grouped(*ds, dtype=0):
+        return L.mxfp8_gemm_grouped((G * len(ds))(*[G(*d) for d in ds]), len(ds), dtype, None)
+    good = (A, B, C, D, 4, 4, 128, 0, 0, A, 0)
+    assert grouped(good, (A, B, C, D, 4, 4, 96, 0, 0, A, 0)) == ERR_SHAPE     # K % 128, after a valid one
+    assert grouped(good, (A, B, C, None, 4, 4, 128, 0, 0, A, 0)) == ERR_NULL
+    assert grouped(good, (A, B, C, D, 4, 4, 128, 0, 0, MIS, 0)) == ERR_ALIGN
+    assert grouped(good, (A, B, C, D, 4, 4, 128, 0, 0, A, 3)) == ERR_SHAPE     # out pitch < N
+    assert grouped(good, (A, B, C, D, 4, 4, 256, -1, 0, A, 0)) == ERR_SHAPE    # MFMA order needs K % 512
+    assert grouped(good, dtype=7) == ERR_ARG
+    assert L.mxfp8_gemm_grouped(None, 2, 0, None) == ERR_NULL
+    assert L.mxfp8_gemm_grouped(None, -1, 0, None) == ERR_ARG
+    assert L.mxfp8_gemm_grouped(None, 0, 0, None) == OK
+    assert grouped((A, B, C, D, 0, 4, 96, 0, 0, None, 0)) == OK               # M == 0: a no-op, as in mxfp8_gemm
+    assert grouped((A, B, C, D, -1, 4, 128, 0, 0, A, 0)) == ERR_SHAPE
 
 
 def test_transposed_columnwise_checks(L):

@@ -1,0 +1,119 @@
+"""GPU parity of the grouped matrix product (mxfp8_gemm_grouped): MoE experts,
+each with its own token count, weight and output.  Every product equals the
+single call on the same planes bit for bit (the grouped launch runs the same
+per-tile arithmetic in 32-row blocks), and lies within the accumulation bound
+of the oracle's float64 product."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_02_amd as mx
+from tests import gemm_accuracy as acc
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def planes(rows, cols, std, seed, order="row"):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(rows, cols, generator=g) * std).to(torch.bfloat16).to(DEV)
+    p = mx.quantize(x, True, False, scale_order=order)
+    return p.rowwise_data, p.rowwise_scale
+
+
+def same_bits(a, b):
+    v = torch.int32 if a.dtype == torch.float32 else torch.int16
+    return torch.equal(a.view(v), b.view(v))
+
+
+def check_oracle(orc, qa, sa, qb, sb, out, what):
+    hp = [t.cpu().numpy() for t in (qa, sa, qb, sb)]
+    if sa.dim() == 3:            # MFMA order -> compact
+        M, K = qa.shape
+        hp[1] = hp[1].transpose(1, 0, 2).reshape(M, K // 32)
+    if sb.dim() == 3:
+        N, K = qb.shape
+        hp[3] = hp[3].transpose(1, 0, 2).reshape(N, K // 32)
+    C, _ = orc.gemm(*hp)
+    tol = acc.bound(*hp)
+    got = out.float().cpu().numpy().astype(np.float64)
+    if out.dtype == torch.bfloat16:
+        tol = tol + 2.0 ** -8 * (np.abs(C) + tol)
+    assert (np.abs(got - C) <= tol).all(), "%s: outside the accumulation bound" % what
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_moe_experts(orc, dtype):
+    """12 experts, weights [N, 1024] of three widths, token counts 0 .. 300
+    (up to 128: the shared launch; above: single-call routes)."""
+    tokens = [0, 1, 3, 16, 31, 32, 33, 64, 100, 128, 129, 300]
+    widths = [384, 520, 1000]
+    K = 1024
+    A = [planes(m, K, 1.0, 10 + i) for i, m in enumerate(tokens)]
+    B = [planes(widths[i % 3], K, 0.05, 40 + i) for i in range(len(tokens))]
+    say("grouped experts", tokens, widths, dtype)
+    outs = mx.gemm_grouped([a[0] for a in A], [a[1] for a in A], [b[0] for b in B], [b[1] for b in B], dtype)
+    torch.cuda.synchronize()
+    for i, (a, b, o) in enumerate(zip(A, B, outs)):
+        assert tuple(o.shape) == (tokens[i], widths[i % 3])
+        single = mx.gemm(a[0], a[1], b[0], b[1], dtype)
+        torch.cuda.synchronize()
+        assert same_bits(o, single), "expert %d (%d tokens) differs from the single call" % (i, tokens[i])
+        if tokens[i]:
+            check_oracle(orc, a[0], a[1], b[0], b[1], o, "expert %d" % i)
+
+
+def test_many_products_both_scale_modes(orc):
+    """40 products (two tables of the staged mode), some with K = 16896
+    (paired scale words) in between: each equals its single call."""
+    specs = [(1 + (7 * i) % 96, 64 + 32 * (i % 5), 16896 if i % 9 == 4 else 512) for i in range(40)]
+    A = [planes(m, k, 1.0, 100 + i) for i, (m, n, k) in enumerate(specs)]
+    B = [planes(n, k, 0.05, 200 + i) for i, (m, n, k) in enumerate(specs)]
+    say("grouped 40 products", specs[:6], "...")
+    outs = mx.gemm_grouped([a[0] for a in A], [a[1] for a in A], [b[0] for b in B], [b[1] for b in B])
+    torch.cuda.synchronize()
+    for i, (a, b, o) in enumerate(zip(A, B, outs)):
+        single = mx.gemm(a[0], a[1], b[0], b[1])
+        torch.cuda.synchronize()
+        assert same_bits(o, single), "product %d %s differs from the single call" % (i, specs[i])
+    for i in (0, 4, 13, 39):
+        check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], outs[i], "product %d" % i)
+
+
+def test_mfma_order_and_output_slices(orc):
+    """Scales in the MFMA order, outputs written as column slices of one
+    wider matrix (the experts' outputs side by side) inside a buffer of
+    guard bytes: nothing outside the slices changes."""
+    tokens, N, K = [5, 40, 128, 17], 256, 1536
+    A = [planes(m, K, 1.0, 300 + i, "mfma") for i, m in enumerate(tokens)]
+    B = [planes(N, K, 0.05, 400 + i, "mfma") for i in range(len(tokens))]
+    M = max(tokens)
+    pad, width = 4096, len(tokens) * N + 8
+    buf = torch.full((pad + M * width + pad,), -0x5A5A5A5B, dtype=torch.int32, device=DEV)
+    wide = buf[pad:pad + M * width].view(M, width).view(torch.float32)
+    outs = [wide[:m, i * N:(i + 1) * N] for i, m in enumerate(tokens)]
+    say("grouped mfma order, output slices", tokens)
+    got = mx.gemm_grouped([a[0] for a in A], [a[1] for a in A], [b[0] for b in B], [b[1] for b in B],
+                          torch.float32, outs=outs)
+    torch.cuda.synchronize()
+    inside = torch.zeros(buf.numel(), dtype=torch.bool, device=DEV)
+    for i, m in enumerate(tokens):
+        assert got[i].data_ptr() == outs[i].data_ptr()
+        inside[pad:pad + M * width].view(M, width)[:m, i * N:(i + 1) * N] = True
+        single = mx.gemm(A[i][0], A[i][1], B[i][0], B[i][1])
+        torch.cuda.synchronize()
+        assert same_bits(got[i].contiguous(), single), "expert %d" % i
+        check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], got[i], "expert %d" % i)
+    assert bool((buf[~inside] == -0x5A5A5A5B).all()), "guard bytes written"
+
+
+def test_empty_list_and_refused_product():
+    assert mx.gemm_grouped([], [], [], []) == []
+    qa, sa = planes(4, 256, 1.0, 1)
+    qb, sb = planes(8, 128, 1.0, 2)
+    with pytest.raises(ValueError):
+        mx.gemm_grouped([qa], [sa], [qb], [sb])          # K 256 against 128
