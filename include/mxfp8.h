@@ -365,9 +365,9 @@ mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc *descs, int32_t n,
  * MoE products take MXFP8 expert weights).  Each descriptor follows
  * mxfp8_gemm's rules and gives the same result as that call; out_dtype
  * applies to all.  Products of at most 128 rows (a few tokens per expert)
- * share launches: every one of them is cut into 32-row blocks of 32 output
- * columns, so even a list of one-token products fills the GPU; larger
- * products run as single calls.  Every descriptor is checked before the
+ * share launches, one workgroup per 32 output columns of each, so even a
+ * list of one-token products fills the GPU; larger products run as single
+ * calls.  Every descriptor is checked before the
  * first launch; n == 0 is a no-op, n < 0 is MXFP8_ERR_ARG.
  */
 mxfp8_status mxfp8_gemm_grouped(const mxfp8_gemm_desc *descs, int32_t n,

@@ -190,8 +190,9 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
                        int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
                        void* out, int64_t out_ld, bool out_bf16, hipStream_t s);
 // A list of products (MoE experts): those with at most kGemmGroupRows rows
-// share launches of the skinny kernel in 32-row blocks (a table of up to 32
-// products each, one table for each scale-word mode); larger ones take
+// share launches of the skinny kernel, one workgroup per 32 output columns
+// with one, two or four 32-row A tiles (a table of up to 32 products each,
+// one table for each tile count and scale-word mode); larger ones take
 // launch_gemm's routes one by one.
 struct GemmDesc {
   const uint8_t *qa, *sa, *qb, *sb;
