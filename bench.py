@@ -358,11 +358,11 @@ def bench_other_rows(torch, mx, synth, steps):
                "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "Gelem_s": round(e / (ms * 1e-3) / 1e9, 2), "alg_bytes": b}
            for k, (ms, b, e) in res.items()}
-    out.update(bench_gemm(torch, mx, steps))
+    out.update(bench_gemm(torch, mx, steps, synth))
     return out
 
 
-def bench_gemm(torch, mx, steps):
+def bench_gemm(torch, mx, steps, synth=None):
     """The MXFP8 product of a quantized activation and a quantized weight:
     TFLOP/s (2 M N K per launch) against the dense fp8 matrix-core peak."""
     dev = torch.device("cuda:0")
@@ -404,6 +404,29 @@ def bench_gemm(torch, mx, steps):
                         "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
         res["gemm_bf16out_%dx%dx%d%s" % (M, N, K, "_mfma_scales" if order == "mfma" else "")] = rec
         del bs, pa, out
+
+    # the grouped product of an MoE layer in decode: the 64 expert weights
+    # [2048, 7168] of the grouped quantize, 16 tokens each, one launch; the
+    # weights (940 MB) exceed the Infinity Cache, so each launch reads them
+    # from HBM
+    ws = synth.workload(HEADLINE, device=dev)["xs"]
+    E, (N, K), tok = len(ws), ws[0].shape, 16
+    pw = mx.quantize_grouped(ws, True, False)
+    del ws
+    g = torch.Generator(device=dev).manual_seed(7)
+    pa = [mx.quantize(torch.randn((tok, K), generator=g, device=dev).to(torch.bfloat16), True, False)
+          for _ in range(E)]
+    outs = [torch.empty((tok, N), dtype=torch.bfloat16, device=dev) for _ in range(E)]
+    args = ([p.rowwise_data for p in pa], [p.rowwise_scale for p in pa], [p.rowwise_data for p in pw],
+            [p.rowwise_scale for p in pw])
+    ms, _ = T.run(lambda i: mx.gemm_grouped(*args, torch.bfloat16, outs=outs), max(steps // 4, 20), 3, replays=5)
+    alg = E * ((tok + N) * K * (1 + 1 / 32) + 2 * tok * N)
+    tf = 2.0 * E * tok * N * K / (ms * 1e-3) / 1e12
+    res["gemm_grouped_moe_64_experts_16x2048x7168"] = {
+        "ms_per_launch": round(ms, 5), "TFLOP_s": round(tf, 1), "frac_mfma_fp8": round(tf / FP8_MFMA_PEAK_TFLOPS, 4),
+        "alg_bytes": int(alg), "GB_s": round(alg / (ms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del pw, pa, outs, args
     return res
 
 
