@@ -3,8 +3,8 @@ against the oracle: rowwise-only (flat tasks), columnwise-only (tiles, and
 the narrow path for rows of any length) and both planes, bf16 and float32
 input, compact and padded scale planes, the columnwise plane stored
 transposed, grouped lists spanning launches, the fused RMSNorm, dequantize on
-both axes, and the matrix product on each of its tilings (within the
-accumulation bound)."""
+both axes, the matrix product on each of its tilings (within the
+accumulation bound), and grouped products (equal to single calls)."""
 import numpy as np
 import pytest
 import torch
@@ -154,6 +154,36 @@ def test_random_gemm_shapes(orc, seed):
         tol = acc.bound(*(t.cpu().numpy() for t in (pa.rowwise_data, pa.rowwise_scale,
                                                      pb.rowwise_data, pb.rowwise_scale)))
         assert (err <= tol).all(), "gemm %s beyond the accumulation bound" % ((M, N, K),)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_grouped_gemm(seed):
+    """Random lists of products (token counts 0 .. 200, widths, depths, scale
+    orders, output dtypes): every product of a grouped call equals its single
+    call bit for bit."""
+    g = np.random.default_rng(4000 + seed)
+    for case in range(3):
+        n = int(g.integers(1, 45))
+        dtype = torch.bfloat16 if g.random() < 0.5 else torch.float32
+        specs = []
+        for _ in range(n):
+            K = 128 * int(g.integers(1, 20)) if g.random() < 0.9 else 16896
+            M = int(g.choice([int(g.integers(0, 33)), int(g.integers(33, 129)), int(g.integers(129, 200))]))
+            specs.append((M, int(g.integers(1, 600)), K))
+        say("grouped gemm seed", seed, "case", case, n, "products", dtype, specs[:4])
+        A, B = [], []
+        for M, N, K in specs:
+            order = "mfma" if K % 512 == 0 and g.random() < 0.3 else "row"
+            A.append(mx.quantize(input_tensor(M, K, g, torch.bfloat16), True, False, scale_order=order))
+            B.append(mx.quantize(input_tensor(N, K, g, torch.bfloat16), True, False, scale_order=order))
+        got = mx.gemm_grouped([a.rowwise_data for a in A], [a.rowwise_scale for a in A],
+                              [b.rowwise_data for b in B], [b.rowwise_scale for b in B], dtype)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(A, B)):
+            single = mx.gemm(a.rowwise_data, a.rowwise_scale, b.rowwise_data, b.rowwise_scale, dtype)
+            torch.cuda.synchronize()
+            bits = torch.int32 if dtype == torch.float32 else torch.int16
+            assert torch.equal(got[i].view(bits), single.view(bits)), "product %d %s" % (i, specs[i])
 
 
 @pytest.mark.parametrize("seed", range(4))

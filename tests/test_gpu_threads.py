@@ -24,8 +24,11 @@ def work(x, gamma, w):
     d = mx.dequantize(p.columnwise_data, p.columnwise_scale, mx.COLUMNWISE, torch.float32)
     g = mx.quantize_grouped([x, w], True, True)
     y = mx.gemm(p.rowwise_data, p.rowwise_scale, g[1].rowwise_data, g[1].rowwise_scale, torch.bfloat16)
+    t = mx.quantize(x, False, True, columnwise_transposed=True)
+    yg = mx.gemm_grouped([p.rowwise_data[:16], p.rowwise_data], [p.rowwise_scale[:16], p.rowwise_scale],
+                         [g[1].rowwise_data, g[1].rowwise_data], [g[1].rowwise_scale, g[1].rowwise_scale])
     return [p.rowwise_data, p.rowwise_scale, p.columnwise_data, p.columnwise_scale, n, q, s, d,
-            g[0].columnwise_data, y]
+            g[0].columnwise_data, y, t.columnwise_data, t.columnwise_scale] + yg
 
 
 def same(a, b):
