@@ -404,18 +404,36 @@ struct TileRing {
   }
 };
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const GemmParams p) {
+__device__ __forceinline__ const GemmParams& product_of(const GemmParams& p, int) { return p; }
+__device__ __forceinline__ const GemmParams& product_of(const GemmGroupArgs& a, int i) { return a.d[i]; }
+
+// Arg: GemmParams, one product; or GemmGroupArgs, a table of products whose
+// tiles share one launch (each product's tiles in its own order).
+template <int BM, int BN, class Arg = GemmParams>
+__global__ __launch_bounds__(kThreads) void mxfp8_gemm_ring_kernel(const Arg pp) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // workgroups go round-robin over the 8 XCDs: give XCD x the x-th contiguous
   // run of the tile order, then walk groups of kGroupM tile rows column by column
-  const uint32_t T = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n;
+  // (a grouped launch: the order over the whole grid, then the task's product
+  // by binary search over the prefix sum of tile counts)
   const uint32_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const uint32_t per = T / 8, rem = T % 8;
-  const uint32_t v = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  int prod = 0;
+  uint32_t v;
+  if constexpr (!__is_same(Arg, GemmParams)) {
+    const uint32_t T = gridDim.x, per = T / 8, rem = T % 8;
+    v = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    prod = find_desc(pp.task_start, pp.n, (int32_t)v);
+    v -= (uint32_t)pp.task_start[prod];
+  }
+  const GemmParams p = product_of(pp, prod);
+  if constexpr (__is_same(Arg, GemmParams)) {
+    const uint32_t T = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n;
+    const uint32_t per = T / 8, rem = T % 8;
+    v = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  }
   const uint32_t gsize = (uint32_t)kGroupM * (uint32_t)p.tiles_n;
   const uint32_t grp = v / gsize, first_m = grp * kGroupM;
   const uint32_t gm = min((uint32_t)p.tiles_m - first_m, (uint32_t)kGroupM);
@@ -1021,6 +1039,30 @@ hipError_t flush_group(GemmGroupArgs& g, int64_t& tasks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the ring tiles, in the order of the single-call cost model, and the time of
+// one tile at full load in eighths of a 256 x 256 tile's
+struct RingTile { int bm, bn; int64_t weight; };
+constexpr RingTile kRingTiles[4] = {{256, 256, 8}, {128, 256, 5}, {128, 128, 3}, {64, 128, 2}};
+
+template <int BM, int BN>
+hipError_t flush_ring_group(GemmGroupArgs& g, int64_t& tasks, hipStream_t s) {
+  if (g.n == 0) return hipSuccess;
+  hipLaunchKernelGGL((mxfp8_gemm_ring_kernel<BM, BN, GemmGroupArgs>), dim3((uint32_t)tasks), dim3(kThreads), 0,
+                     s, g);
+  g.n = 0;
+  tasks = 0;
+  return hipGetLastError();
+}
+
+hipError_t flush_ring_table(int t, GemmGroupArgs& g, int64_t& tasks, hipStream_t s) {
+  switch (t) {
+    case 0: return flush_ring_group<256, 256>(g, tasks, s);
+    case 1: return flush_ring_group<128, 256>(g, tasks, s);
+    case 2: return flush_ring_group<128, 128>(g, tasks, s);
+    default: return flush_ring_group<64, 128>(g, tasks, s);
+  }
+}
+
 // table t: A tiles per workgroup 1, 2 or 4 (t / 2), staged or paired scale words (t % 2)
 hipError_t flush_table(int t, GemmGroupArgs& g, int64_t& tasks, hipStream_t s) {
   switch (t) {
@@ -1036,20 +1078,51 @@ hipError_t flush_table(int t, GemmGroupArgs& g, int64_t& tasks, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStream_t s) {
-  constexpr int kTables = 6;
-  GemmGroupArgs g[kTables];
-  int64_t tasks[kTables] = {};
+  constexpr int kTables = 6, kRingTables = 4;
+  GemmGroupArgs g[kTables], rg[kRingTables];
+  int64_t tasks[kTables] = {}, rtasks[kRingTables] = {};
   for (int k = 0; k < kTables; ++k) {
     g[k].n = 0;
     g[k].task_start[0] = 0;
   }
+  for (int k = 0; k < kRingTables; ++k) {
+    rg[k].n = 0;
+    rg[k].task_start[0] = 0;
+  }
   for (int i = 0; i < n; ++i) {
     const GemmDesc& e = d[i];
     if (e.M == 0 || e.N == 0) continue;
-    if (e.M > kGemmGroupRows) {
+    if (e.M > kGemmGroupRows && e.K < kBK * kGroup) {
+      // K below one scale group: the single call's tile128 route
       if (hipError_t r = launch_gemm(e.qa, e.sa, e.qb, e.sb, e.M, e.N, e.K, e.sa_stride, e.sb_stride, e.out,
                                      e.out_ld, out_bf16, s))
         return r;
+      continue;
+    }
+    if (e.M > kGemmGroupRows) {
+      // ring tiles: the grouped grid is large, so the tile with the least
+      // time over all its tiles (no rounds over the CUs to weigh)
+      int best = 0;
+      int64_t best_cost = 0;
+      for (int c = 0; c < kRingTables; ++c) {
+        const int64_t tiles = ((e.M + kRingTiles[c].bm - 1) / kRingTiles[c].bm) *
+                              ((e.N + kRingTiles[c].bn - 1) / kRingTiles[c].bn);
+        if (c == 0 || tiles * kRingTiles[c].weight < best_cost) {
+          best = c;
+          best_cost = tiles * kRingTiles[c].weight;
+        }
+      }
+      GemmParams p = make_params(e.qa, e.sa, e.qb, e.sb, e.M, e.N, e.K, e.sa_stride, e.sb_stride, e.out,
+                                 e.out_ld, out_bf16);
+      p.tiles_m = (int32_t)((e.M + kRingTiles[best].bm - 1) / kRingTiles[best].bm);
+      p.tiles_n = (int32_t)((e.N + kRingTiles[best].bn - 1) / kRingTiles[best].bn);
+      const int64_t t = (int64_t)p.tiles_m * p.tiles_n;
+      if (rg[best].n == kGemmGroupMax || rtasks[best] + t > kMaxGroupTasks) {
+        if (hipError_t r = flush_ring_table(best, rg[best], rtasks[best], s)) return r;
+      }
+      rg[best].d[rg[best].n] = p;
+      rtasks[best] += t;
+      rg[best].task_start[++rg[best].n] = (int32_t)rtasks[best];
       continue;
     }
     GemmParams p = make_params(e.qa, e.sa, e.qb, e.sb, e.M, e.N, e.K, e.sa_stride, e.sb_stride, e.out, e.out_ld,
@@ -1073,6 +1146,8 @@ hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStrea
   }
   for (int k = 0; k < kTables; ++k)
     if (hipError_t r = flush_table(k, g[k], tasks[k], s)) return r;
+  for (int k = 0; k < kRingTables; ++k)
+    if (hipError_t r = flush_ring_table(k, rg[k], rtasks[k], s)) return r;
   return hipSuccess;
 }
 

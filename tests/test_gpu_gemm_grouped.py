@@ -1,8 +1,10 @@
 """GPU parity of the grouped matrix product (mxfp8_gemm_grouped): MoE experts,
-each with its own token count, weight and output.  Every product equals the
-single call on the same planes bit for bit (the grouped launch runs the same
-per-tile arithmetic in 32-row blocks), and lies within the accumulation bound
-of the oracle's float64 product."""
+each with its own token count, weight and output.  Every product lies within
+the accumulation bound of the oracle's float64 product.  Products of up to
+128 rows equal the single call on the same planes bit for bit (the grouped
+launch runs the same per-tile arithmetic); larger ones share ring-tile
+launches, whose tiles may start K at another quarter than the single call's,
+so their sums may be taken in another order."""
 import numpy as np
 import pytest
 import torch
@@ -30,7 +32,9 @@ def same_bits(a, b):
     return torch.equal(a.view(v), b.view(v))
 
 
-def check_oracle(orc, qa, sa, qb, sb, out, what):
+def check_oracle(orc, qa, sa, qb, sb, out, what, samples=None):
+    """Within the accumulation bound; samples: check that many random
+    outputs (and the last row and column) instead of all."""
     hp = [t.cpu().numpy() for t in (qa, sa, qb, sb)]
     if sa.dim() == 3:            # MFMA order -> compact
         M, K = qa.shape
@@ -38,9 +42,18 @@ def check_oracle(orc, qa, sa, qb, sb, out, what):
     if sb.dim() == 3:
         N, K = qb.shape
         hp[3] = hp[3].transpose(1, 0, 2).reshape(N, K // 32)
-    C, _ = orc.gemm(*hp)
-    tol = acc.bound(*hp)
     got = out.float().cpu().numpy().astype(np.float64)
+    if samples is not None:
+        M, N = got.shape
+        g = np.random.default_rng(M * 7 + N)
+        ms = np.concatenate([g.integers(0, M, samples), np.full(N, M - 1), np.arange(M)])
+        ns = np.concatenate([g.integers(0, N, samples), np.arange(N), np.full(M, N - 1)])
+        C, _ = orc.gemm_at(*hp, ms, ns)
+        tol = acc.bound_at(*hp, ms, ns)
+        got = got[ms, ns]
+    else:
+        C, _ = orc.gemm(*hp)
+        tol = acc.bound(*hp)
     if out.dtype == torch.bfloat16:
         tol = tol + 2.0 ** -8 * (np.abs(C) + tol)
     assert (np.abs(got - C) <= tol).all(), "%s: outside the accumulation bound" % what
@@ -49,7 +62,7 @@ def check_oracle(orc, qa, sa, qb, sb, out, what):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_moe_experts(orc, dtype):
     """12 experts, weights [N, 1024] of three widths, token counts 0 .. 300
-    (up to 128: the shared launch; above: single-call routes)."""
+    (up to 128: the skinny tables; above: the ring-tile tables)."""
     tokens = [0, 1, 3, 16, 31, 32, 33, 64, 100, 128, 129, 300]
     widths = [384, 520, 1000]
     K = 1024
@@ -60,9 +73,10 @@ def test_moe_experts(orc, dtype):
     torch.cuda.synchronize()
     for i, (a, b, o) in enumerate(zip(A, B, outs)):
         assert tuple(o.shape) == (tokens[i], widths[i % 3])
-        single = mx.gemm(a[0], a[1], b[0], b[1], dtype)
-        torch.cuda.synchronize()
-        assert same_bits(o, single), "expert %d (%d tokens) differs from the single call" % (i, tokens[i])
+        if tokens[i] <= 128:
+            single = mx.gemm(a[0], a[1], b[0], b[1], dtype)
+            torch.cuda.synchronize()
+            assert same_bits(o, single), "expert %d (%d tokens) differs from the single call" % (i, tokens[i])
         if tokens[i]:
             check_oracle(orc, a[0], a[1], b[0], b[1], o, "expert %d" % i)
 
@@ -109,6 +123,26 @@ def test_mfma_order_and_output_slices(orc):
         assert same_bits(got[i].contiguous(), single), "expert %d" % i
         check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], got[i], "expert %d" % i)
     assert bool((buf[~inside] == -0x5A5A5A5B).all()), "guard bytes written"
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_prefill_experts(orc, dtype):
+    """Experts of 129 .. 900 tokens share ring-tile launches, each with the
+    tile its shape favours (256 x 256, 128 x 256 and 128 x 128 occur), K with
+    and without a short last scale group, and one K below 512 (a single
+    call)."""
+    specs = [(129, 256, 512), (200, 384, 640), (256, 520, 1024), (300, 1000, 1536), (512, 256, 512),
+             (640, 2048, 1024), (900, 300, 1152), (130, 130, 384), (256, 256, 2048), (384, 640, 512),
+             (160, 128, 512), (170, 100, 1024)]
+    A = [planes(m, k, 1.0, 500 + i) for i, (m, n, k) in enumerate(specs)]
+    B = [planes(n, k, 0.05, 600 + i) for i, (m, n, k) in enumerate(specs)]
+    say("grouped prefill experts", specs, dtype)
+    outs = mx.gemm_grouped([a[0] for a in A], [a[1] for a in A], [b[0] for b in B], [b[1] for b in B], dtype)
+    torch.cuda.synchronize()
+    for i, (m, n, k) in enumerate(specs):
+        assert tuple(outs[i].shape) == (m, n)
+        check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], outs[i], "expert %s" % (specs[i],),
+                     samples=None if m * n * k <= 1 << 27 else 4000)
 
 
 def test_empty_list_and_refused_product():
