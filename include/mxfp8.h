@@ -363,12 +363,14 @@ mxfp8_status mxfp8_dequantize_grouped(const mxfp8_deq_desc *descs, int32_t n,
  * experts of an MoE layer, each with its own activation rows, weight,
  * shape and output (quantization.utils page, resolve_mxfp8_backend: grouped
  * MoE products take MXFP8 expert weights).  Each descriptor follows
- * mxfp8_gemm's rules and gives the same result as that call; out_dtype
- * applies to all.  Products of at most 128 rows (a few tokens per expert)
- * share launches, one workgroup per 32 output columns of each, so even a
- * list of one-token products fills the GPU; larger products run as single
- * calls.  Every descriptor is checked before the
- * first launch; n == 0 is a no-op, n < 0 is MXFP8_ERR_ARG.
+ * mxfp8_gemm's rules and its result meets mxfp8_gemm's accuracy statement;
+ * out_dtype applies to all.  The products share launches, so even a list of
+ * one-token products fills the GPU: products of at most 32 rows (and of at
+ * most 128 with K < 512) one workgroup per 32 output columns, their results
+ * equal to mxfp8_gemm's bit for bit; larger ones ring tiles, whose 64-deep
+ * steps may be summed in another order than mxfp8_gemm's; more than 128
+ * rows with K < 512 run as single calls.  Every descriptor is checked
+ * before the first launch; n == 0 is a no-op, n < 0 is MXFP8_ERR_ARG.
  */
 mxfp8_status mxfp8_gemm_grouped(const mxfp8_gemm_desc *descs, int32_t n,
                                 mxfp8_out_dtype out_dtype, void *stream);

@@ -1092,16 +1092,21 @@ hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStrea
   for (int i = 0; i < n; ++i) {
     const GemmDesc& e = d[i];
     if (e.M == 0 || e.N == 0) continue;
-    if (e.M > kGemmGroupRows && e.K < kBK * kGroup) {
+    // Products of more than 32 rows take ring tiles when K allows (K >= 512):
+    // with a grouped grid that large they beat the skinny kernel's tiles
+    // (64 experts x [2048, 7168]: 33 tokens each 207 against 275 us, 64
+    // tokens 212 against 315 us, 128 tokens 222 against 435 us).
+    const bool ring = e.M > kGroupSkinnyRows && e.K >= kBK * kGroup;
+    if (!ring && e.M > kGemmGroupRows) {
       // K below one scale group: the single call's tile128 route
       if (hipError_t r = launch_gemm(e.qa, e.sa, e.qb, e.sb, e.M, e.N, e.K, e.sa_stride, e.sb_stride, e.out,
                                      e.out_ld, out_bf16, s))
         return r;
       continue;
     }
-    if (e.M > kGemmGroupRows) {
-      // ring tiles: the grouped grid is large, so the tile with the least
-      // time over all its tiles (no rounds over the CUs to weigh)
+    if (ring) {
+      // the tile with the least time over all its tiles (the grouped grid is
+      // large, so there are no rounds over the CUs to weigh)
       int best = 0;
       int64_t best_cost = 0;
       for (int c = 0; c < kRingTables; ++c) {

@@ -189,11 +189,13 @@ hipError_t launch_dequantize(const DeqArgsPitched& a, int64_t total_tasks, hipSt
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, const uint8_t* sb,
                        int64_t M, int64_t N, int64_t K, ScaleStride sa_stride, ScaleStride sb_stride,
                        void* out, int64_t out_ld, bool out_bf16, hipStream_t s);
-// A list of products (MoE experts): those with at most kGemmGroupRows rows
-// share launches of the skinny kernel, one workgroup per 32 output columns
-// with one, two or four 32-row A tiles (a table of up to 32 products each,
-// one table for each tile count and scale-word mode); larger ones take
-// launch_gemm's routes one by one.
+// A list of products (MoE experts), in shared launches: products of up to
+// kGroupSkinnyRows rows (or up to kGemmGroupRows with K < 512) run the
+// skinny kernel, one workgroup per 32 output columns with one, two or four
+// 32-row A tiles; the others with K >= 512 run ring tiles, each product with
+// its own tile size; a table of up to 32 products per launch, one table for
+// each kernel variant.  Products of more than kGemmGroupRows rows with
+// K < 512 take launch_gemm's route one by one.
 struct GemmDesc {
   const uint8_t *qa, *sa, *qb, *sb;
   int64_t M, N, K;
@@ -202,6 +204,7 @@ struct GemmDesc {
   int64_t out_ld;
 };
 constexpr int64_t kGemmGroupRows = 128;
+constexpr int64_t kGroupSkinnyRows = 32;
 hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStream_t s);
 
 // The tensor of a launch's table that task belongs to: the last i with

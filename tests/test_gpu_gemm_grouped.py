@@ -1,10 +1,10 @@
 """GPU parity of the grouped matrix product (mxfp8_gemm_grouped): MoE experts,
 each with its own token count, weight and output.  Every product lies within
 the accumulation bound of the oracle's float64 product.  Products of up to
-128 rows equal the single call on the same planes bit for bit (the grouped
-launch runs the same per-tile arithmetic); larger ones share ring-tile
-launches, whose tiles may start K at another quarter than the single call's,
-so their sums may be taken in another order."""
+32 rows (up to 128 with K < 512) equal the single call on the same planes
+bit for bit (the grouped launch runs the same per-tile arithmetic); the
+others share ring-tile launches, whose tiles may start K at another quarter
+than the single call's, so their sums may be taken in another order."""
 import numpy as np
 import pytest
 import torch
@@ -25,6 +25,11 @@ def planes(rows, cols, std, seed, order="row"):
     x = (torch.randn(rows, cols, generator=g) * std).to(torch.bfloat16).to(DEV)
     p = mx.quantize(x, True, False, scale_order=order)
     return p.rowwise_data, p.rowwise_scale
+
+
+def skinny_group(M, K):
+    """The products a grouped call runs on the skinny kernel."""
+    return M <= 32 or (M <= 128 and K < 512)
 
 
 def same_bits(a, b):
@@ -62,7 +67,7 @@ def check_oracle(orc, qa, sa, qb, sb, out, what, samples=None):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_moe_experts(orc, dtype):
     """12 experts, weights [N, 1024] of three widths, token counts 0 .. 300
-    (up to 128: the skinny tables; above: the ring-tile tables)."""
+    (up to 32: the skinny tables; above: the ring-tile tables)."""
     tokens = [0, 1, 3, 16, 31, 32, 33, 64, 100, 128, 129, 300]
     widths = [384, 520, 1000]
     K = 1024
@@ -73,7 +78,7 @@ def test_moe_experts(orc, dtype):
     torch.cuda.synchronize()
     for i, (a, b, o) in enumerate(zip(A, B, outs)):
         assert tuple(o.shape) == (tokens[i], widths[i % 3])
-        if tokens[i] <= 128:
+        if skinny_group(tokens[i], K):
             single = mx.gemm(a[0], a[1], b[0], b[1], dtype)
             torch.cuda.synchronize()
             assert same_bits(o, single), "expert %d (%d tokens) differs from the single call" % (i, tokens[i])
@@ -82,20 +87,24 @@ def test_moe_experts(orc, dtype):
 
 
 def test_many_products_both_scale_modes(orc):
-    """40 products (two tables of the staged mode), some with K = 16896
-    (paired scale words) in between: each equals its single call."""
-    specs = [(1 + (7 * i) % 96, 64 + 32 * (i % 5), 16896 if i % 9 == 4 else 512) for i in range(40)]
+    """40 skinny products (two tables of the staged mode), some with K = 16896
+    (paired scale words) in between, and 10 ring-tile products: each skinny
+    one equals its single call; every one is within the bound."""
+    specs = [(1 + (7 * i) % 32, 64 + 32 * (i % 5), 16896 if i % 9 == 4 else 512) for i in range(40)]
+    specs += [(33 + 9 * i, 96 + 40 * i, 512 if i % 2 else 1024) for i in range(10)]
     A = [planes(m, k, 1.0, 100 + i) for i, (m, n, k) in enumerate(specs)]
     B = [planes(n, k, 0.05, 200 + i) for i, (m, n, k) in enumerate(specs)]
-    say("grouped 40 products", specs[:6], "...")
+    say("grouped 50 products", specs[:6], "...")
     outs = mx.gemm_grouped([a[0] for a in A], [a[1] for a in A], [b[0] for b in B], [b[1] for b in B])
     torch.cuda.synchronize()
     for i, (a, b, o) in enumerate(zip(A, B, outs)):
-        single = mx.gemm(a[0], a[1], b[0], b[1])
-        torch.cuda.synchronize()
-        assert same_bits(o, single), "product %d %s differs from the single call" % (i, specs[i])
-    for i in (0, 4, 13, 39):
-        check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], outs[i], "product %d" % i)
+        if skinny_group(specs[i][0], specs[i][2]):
+            single = mx.gemm(a[0], a[1], b[0], b[1])
+            torch.cuda.synchronize()
+            assert same_bits(o, single), "product %d %s differs from the single call" % (i, specs[i])
+    for i in (0, 4, 13, 39) + tuple(range(40, 50)):
+        check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], outs[i], "product %d" % i,
+                     samples=2000 if specs[i][2] > 4096 else None)
 
 
 def test_mfma_order_and_output_slices(orc):
@@ -118,9 +127,10 @@ def test_mfma_order_and_output_slices(orc):
     for i, m in enumerate(tokens):
         assert got[i].data_ptr() == outs[i].data_ptr()
         inside[pad:pad + M * width].view(M, width)[:m, i * N:(i + 1) * N] = True
-        single = mx.gemm(A[i][0], A[i][1], B[i][0], B[i][1])
-        torch.cuda.synchronize()
-        assert same_bits(got[i].contiguous(), single), "expert %d" % i
+        if skinny_group(m, K):
+            single = mx.gemm(A[i][0], A[i][1], B[i][0], B[i][1])
+            torch.cuda.synchronize()
+            assert same_bits(got[i].contiguous(), single), "expert %d" % i
         check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], got[i], "expert %d" % i)
     assert bool((buf[~inside] == -0x5A5A5A5B).all()), "guard bytes written"
 
@@ -143,6 +153,22 @@ def test_prefill_experts(orc, dtype):
         assert tuple(outs[i].shape) == (m, n)
         check_oracle(orc, A[i][0], A[i][1], B[i][0], B[i][1], outs[i], "expert %s" % (specs[i],),
                      samples=None if m * n * k <= 1 << 27 else 4000)
+
+
+def test_short_k_tables(orc):
+    """K below 512 with 33 .. 128 rows: the skinny tables of two and four A
+    tiles (equal to single calls); above 128 rows, the single call."""
+    specs = [(40, 300, 384), (64, 200, 128), (100, 520, 256), (128, 64, 384), (129, 300, 256), (20, 33, 128)]
+    A = [planes(m, k, 1.0, 700 + i) for i, (m, n, k) in enumerate(specs)]
+    B = [planes(n, k, 0.05, 800 + i) for i, (m, n, k) in enumerate(specs)]
+    say("grouped short K", specs)
+    outs = mx.gemm_grouped([a[0] for a in A], [a[1] for a in A], [b[0] for b in B], [b[1] for b in B])
+    torch.cuda.synchronize()
+    for i, (a, b, o) in enumerate(zip(A, B, outs)):
+        single = mx.gemm(a[0], a[1], b[0], b[1])
+        torch.cuda.synchronize()
+        assert same_bits(o, single), "product %d %s differs from the single call" % (i, specs[i])
+        check_oracle(orc, a[0], a[1], b[0], b[1], o, "product %d" % i)
 
 
 def test_empty_list_and_refused_product():
