@@ -52,6 +52,8 @@
 // order in which the 64-deep MFMA steps accumulate depends on the tiling and,
 // for the ring tiles, on the tile's starting quarter; every order stays
 // within the tolerance that the tests derive for the instruction.
+#include <vector>
+
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -1079,15 +1081,14 @@ hipError_t flush_table(int t, GemmGroupArgs& g, int64_t& tasks, hipStream_t s) {
 
 hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStream_t s) {
   constexpr int kTables = 6, kRingTables = 4;
-  GemmGroupArgs g[kTables], rg[kRingTables];
+  // about 4 KiB a table: on the heap, not on the caller's stack
+  std::vector<GemmGroupArgs> tables(kTables + kRingTables);
+  GemmGroupArgs* g = tables.data();
+  GemmGroupArgs* rg = g + kTables;
   int64_t tasks[kTables] = {}, rtasks[kRingTables] = {};
-  for (int k = 0; k < kTables; ++k) {
-    g[k].n = 0;
-    g[k].task_start[0] = 0;
-  }
-  for (int k = 0; k < kRingTables; ++k) {
-    rg[k].n = 0;
-    rg[k].task_start[0] = 0;
+  for (GemmGroupArgs& t : tables) {
+    t.n = 0;
+    t.task_start[0] = 0;
   }
   for (int i = 0; i < n; ++i) {
     const GemmDesc& e = d[i];
@@ -1132,10 +1133,11 @@ hipError_t launch_gemm_grouped(const GemmDesc* d, int n, bool out_bf16, hipStrea
     }
     GemmParams p = make_params(e.qa, e.sa, e.qb, e.sb, e.M, e.N, e.K, e.sa_stride, e.sb_stride, e.out, e.out_ld,
                                out_bf16);
-    // one workgroup per strip with as many A tiles as the product has rows:
-    // a grouped grid is large already, so each strip of B is streamed once
-    // (64 experts x [2048, 7168] at 64 tokens each: 354 -> 314 us against
-    // 32-row blocks; at 128 tokens: 582 -> 435 us)
+    // one workgroup per strip with as many A tiles as the product has rows
+    // (more than 32 only with K < 512): a grouped grid is large already, so
+    // each strip of B is streamed once (with K = 7168, before ring tiles took
+    // these products: 64 tokens each 354 -> 314 us against 32-row blocks,
+    // 128 tokens 582 -> 435 us)
     const int mt = e.M <= 32 ? 1 : e.M <= 64 ? 2 : 4;
     p.tiles_m = (int32_t)((e.M + 32 * mt - 1) / (32 * mt));
     const int64_t t = p.tiles_m * ((e.N + 31) / 32);
