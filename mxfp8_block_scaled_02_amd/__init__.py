@@ -25,7 +25,8 @@ import torch
 
 __all__ = [
     "MXFP8Planes", "quantize", "rmsnorm_quantize", "dequantize", "quantize_grouped",
-    "rmsnorm_quantize_grouped", "dequantize_grouped", "gemm", "gemm_grouped", "as_fp8", "library_path", "lib",
+    "rmsnorm_quantize_grouped", "dequantize_grouped", "gemm", "gemm_grouped", "linear", "linear_grouped", "as_fp8",
+    "library_path", "lib",
     "BLOCK", "ROWWISE", "COLUMNWISE", "MFMA_GROUP", "mfma_scale_shape",
 ]
 
@@ -479,6 +480,34 @@ def gemm_grouped(qas: Sequence[torch.Tensor], sas: Sequence[torch.Tensor], qbs: 
     with _on(dev):
         _check(lib().mxfp8_gemm_grouped(arr, n, _out_code(dtype), _stream(dev)))
     return res
+
+
+def linear(x: torch.Tensor, w: MXFP8Planes, dtype: torch.dtype = torch.bfloat16,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [M, K] (bf16) times a pre-quantized weight w [N, K] (its rowwise plane)
+    transposed: the activation is quantized on the fly, then multiplied
+    (quantization.utils page, mm_mxfp8).  Two library calls; the activation's
+    scales take the weight's scale order."""
+    order = "mfma" if w.rowwise_scale.dim() == 3 else "row"
+    a = quantize(x, True, False, scale_order=order)
+    return gemm(a.rowwise_data, a.rowwise_scale, w.rowwise_data, w.rowwise_scale, dtype, out=out)
+
+
+def linear_grouped(xs: Sequence[torch.Tensor], ws: Sequence[MXFP8Planes], dtype: torch.dtype = torch.bfloat16,
+                   outs: Optional[Sequence[Optional[torch.Tensor]]] = None) -> list:
+    """The experts of an MoE layer: xs[i] [M_i, K_i] (bf16, any M_i) times the
+    pre-quantized weight ws[i] [N_i, K_i]: one grouped quantize of the
+    activations, then one grouped product."""
+    if len(xs) != len(ws):
+        raise ValueError("linear_grouped: one weight per activation")
+    if not xs:
+        return []
+    orders = {"mfma" if w.rowwise_scale.dim() == 3 else "row" for w in ws}
+    if len(orders) != 1:
+        raise ValueError("linear_grouped: the weights' scales must share one order")
+    a = quantize_grouped(xs, True, False, scale_order=orders.pop())
+    return gemm_grouped([p.rowwise_data for p in a], [p.rowwise_scale for p in a],
+                        [w.rowwise_data for w in ws], [w.rowwise_scale for w in ws], dtype, outs=outs)
 
 
 def _gemm_desc(qa, sa, qb, sb, dtype, out):

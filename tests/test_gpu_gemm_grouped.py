@@ -177,3 +177,28 @@ def test_empty_list_and_refused_product():
     qb, sb = planes(8, 128, 1.0, 2)
     with pytest.raises(ValueError):
         mx.gemm_grouped([qa], [sa], [qb], [sb])          # K 256 against 128
+
+
+def test_linear_compositions(orc):
+    """linear and linear_grouped equal their two explicit calls bit for bit:
+    the activation quantized on the fly (in the weight's scale order), then
+    the product."""
+    g = torch.Generator().manual_seed(91)
+    ws = [(torch.randn(n, 1024, generator=g) * 0.05).to(torch.bfloat16).to(DEV) for n in (256, 384, 512)]
+    xs = [torch.randn(m, 1024, generator=g).to(torch.bfloat16).to(DEV) for m in (3, 40, 300)]
+    for order in ("row", "mfma"):
+        wp = [mx.quantize(w, True, False, scale_order=order) for w in ws]
+        say("linear compositions", order)
+        got = mx.linear_grouped(xs, wp)
+        for x, w, y in zip(xs, wp, got):
+            a = mx.quantize(x, True, False, scale_order=order)
+            want = mx.gemm(a.rowwise_data, a.rowwise_scale, w.rowwise_data, w.rowwise_scale, torch.bfloat16)
+            one = mx.linear(x, w)
+            torch.cuda.synchronize()
+            assert same_bits(one, want), "linear"
+            if skinny_group(x.shape[0], 1024):
+                assert same_bits(y, want), "linear_grouped"
+            else:
+                # ring tiles in the grouped launch: the same bound, not the same bits
+                check_oracle(orc, a.rowwise_data, a.rowwise_scale, w.rowwise_data, w.rowwise_scale, y,
+                             "linear_grouped %d rows" % x.shape[0])
