@@ -101,6 +101,52 @@ def test_graph_replays_match_eager_f32_grouped_and_gemm():
         assert np.array_equal(host(c2.view(torch.int16)), host(d2.view(torch.int16))), "replay %d: ring" % rep
 
 
+def test_graph_replays_match_eager_transposed_and_grouped_gemm():
+    """The transposed columnwise plane (bf16 and float32 input) and a grouped
+    product with skinny and ring-tile tables, captured together: every replay
+    equals the eager calls bit for bit."""
+    print("[case] graph: transposed quantize bf16 [256, 520] and f32 [160, 264], grouped gemm "
+          "of 5 experts", flush=True)
+    x = synth.weight_with_outliers(256, 520, seed=61).to(DEV)
+    xf = synth.weight_with_outliers(160, 264, seed=62).to(DEV).float()
+    toks, widths, K = [1, 20, 64, 200, 0], [256, 384, 512, 300, 128], 1024
+    A = [synth.weight_with_outliers(m, K, seed=70 + i).to(DEV) for i, m in enumerate(toks)]
+    W = [mx.quantize(synth.weight_with_outliers(n, K, seed=80 + i).to(DEV), True, False) for i, n in enumerate(widths)]
+    pt = mx.quantize(x, False, True, columnwise_transposed=True)
+    pft = mx.quantize(xf, False, True, columnwise_transposed=True)
+    pa = [mx.quantize(a, True, False) for a in A]
+    ys = mx.gemm_grouped([p.rowwise_data for p in pa], [p.rowwise_scale for p in pa],
+                         [w.rowwise_data for w in W], [w.rowwise_scale for w in W], torch.bfloat16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mx.quantize(x, False, True, out=pt, columnwise_transposed=True)
+        mx.quantize(xf, False, True, out=pft, columnwise_transposed=True)
+        for a, p in zip(A, pa):
+            mx.quantize(a, True, False, out=p)
+        mx.gemm_grouped([p.rowwise_data for p in pa], [p.rowwise_scale for p in pa],
+                        [w.rowwise_data for w in W], [w.rowwise_scale for w in W], torch.bfloat16, outs=ys)
+    for rep in range(4):
+        x.copy_(synth.weight_with_outliers(256, 520, seed=400 + rep).to(DEV))
+        xf.mul_(-0.75)
+        for i, a in enumerate(A):
+            a.copy_(synth.weight_with_outliers(toks[i], K, seed=500 + 10 * rep + i).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        wt = mx.quantize(x.clone(), False, True, columnwise_transposed=True)
+        wft = mx.quantize(xf.clone(), False, True, columnwise_transposed=True)
+        wa = [mx.quantize(a.clone(), True, False) for a in A]
+        wy = mx.gemm_grouped([p.rowwise_data for p in wa], [p.rowwise_scale for p in wa],
+                             [w.rowwise_data for w in W], [w.rowwise_scale for w in W], torch.bfloat16)
+        torch.cuda.synchronize()
+        for got, want in ((pt, wt), (pft, wft)):
+            assert np.array_equal(host(got.columnwise_data), host(want.columnwise_data)), "replay %d" % rep
+            assert np.array_equal(host(got.columnwise_scale), host(want.columnwise_scale)), "replay %d" % rep
+        for i, (y, w) in enumerate(zip(ys, wy)):
+            assert np.array_equal(host(y.view(torch.int16)), host(w.view(torch.int16))), "replay %d expert %d" % (rep, i)
+
+
 def test_calls_run_on_the_current_stream():
     """Every entry point launches on the caller's current stream: on a side
     stream held up by a long sleep, then given a new input, each result must
