@@ -1,7 +1,7 @@
 """Refused calls on the GPU: every argument is checked before the first launch,
-so a grouped call with one bad tensor raises and leaves the outputs of its
-valid tensors untouched (filled with 0xA5 beforehand); bad single calls raise
-ValueError before touching the GPU."""
+so a grouped call with one bad tensor or product raises and leaves the
+outputs of its valid ones untouched (filled with 0xA5 beforehand); bad single
+calls raise ValueError before touching the GPU."""
 import pytest
 import torch
 
@@ -58,6 +58,27 @@ def test_grouped_dequantize_refused_writes_nothing():
         mx.dequantize_grouped([p.rowwise_data, q_bad], [p.rowwise_scale, s_bad], [mx.ROWWISE, mx.COLUMNWISE],
                               torch.float32, outs=[out, None])
     assert untouched(out)
+
+
+def test_grouped_gemm_refused_writes_nothing():
+    """A grouped product whose last descriptor is bad (K not a multiple of
+    128) raises before any launch: the valid products' outputs (skinny and
+    ring-tile tables) keep their 0xA5 fill."""
+    def quantized(rows, K, seed):
+        p = mx.quantize(bf16(rows, K, seed), True, False)
+        return p.rowwise_data, p.rowwise_scale
+    qa, sa = zip(*[quantized(m, 512, 10 + i) for i, m in enumerate((8, 200))])
+    qb, sb = zip(*[quantized(n, 512, 20 + i) for i, n in enumerate((256, 384))])
+    outs = [filled((8, 256), torch.float32), filled((200, 384), torch.float32)]
+    G = mx._GemmDesc
+    descs = [G(qa[i].data_ptr(), sa[i].data_ptr(), qb[i].data_ptr(), sb[i].data_ptr(), qa[i].shape[0],
+               qb[i].shape[0], 512, 0, 0, outs[i].data_ptr(), 0) for i in range(2)]
+    descs.append(G(qa[0].data_ptr(), sa[0].data_ptr(), qb[0].data_ptr(), sb[0].data_ptr(), 8, 256, 96, 0, 0,
+                   outs[0].data_ptr(), 0))
+    print("[case] grouped gemm with a bad last product", flush=True)
+    status = mx.lib().mxfp8_gemm_grouped((G * 3)(*descs), 3, 0, mx._stream(DEV))
+    assert status == 2                                     # MXFP8_ERR_SHAPE
+    assert untouched(*outs)
 
 
 def test_single_calls_refused():
