@@ -298,6 +298,31 @@ DeqItem to_item(const mxfp8_deq_desc& d) {
   return it;
 }
 
+// A grouped quantize: every descriptor, and every tensor's task count, is
+// checked before the first launch; tensors whose columnwise plane is stored
+// transposed go to their own tiles.
+template <class TaskFn, class TaskFnT, class LaunchFn, class LaunchFnT>
+mxfp8_status quantize_lists(const mxfp8_quant_desc* descs, int32_t n, void* stream, TaskFn tasks,
+                            TaskFnT tasks_t, LaunchFn launch, LaunchFnT launch_t) {
+  if (n < 0) return MXFP8_ERR_ARG;
+  if (n == 0) return MXFP8_OK;
+  if (!descs) return MXFP8_ERR_NULL;
+  std::vector<QuantItem> v, vt;
+  v.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (mxfp8_status st = check_quant(descs[i])) return st;
+    (col_t(descs[i]) ? vt : v).push_back(to_item(descs[i]));
+  }
+  for (const QuantItem& it : vt)
+    if (tasks_t(it.d) > kMaxTasksPerLaunch) return MXFP8_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mxfp8_status st = run_items<mx::QuantArgs, mx::QuantArgsPitched>(
+          v, tasks, [&](const auto& args, int64_t t) { return launch(args, t, s); }))
+    return st;
+  return run_items<mx::QuantArgs, mx::QuantArgsPitched>(
+      vt, tasks_t, [&](const auto& args, int64_t t) { return launch_t(args, t, s); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,46 +343,17 @@ const char* mxfp8_status_string(mxfp8_status status) {
 }
 
 mxfp8_status mxfp8_quantize_grouped(const mxfp8_quant_desc* descs, int32_t n, void* stream) {
-  if (n < 0) return MXFP8_ERR_ARG;
-  if (n == 0) return MXFP8_OK;
-  if (!descs) return MXFP8_ERR_NULL;
-  // tensors whose columnwise plane is stored transposed go to their own tiles
-  std::vector<QuantItem> v, vt;
-  v.reserve(n);
-  for (int32_t i = 0; i < n; ++i) {
-    if (mxfp8_status st = check_quant(descs[i])) return st;
-    (col_t(descs[i]) ? vt : v).push_back(to_item(descs[i]));
-  }
-  for (const QuantItem& it : vt)   // before any launch
-    if (mx::quant_colt_tasks(it.d) > kMaxTasksPerLaunch) return MXFP8_ERR_SHAPE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mxfp8_status st = run_items<mx::QuantArgs, mx::QuantArgsPitched>(
-          v, mx::quant_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize(args, t, s); }))
-    return st;
-  return run_items<mx::QuantArgs, mx::QuantArgsPitched>(
-      vt, mx::quant_colt_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize_colt(args, t, s); });
+  return quantize_lists(descs, n, stream, mx::quant_tasks, mx::quant_colt_tasks,
+                        [](const auto& args, int64_t t, hipStream_t s) { return mx::launch_quantize(args, t, s); },
+                        [](const auto& args, int64_t t, hipStream_t s) { return mx::launch_quantize_colt(args, t, s); });
 }
 
 mxfp8_status mxfp8_quantize_f32_grouped(const mxfp8_quant_desc* descs, int32_t n,
                                         void* stream) {
-  if (n < 0) return MXFP8_ERR_ARG;
-  if (n == 0) return MXFP8_OK;
-  if (!descs) return MXFP8_ERR_NULL;
-  std::vector<QuantItem> v, vt;
-  v.reserve(n);
-  for (int32_t i = 0; i < n; ++i) {
-    if (mxfp8_status st = check_quant(descs[i])) return st;
-    (col_t(descs[i]) ? vt : v).push_back(to_item(descs[i]));
-  }
-  for (const QuantItem& it : vt)   // before any launch
-    if (mx::quant_f32_colt_tasks(it.d) > kMaxTasksPerLaunch) return MXFP8_ERR_SHAPE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mxfp8_status st = run_items<mx::QuantArgs, mx::QuantArgsPitched>(
-          v, mx::quant_f32_tasks, [&](const auto& args, int64_t t) { return mx::launch_quantize_f32(args, t, s); }))
-    return st;
-  return run_items<mx::QuantArgs, mx::QuantArgsPitched>(
-      vt, mx::quant_f32_colt_tasks,
-      [&](const auto& args, int64_t t) { return mx::launch_quantize_f32_colt(args, t, s); });
+  return quantize_lists(
+      descs, n, stream, mx::quant_f32_tasks, mx::quant_f32_colt_tasks,
+      [](const auto& args, int64_t t, hipStream_t s) { return mx::launch_quantize_f32(args, t, s); },
+      [](const auto& args, int64_t t, hipStream_t s) { return mx::launch_quantize_f32_colt(args, t, s); });
 }
 
 mxfp8_status mxfp8_quantize_f32(const void* x, int64_t rows, int64_t cols, void* q_row,
