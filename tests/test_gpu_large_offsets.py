@@ -76,6 +76,20 @@ def test_quantize_bf16_transposed_columnwise(orc):
         assert_same(host(p.columnwise_scale[:, r0 // 32]), sc[0], "s_colT block %d" % (r0 // 32))
 
 
+def test_quantize_f32_transposed_columnwise(orc):
+    """float32 input [65600, 32768] (8.6 GB), the columnwise plane stored
+    transposed: its rows' offsets pass 2^31."""
+    x = big(ROWS, COLS, 11, torch.float32, 0.02)
+    say("large quantize f32, transposed columnwise", (ROWS, COLS))
+    p = mx.quantize(x, False, True, columnwise_transposed=True)
+    torch.cuda.synchronize()
+    for r0 in strips(ROWS):
+        qc, sc = orc.quantize_colwise(host(x[r0:r0 + 32]))
+        assert_same(host(p.columnwise_data[:, r0:r0 + 32]), np.ascontiguousarray(qc.T),
+                    "f32 q_colT rows %d.." % r0)
+        assert_same(host(p.columnwise_scale[:, r0 // 32]), sc[0], "f32 s_colT block %d" % (r0 // 32))
+
+
 def test_quantize_f32(orc):
     x = big(ROWS, COLS, 2, torch.float32, 0.02)
     for row, col in ((True, True), (True, False)):
@@ -154,6 +168,22 @@ def test_gemm_ring_tiles(orc):
     ms = torch.tensor([0, 1, M // 2, M - 33, M - 2, M - 1], device=DEV)
     ns = torch.tensor([0, 37, 128, 255], device=DEV)
     check_products(orc, qa, sa, qb, sb, out, ms, ns, "ring")
+
+
+def test_gemm_grouped_ring_tiles(orc):
+    """The same A [65600, 32768] as one product of a grouped call (its ring
+    tiles in a launch table), and a 16-row product beside it."""
+    M, N, K = ROWS, 256, COLS
+    qa, sa = random_planes(M, K, 6)
+    qb, sb = random_planes(N, K, 7)
+    qc, sc = random_planes(16, K, 10)
+    say("large gemm grouped", (M, N, K), (16, N, K))
+    out, small = mx.gemm_grouped([qa, qc], [sa, sc], [qb, qb], [sb, sb], torch.float32)
+    torch.cuda.synchronize()
+    ms = torch.tensor([0, 1, M // 2, M - 33, M - 2, M - 1], device=DEV)
+    ns = torch.tensor([0, 37, 128, 255], device=DEV)
+    check_products(orc, qa, sa, qb, sb, out, ms, ns, "grouped ring")
+    check_products(orc, qc, sc, qb, sb, small, torch.tensor([0, 15], device=DEV), ns, "grouped skinny")
 
 
 def test_gemm_skinny(orc):
