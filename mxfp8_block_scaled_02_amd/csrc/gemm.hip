@@ -1186,13 +1186,19 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* sa, const uint8_t* qb, 
     launch_skinny<4, true>(p, r128 * skinny, s);
   } else if (M <= 32) {
     launch_skinny<1>(p, skinny, s);
-  } else if (M <= 64) {
-    launch_skinny<2>(p, skinny, s);
-  } else if (M <= 128) {
-    // four A tiles; with the weight read from HBM this beats the ring tiles
-    // (128 x 7168 x 7168: 28 us against 43 us for 64 x 128 tiles; K = 4096:
-    // 19 against 26 us; K = 16384: 66 against 88 us)
-    launch_skinny<4>(p, skinny, s);
+  } else if (M <= 128 && !(K >= kBK * kGroup && r64 * ((N + 127) / 128) * 16 >= 9 * (int64_t)kCUs)) {
+    // two or four A tiles.  With the weight read from HBM they beat the ring
+    // tiles while those are few (128 x 7168 x 7168: 29 us against 43 us; 64 x
+    // 14336 x 7168: 40 against 46 us; 33 x 16384 x 4096: 25 against 29 us, at
+    // 112, 112 and 128 tiles of 64 x 128).  From 144 such tiles on (9/16 of
+    // the CUs) the ring tiles, chosen as below, win: 64 x 18432 x
+    // 7168 55 -> 48 us, 128 x 12288 x 4096 37 -> 27 us, 64 x 28672 x 7168
+    // 75 -> 52 us, 128 x 28672 x 7168 107 -> 59 us.  With up to 32 rows the
+    // single A tile wins at any width (16 x 28672 x 7168: 42 against 48 us).
+    if (M <= 64)
+      launch_skinny<2>(p, skinny, s);
+    else
+      launch_skinny<4>(p, skinny, s);
   } else if (K >= kBK * kGroup) {
     // the ring tile with the least rounds of tiles over the CUs times the
     // time of one tile at full load, in eighths of a 256 x 256 tile's

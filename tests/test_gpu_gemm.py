@@ -141,6 +141,9 @@ def test_gemm_nan_scale(orc):
     (500, 7000, 1024), (400, 6000, 512),
     # 64 x 128 tiles (few tiles in all):
     (600, 2048, 4096), (520, 1000, 512), (520, 900, 1024),
+    # 33 .. 128 rows under a wide weight (at least 144 tiles of 64 x 128), one
+    # and two 64-row tiles, ragged N, a short last group:
+    (64, 18432, 1024), (33, 18433, 512), (100, 9216, 512), (128, 12288, 640), (65, 9300, 1024),
     # K % 512 != 0 with K >= 512: the ring tiles' short last group, whose first
     # 2, 4 or 6 stages repeat the stage before with scales 0, on each tile size
     (4352, 3840, 640), (4096, 4096 + 256, 896), (500, 7000, 768), (520, 1000, 1152),
@@ -213,6 +216,9 @@ def test_gemm_bf16_output_is_rounded_f32_output(mnk):
                                  (97, 3000, 2048), (65, 2750, 16512),
                                  # four 32-row A tiles (64 < M <= 128, N > 4096)
                                  (128, 7168, 7040), (128, 7168, 7168), (100, 4200, 8320),
+                                 # wide weights just short of 144 ring tiles (128 and 142 tiles of
+                                 # 64 x 128), and any width with K < 512
+                                 (33, 16384, 512), (100, 9088, 512), (128, 12288, 384),
                                  # M > 128 with a narrow weight: 32-row blocks (up to 32 per strip),
                                  # 64-row blocks (65 per strip; the last of two rows), 128-row blocks
                                  (200, 1000, 640), (1000, 100, 384), (4100, 40, 256), (300, 1500, 1024),
