@@ -369,11 +369,14 @@ def bench_gemm(torch, mx, steps, synth=None):
     T = Timed(torch, EAGER, warm_ms=25.0)   # untimed replays first: the clocks settle
     res = {}
     # 4096 x 4096 x 11008: an MLP down projection, K not a multiple of 512;
-    # 256 x 2048 x 7168: 256 tokens through one 2048 x 7168 expert weight
+    # 256 x 2048 x 7168: 256 tokens through one 2048 x 7168 expert weight;
+    # 64 x 28672 x 7168: 64 tokens through a fused gate and up projection
+    # (two 14336 x 7168 weights), a wide weight under a few rows
     # "_mfma_scales": both operands' scales in the MFMA order (K % 512 == 0)
     for M, N, K, order in ((8192, 8192, 8192, "row"), (8192, 8192, 8192, "mfma"),
                            (1024, 7168, 7168, "row"), (1024, 7168, 7168, "mfma"),
                            (4096, 4096, 11008, "row"), (256, 2048, 7168, "row"),
+                           (64, 28672, 7168, "row"),
                            (128, 7168, 7168, "row"), (128, 7168, 7168, "mfma"),
                            (16, 7168, 7168, "row"), (16, 7168, 7168, "mfma")):
         g = torch.Generator(device=dev).manual_seed(M + N + K)
