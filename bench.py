@@ -18,8 +18,8 @@ prefill), after at least 5 warm-up launches; every line but the headline
 first replays its graph untimed for 25 ms, since the clocks ramp up over the
 first milliseconds of work after an idle gap such as the capture.  After the
 timed steps the headline launch is replayed for about 8 s ("sustained"; not
-part of the value), and the matrix-product lines report the median of 5
-replays.
+part of the value).  Every line but the headline reports the median of 5
+timed replays.
 
 Printed: one JSON line with GB/s of algorithmic bytes (input read once plus
 every output written once), its fraction of the 8 TB/s HBM peak, the five
@@ -95,18 +95,22 @@ class Timed:
     the GPU's and not Python's per-call overhead.  HIP events on the replay
     stream bracket the replay; the host synchronizes on both sides."""
 
-    def __init__(self, torch, eager=False, warm_ms=0.0):
+    def __init__(self, torch, eager=False, warm_ms=0.0, replays=1):
         self.torch = torch
         self.eager = eager
         self.warm_ms = warm_ms
+        self.replays = replays
 
-    def run(self, fn, steps, warmup, replays=1):
-        """replays > 1: the graph is replayed that many times, each timed on
-        its own, and the median replay is reported.  warm_ms: the graph is
+    def run(self, fn, steps, warmup, replays=None):
+        """replays > 1 (default: the constructor's): the graph is replayed that
+        many times, each timed on its own, and the median replay is reported
+        (the events also count any host delay before a replay reaches the
+        GPU, so one replay alone can read several times too long).  warm_ms: the graph is
         first replayed untimed until that much time has passed (the clocks
         ramp up over the first ten or so milliseconds of work after an idle
         gap, such as the capture itself).  Eager: both ignored."""
         torch = self.torch
+        replays = self.replays if replays is None else replays
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -216,9 +220,10 @@ def bench_headline(torch, mx, synth, steps, warmup, sustain_s=0.0):
 
 def bench_configs(torch, mx, synth, steps):
     """The other four workloads, each at least 50 launches (20 for the 65536-row
-    prefill) after 5 warm-up launches and 25 ms of untimed graph replays."""
+    prefill) after 5 warm-up launches and 25 ms of untimed graph replays; the
+    median of 5 timed replays."""
     dev = torch.device("cuda:0")
-    T = Timed(torch, EAGER, warm_ms=25.0)   # untimed replays first: the clocks settle
+    T = Timed(torch, EAGER, warm_ms=25.0, replays=5)   # untimed replays first: the clocks settle
     res = {}
     k_small = max(50, steps // 2)
     k_large = max(20, steps // 10)
@@ -272,10 +277,11 @@ def bench_configs(torch, mx, synth, steps):
 
 
 def bench_other_rows(torch, mx, synth, steps):
-    """The entry points outside the five workloads, each on its own input."""
+    """The entry points outside the five workloads, each on its own input; the
+    median of 5 timed replays."""
     dev = torch.device("cuda:0")
     res = {}
-    T = Timed(torch, EAGER, warm_ms=25.0)   # untimed replays first: the clocks settle
+    T = Timed(torch, EAGER, warm_ms=25.0, replays=5)   # untimed replays first: the clocks settle
 
     x = synth.workload("rowwise_8192x7168", device=dev)["x"]
     r, c = x.shape
