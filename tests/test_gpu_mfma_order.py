@@ -150,6 +150,7 @@ def test_dequantize(shape):
 
 @pytest.mark.parametrize("mnk", [
     (1024, 1024, 512), (1024, 7168, 7168), (4352, 3840, 1536), (600, 2048, 4096),  # ring tiles
+    (64, 18432, 1024), (100, 20480, 512),             # ring tiles under 33 .. 128 rows (a wide weight)
     (16, 4096, 4096), (40, 1000, 2048), (100, 200, 512), (300, 2048, 4096),       # skinny, staged words
     (16, 96, 16896), (40, 130, 16896), (100, 64, 8704),                           # skinny, paired words
     (1024, 512, 1024), (300, 2048, 8704)])            # skinny row blocks: 64 rows; 128 rows, paired words
